@@ -1,0 +1,236 @@
+"""Benchmark of the AWQ scale search + INT4 group quantization hot path on one MI355X.
+
+One step = one whole layer: activation statistic, candidate scales, quantize->delta for every
+candidate, the error GEMM with its fused squared-error epilogue, losses + argmin, and the final
+quantize + pack, each through the C ABI on the current stream. Inputs are generated on the host
+(seeded, synthetic) and copied to HBM before timing; outputs and workspaces are preallocated.
+
+Prints one JSON line. `value` = candidate evaluations per second for the whole layer search
+(n_grid / seconds per step). `roofline` is for the error GEMM (the dominant kernel), timed with
+HIP events on the stream it runs on. `cpu_baseline` times the CPU oracle on a bounded row sample
+of the same layer and scales it to the whole layer.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+METRIC = "layer scale-search time, grid candidates/s, error-GEMM TFLOP/s (% bf16 MFMA peak)"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 matrix peak
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+
+
+def _log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def _copy_probe(nbytes: int, reps: int) -> None:
+    """A plain device copy of known size, for scaling the HBM byte counters."""
+    import torch
+
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+    a.fill_(1.0)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes, "reps": reps}))
+
+
+def cpu_baseline(wl, x_np, w_np, target_s: float) -> dict:
+    """The CPU oracle as it stands on a row sample of the layer, scaled to the whole layer."""
+    from oracle import awq_oracle as O
+    from workloads import to_f32
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    X = to_f32(x_np).astype(np.float64)
+
+    def run(rows: int) -> float:
+        W = to_f32(w_np[:rows]).astype(np.float64)
+        t0 = time.perf_counter()
+        O.search_scales(X, W, wl.group_size, wl.n_grid)
+        return time.perf_counter() - t0
+
+    rows = 64
+    t = run(rows)
+    rows_full = min(wl.d_out, max(rows, int(rows * target_s / max(t, 1e-3))))
+    rows_full = max(64, rows_full // 64 * 64)
+    if rows_full != rows:
+        t = run(rows_full)
+        rows = rows_full
+    layer_s = t * wl.d_out / rows
+    return {"value": wl.n_grid / layer_s, "unit": "candidates/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"full search (act_mean over all {wl.n_tokens} tokens, {wl.n_grid} candidates, float64) on "
+                      f"the first {rows} of {wl.d_out} weight rows; {t:.1f} s, scaled by d_out/rows to the layer",
+            "layer_seconds_est": layer_s}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", type=int, default=2, help="workload id (2 = 7B fused QKV, the headline)")
+    ap.add_argument("--cand-per-pass", type=int, default=0, help="candidates per GEMM launch (0 = all)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-probe", type=int, default=0, help="only run a device copy of this many bytes")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the search shards by weight "
+              "rows with one tiny loss exchange, which this single-GPU build does not implement.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    if args.copy_probe:
+        _copy_probe(args.copy_probe, 10)
+        return 0
+
+    from post_quantization_mean_amd import binding as B
+    from workloads import make_w, make_x, to_torch, workload
+
+    wl = workload(args.config)
+    cpp = args.cand_per_pass or wl.n_grid
+    torch.cuda.set_device(0)
+    B.load_library()
+    _log(f"generating {wl.name}: X {wl.n_tokens}x{wl.d_in} W {wl.d_out}x{wl.d_in} {wl.dtype}")
+    x_np, w_np = make_x(wl), make_w(wl)
+    x = to_torch(x_np, "cuda")
+    w = to_torch(w_np, "cuda")
+    parts = list(wl.parts) or [wl.d_out]
+    w_parts, r = [], 0
+    for p in parts:
+        w_parts.append(w[r:r + p])
+        r += p
+    dev = x.device
+    dt = B.AWQ_DTYPE_BF16 if wl.dtype == "bf16" else B.AWQ_DTYPE_F32
+    n_tiles = B.awq_error_tiles(wl.n_tokens, wl.d_out)
+    G = wl.d_in // wl.group_size
+    act = torch.empty(wl.d_in, dtype=torch.float64, device=dev)
+    ws_act = torch.empty(B.awq_act_stats_workspace_bytes(dt, wl.n_tokens, wl.d_in), dtype=torch.uint8, device=dev)
+    cand = torch.empty((wl.n_grid, wl.d_in), dtype=torch.float64, device=dev)
+    delta = torch.empty((cpp, wl.d_out, wl.d_in), dtype=x.dtype, device=dev)
+    sse = torch.empty((wl.n_grid, n_tiles), dtype=torch.float64, device=dev)
+    losses = torch.empty(wl.n_grid, dtype=torch.float64, device=dev)
+    best = torch.empty(wl.d_in, dtype=torch.float64, device=dev)
+    info = torch.empty(2, dtype=torch.int32, device=dev)
+    pack_out = {"codes": torch.empty((wl.d_out, wl.d_in // 2), dtype=torch.uint8, device=dev),
+                "qscales": torch.empty((wl.d_out, G), dtype=torch.float32, device=dev),
+                "zeros": torch.empty((wl.d_out, G), dtype=torch.int32, device=dev)}
+    stream = torch.cuda.current_stream()
+    ev = {}
+
+    def mark(name):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        ev.setdefault(name, []).append(e)
+
+    def step(timed: bool):
+        if timed:
+            mark("act0")
+        B.awq_act_stats(x, act, ws_act)
+        B.awq_candidate_scales(act, wl.n_grid, cand)
+        for k0 in range(0, wl.n_grid, cpp):
+            nk = min(cpp, wl.n_grid - k0)
+            if timed:
+                mark("q0")
+            B.awq_quant_delta(w_parts, cand[k0:k0 + nk], wl.group_size, delta[:nk])
+            if timed:
+                mark("g0")
+            B.awq_error_sse(x, delta[:nk], sse[k0:k0 + nk])
+            if timed:
+                mark("g1")
+        B.awq_loss_argmin(sse, wl.n_tokens, wl.d_out, cand, losses, best, info)
+        if timed:
+            mark("p0")
+        B.awq_quantize_pack(w_parts, best, wl.group_size, pack_out)
+        if timed:
+            mark("p1")
+
+    _log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    _log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+
+    def span(a, b):
+        return float(sum(s.elapsed_time(e) for s, e in zip(ev[a], ev[b])))
+
+    n_gemm = len(ev["g0"])
+    gemm_ms = span("g0", "g1") / n_gemm
+    quant_ms = span("q0", "g0") / n_gemm
+    pack_ms = span("p0", "p1") / args.steps
+    act_ms = float(sum(ev["act0"][i].elapsed_time(ev["q0"][i * (n_gemm // args.steps)])
+                       for i in range(args.steps))) / args.steps
+    flops_launch = 2.0 * wl.n_tokens * wl.d_in * wl.d_out * min(cpp, wl.n_grid)
+    peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
+    achieved = flops_launch / (gemm_ms * 1e-3) / 1e12
+    esz = 2 if wl.dtype == "bf16" else 4
+    q_bytes = wl.d_out * wl.d_in * esz * (1 + min(cpp, wl.n_grid))
+    p_bytes = wl.d_out * wl.d_in * (esz + 0.5) + wl.d_out * G * 8 + wl.d_in * 8
+    info_h = info.cpu().tolist()
+    _log(f"k*={info_h[0]} flags={info_h[1]} ms/step={ms_step:.3f} gemm={gemm_ms:.3f} ms ({achieved:.1f} TFLOP/s)")
+
+    out = {
+        "metric": METRIC,
+        "value": wl.n_grid / (ms_step * 1e-3),
+        "unit": "candidates/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "n_tokens": wl.n_tokens, "d_in": wl.d_in, "d_out": wl.d_out,
+                   "parts": parts, "group_size": wl.group_size, "n_grid": wl.n_grid, "cand_per_pass": cpp},
+        "roofline": {"bound": "mfma", "kernel": "error_sse_kernel", "achieved": achieved, "peak": peak,
+                     "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,
+                     "launch_ms": gemm_ms, "flops_per_launch": flops_launch},
+        "search_ms": ms_step,
+        "error_gemm_tflops": achieved,
+        "kernels_ms": {"act_stats+finalize": act_ms, "quant_delta": quant_ms, "error_sse": gemm_ms,
+                       "quantize_pack": pack_ms},
+        "hbm_gbps": {"quant_delta": q_bytes / (quant_ms * 1e-3) / 1e9,
+                     "quantize_pack": p_bytes / (pack_ms * 1e-3) / 1e9,
+                     "act_stats": (wl.n_tokens * wl.d_in * esz + wl.d_in * 8) / (act_ms * 1e-3) / 1e9},
+        "best_k": info_h[0],
+    }
+    if not args.no_cpu_baseline:
+        _log("cpu baseline (oracle on a row sample)")
+        out["cpu_baseline"] = cpu_baseline(wl, x_np, w_np, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,206 @@
+/*
+ * awq.h - C ABI of the MI355X (gfx950) AWQ activation-aware scale search and INT4
+ * group quantization library (libawq_mi355x.so).
+ *
+ * The method, as the pages define it:
+ *   act_mean[c] = mean over tokens i of |X[i,c]|
+ *       (bjdmk.com.cn AWQ article, section "显著权重的识别", the S_X equation;
+ *        msModelSlim "AWQ：激活感知权重量化算法说明", 原理 / 算法公式).
+ *   for k = 0 .. n_grid-1, r = k / n_grid:  s = max(act_mean^r, 1e-4);  s /= sqrt(max(s)*min(s))
+ *       (msModelSlim 算法公式; the grid covers [0, 1) in steps of 1/n_grid).
+ *   W is scaled by s per input channel, quantized to asymmetric INT4 in groups of 128
+ *   consecutive input channels of a row: step = max((max-min)/15, 1e-8),
+ *   zero = round(-min/step), q = clamp(round(y/step) + zero, 0, 15), dequantized as
+ *   (q - zero)*step and divided by s again
+ *       (gsyq.cn "AWQ 离群激活平滑实操：逐通道等价缩放与 4-bit 精度无损转换", section 二,
+ *        pseudo_quantize_int4 and search_smooth_scaling_factors).
+ *   Each ratio is scored by mean((X W^T - X What^T)^2) (gsyq section 二; bjdmk L(s)),
+ *   the first strict minimum is chosen (gsyq section 二, best_loss / best_scale = ones),
+ *   and W*s* is exported as packed INT4 codes with per-group steps and zero points
+ *   (qqiyuan.cn "基于awq 4-bit量化技术的大模型推理优化实战", group_quantize;
+ *    bjdmk section "GPU 硬件级反量化算子内联融合": two 4-bit values per uint8).
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor argument is DEVICE memory owned by the caller; the library never
+ *     allocates, frees or keeps a pointer after the call returns. Host-side arrays are
+ *     marked "host" (the list of weight-part pointers and their row counts).
+ *   - Matrices are row-major. X is [n_tokens, d_in] with row pitch ld_x elements
+ *     (ld_x >= d_in, ld_x a multiple of 8). W is [d_out, d_in], contiguous; a fused set
+ *     of linears that share the input (q/k/v, gate/up) is passed as up to
+ *     AWQ_MAX_PARTS parts whose rows are stacked in order (total rows d_out), and every
+ *     per-row output follows that stacked order.
+ *   - dtype selects the storage type of X, W and the delta buffer: AWQ_DTYPE_BF16
+ *     (uint16 bfloat16 bit patterns) or AWQ_DTYPE_F32. Statistics, scales and losses
+ *     are float64; exported steps are float32, zero points int32, codes uint8.
+ *   - Device pointers must be 16-byte aligned (256-byte for workspaces).
+ *   - stream is a hipStream_t (NULL = the default stream). Calls only enqueue work and
+ *     return without synchronising; results are ready when the stream reaches them.
+ *   - Argument errors are detected on the host before anything is enqueued; the call
+ *     then returns a non-zero awq_status and enqueues nothing. AWQ_ERR_HIP reports a
+ *     failed HIP runtime call or kernel launch. awq_last_error() gives the detail for
+ *     the calling thread. No entry point aborts the process.
+ *   - Inputs are never modified. Calls that share a workspace must not overlap.
+ *   - group_size must be 128 (the only group the GPU kernels implement).
+ */
+#ifndef AWQ_MI355X_H
+#define AWQ_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define AWQ_API __attribute__((visibility("default")))
+#else
+#define AWQ_API
+#endif
+
+#define AWQ_ABI_VERSION 1
+#define AWQ_MAX_PARTS 8
+#define AWQ_GROUP_SIZE 128
+
+typedef enum {
+  AWQ_OK = 0,
+  AWQ_ERR_NULL = 1,        /* a required pointer is NULL */
+  AWQ_ERR_SHAPE = 2,       /* a size is negative or zero where it must be positive, sizes
+                              disagree, or d_in is not a multiple of group_size */
+  AWQ_ERR_NO_TOKENS = 3,   /* n_tokens == 0: there is no activation mean to search with
+                              (msModelSlim FAQ, "No activation mean for target module") */
+  AWQ_ERR_ARG = 4,         /* n_grid < 1, bad candidate range, ld_x < d_in, too many parts */
+  AWQ_ERR_UNSUPPORTED = 5, /* unknown dtype, group_size != 128, misaligned pointer or pitch,
+                              or a size beyond the kernels' 32-bit tile offsets */
+  AWQ_ERR_WORKSPACE = 6,   /* workspace missing or smaller than the matching query returns */
+  AWQ_ERR_HIP = 7          /* a HIP runtime call or kernel launch failed */
+} awq_status;
+
+typedef enum { AWQ_DTYPE_F32 = 0, AWQ_DTYPE_BF16 = 1 } awq_dtype;
+
+/* Flag bits of best_info[1] (written on the device by awq_loss_argmin / awq_search_scales). */
+#define AWQ_INFO_ALL_NONFINITE 1 /* no loss was below +inf: k* = 0, whose scales are all 1 */
+
+/* ------------------------------------------------------------------ library */
+
+/* Returns AWQ_ABI_VERSION of the built library. */
+AWQ_API int awq_abi_version(void);
+
+/* Static, human-readable name of a status code. Never NULL. */
+AWQ_API const char* awq_status_string(int status);
+
+/* Detail of the last non-OK status returned on the calling thread ("" if none). The string
+ * stays valid until the next call into the library on this thread. */
+AWQ_API const char* awq_last_error(void);
+
+/* ------------------------------------------------------------------ a1: activation statistic */
+
+/* Workspace bytes awq_act_stats needs for this shape (0 on invalid sizes). */
+AWQ_API size_t awq_act_stats_workspace_bytes(int dtype, int64_t n_tokens, int64_t d_in);
+
+/* act_mean[c] = (1/n_tokens) * sum_i |X[i,c]|, accumulated in float64 in a fixed order
+ * (bjdmk S_X equation; msModelSlim 算法公式, act_mean = mean(abs(act))).
+ *   x         device, [n_tokens, ld_x] of dtype.
+ *   act_mean  device, float64 [d_in], written.
+ *   workspace device, >= awq_act_stats_workspace_bytes(dtype, n_tokens, d_in) bytes.
+ * n_tokens == 0 returns AWQ_ERR_NO_TOKENS. NaN/Inf inputs propagate into their channel. */
+AWQ_API int awq_act_stats(const void* x, int dtype, int64_t n_tokens, int64_t d_in, int64_t ld_x,
+                  double* act_mean, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------ a2: candidate scales */
+
+/* For k = 0 .. n_grid-1 and r = k/n_grid:
+ *   cand_scales[k, c] = max(act_mean[c]^r, 1e-4) / sqrt(max_c(.) * min_c(.))   (float64)
+ * (msModelSlim 算法公式, both lines; grid step 1/n_grid over [0, 1)).
+ *   act_mean    device, float64 [d_in].
+ *   cand_scales device, float64 [n_grid, d_in], written. Row 0 is exactly 1.
+ * A NaN in act_mean makes every row with r > 0 NaN, as the formula implies. */
+AWQ_API int awq_candidate_scales(const double* act_mean, int64_t d_in, int n_grid, double* cand_scales,
+                         void* stream);
+
+/* ------------------------------------------------------------------ a3: quantize -> delta */
+
+/* For each of n_cand candidate scale rows s (float64 [n_cand, d_in], consecutive):
+ *   y = W * s (per input channel), asymmetric INT4 group quantization of y (groups of 128
+ *   consecutive channels of a row, gsyq section 二), dequantize, divide by s, and write
+ *   delta[j, o, c] = What[o, c] - W[o, c]   in dtype (bfloat16 rounds to nearest even).
+ * The quantizer decisions are taken in float64, exactly as the definition reads.
+ *   w_parts    host array of n_parts device pointers; part p is [part_rows[p], d_in] of dtype.
+ *   part_rows  host array of n_parts row counts (d_out = their sum).
+ *   cand_scales device, float64 [n_cand, d_in].
+ *   delta      device, [n_cand, d_out, d_in] of dtype, written. */
+AWQ_API int awq_quant_delta(const void* const* w_parts, const int64_t* part_rows, int n_parts, int dtype,
+                    int64_t d_in, int group_size, const double* cand_scales, int n_cand,
+                    void* delta, void* stream);
+
+/* ------------------------------------------------------------------ a4: error GEMM + SSE */
+
+/* Number of 256x256 output tiles per candidate: ceil(n_tokens/256) * ceil(d_out/256). */
+AWQ_API int64_t awq_error_tiles(int64_t n_tokens, int64_t d_out);
+
+/* Per-tile sums of squares of E_j = X * delta_j^T, the output error of candidate j, which by
+ * linearity equals X W^T - X What_j^T (gsyq section 二 target_out - actual_out; bjdmk L(s)).
+ * E_j is never written out: each 256x256 tile of it is squared and summed in the GEMM's
+ * epilogue. Products are exact bf16 (or f32) matrix-core products with float32
+ * accumulation; tile sums are float64.
+ *   x        device, [n_tokens, ld_x] of dtype.
+ *   delta    device, [n_cand, d_out, d_in] of dtype (as written by awq_quant_delta).
+ *   tile_sse device, float64 [n_cand, awq_error_tiles(n_tokens, d_out)], written; within a
+ *            candidate the tiles are ordered token-tile major, row-tile minor. */
+AWQ_API int awq_error_sse(const void* x, int64_t ld_x, const void* delta, int dtype, int64_t n_tokens,
+                  int64_t d_in, int64_t d_out, int n_cand, double* tile_sse, void* stream);
+
+/* ------------------------------------------------------------------ a5: losses and argmin */
+
+/* losses[k] = (sum of tile_sse[k, :], float64, fixed order) / (n_tokens * d_out): the output
+ * MSE of ratio k. k* = the first k with the smallest loss among losses below +inf (a strict
+ * "<" scan starting from +inf), or 0 when there is none (gsyq section 二).
+ *   tile_sse    device, float64 [n_grid, tiles_per_cand].
+ *   cand_scales device, float64 [n_grid, d_in].
+ *   losses      device, float64 [n_grid], written.
+ *   best_scales device, float64 [d_in], written with cand_scales[k*, :].
+ *   best_info   device, int32 [2], written: {k*, flags (AWQ_INFO_*)}. */
+AWQ_API int awq_loss_argmin(const double* tile_sse, int64_t tiles_per_cand, int n_grid, int64_t n_tokens,
+                    int64_t d_out, const double* cand_scales, int64_t d_in, double* losses,
+                    double* best_scales, int32_t* best_info, void* stream);
+
+/* ------------------------------------------------------------------ a2..a5 composed */
+
+/* Workspace bytes awq_search_scales needs when it evaluates cand_per_pass candidates per
+ * GEMM launch (1 <= cand_per_pass <= n_grid; larger passes fill the GPU better and need a
+ * delta buffer of cand_per_pass * d_out * d_in elements). 0 on invalid sizes. */
+AWQ_API size_t awq_search_workspace_bytes(int dtype, int64_t n_tokens, int64_t d_in, int64_t d_out,
+                                  int group_size, int n_grid, int cand_per_pass);
+
+/* The whole grid search for one layer (or fused set): a2, then a3 + a4 for every pass of
+ * cand_per_pass candidates, then a5 (msModelSlim 缩放因子搜索流程, in that order).
+ *   x, ld_x, w_parts, part_rows, n_parts, dtype: as above.
+ *   act_mean    device, float64 [d_in] (from awq_act_stats).
+ *   cand_scales device, float64 [n_grid, d_in], written (all candidates).
+ *   losses, best_scales, best_info: as awq_loss_argmin.
+ *   workspace   device, >= awq_search_workspace_bytes(...) bytes. */
+AWQ_API int awq_search_scales(const void* x, int64_t ld_x, const void* const* w_parts,
+                      const int64_t* part_rows, int n_parts, int dtype, int64_t n_tokens,
+                      int64_t d_in, const double* act_mean, int group_size, int n_grid,
+                      int cand_per_pass, double* cand_scales, double* losses,
+                      double* best_scales, int32_t* best_info, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------ a6: final quantize + pack */
+
+/* Quantize y = W * s with the same quantizer and emit, per row o and group j:
+ *   codes[o, c/2]  = q[o, c] | (q[o, c+1] << 4) for even c (uint8, [d_out, d_in/2]),
+ *   qscales[o, j]  = step (float32, [d_out, d_in/128]),
+ *   zeros[o, j]    = zero point (int32, [d_out, d_in/128]; not clamped to [0,15],
+ *                    saturated to the int32 range),
+ * so that W*s ~= (q - zero) * step. s is usually best_scales from the search; the caller
+ * divides the layer input by s (folds diag(s)^-1 into the previous op, gsyq section 四).
+ *   s  device, float64 [d_in]. */
+AWQ_API int awq_quantize_pack(const void* const* w_parts, const int64_t* part_rows, int n_parts, int dtype,
+                      int64_t d_in, int group_size, const double* s, uint8_t* codes,
+                      float* qscales, int32_t* zeros, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* AWQ_MI355X_H */

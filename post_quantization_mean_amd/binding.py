@@ -1,0 +1,277 @@
+"""Thin Python binding of libawq_mi355x.so (include/awq.h).
+
+Every function has the name of the C entry point it calls and only marshals arguments:
+torch supplies device memory (tensors, workspaces) and the stream; every step of the
+computation runs in the library's HIP kernels. If the library is missing the functions
+raise instead of computing anything another way.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libawq_mi355x.so")
+
+AWQ_OK = 0
+AWQ_DTYPE_F32 = 0
+AWQ_DTYPE_BF16 = 1
+AWQ_INFO_ALL_NONFINITE = 1
+AWQ_MAX_PARTS = 8
+GROUP_SIZE = 128
+
+_c_int, _c_i64, _c_size, _vp = ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
+
+# name -> (restype, argtypes)
+_SIGNATURES = {
+    "awq_abi_version": (_c_int, []),
+    "awq_status_string": (ctypes.c_char_p, [_c_int]),
+    "awq_last_error": (ctypes.c_char_p, []),
+    "awq_act_stats_workspace_bytes": (_c_size, [_c_int, _c_i64, _c_i64]),
+    "awq_act_stats": (_c_int, [_vp, _c_int, _c_i64, _c_i64, _c_i64, _vp, _vp, _c_size, _vp]),
+    "awq_candidate_scales": (_c_int, [_vp, _c_i64, _c_int, _vp, _vp]),
+    "awq_quant_delta": (_c_int, [_vp, _vp, _c_int, _c_int, _c_i64, _c_int, _vp, _c_int, _vp, _vp]),
+    "awq_error_tiles": (_c_i64, [_c_i64, _c_i64]),
+    "awq_error_sse": (_c_int, [_vp, _c_i64, _vp, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _vp, _vp]),
+    "awq_loss_argmin": (_c_int, [_vp, _c_i64, _c_int, _c_i64, _c_i64, _vp, _c_i64, _vp, _vp, _vp, _vp]),
+    "awq_search_workspace_bytes": (_c_size, [_c_int, _c_i64, _c_i64, _c_i64, _c_int, _c_int, _c_int]),
+    "awq_search_scales": (_c_int, [_vp, _c_i64, _vp, _vp, _c_int, _c_int, _c_i64, _c_i64, _vp, _c_int,
+                                   _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
+    "awq_quantize_pack": (_c_int, [_vp, _vp, _c_int, _c_int, _c_i64, _c_int, _vp, _vp, _vp, _vp, _vp]),
+}
+
+_lib = None
+
+
+class AwqError(RuntimeError):
+    def __init__(self, status: int, name: str, detail: str):
+        super().__init__(f"{name} ({status}): {detail}")
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Loads the built library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m post_quantization_mean_amd.build` "
+                           "(or __graft_entry__.build()); there is no other implementation")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def exported_symbols() -> list[str]:
+    return list(_SIGNATURES)
+
+
+def _check(status: int) -> None:
+    if status != AWQ_OK:
+        lib = load_library()
+        raise AwqError(status, lib.awq_status_string(status).decode(), lib.awq_last_error().decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return AWQ_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return AWQ_DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: use torch.bfloat16 or torch.float32")
+
+
+def _stream(stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str) -> int:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    return t.data_ptr()
+
+
+def _parts(w_parts):
+    if isinstance(w_parts, torch.Tensor):
+        w_parts = [w_parts]
+    w_parts = list(w_parts)
+    if not w_parts:
+        raise ValueError("no weight parts")
+    for i, w in enumerate(w_parts):
+        if w.dim() != 2 or not w.is_contiguous():
+            raise ValueError(f"weight part {i} must be a contiguous [rows, d_in] matrix")
+    ptrs = (ctypes.c_void_p * len(w_parts))(*[_dev(w, "weight part") for w in w_parts])
+    rows = (ctypes.c_int64 * len(w_parts))(*[w.shape[0] for w in w_parts])
+    return w_parts, ptrs, rows, sum(w.shape[0] for w in w_parts)
+
+
+def _x_args(x: torch.Tensor):
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a [n_tokens, d_in] matrix with unit stride along d_in")
+    return _dev(x, "x"), x.shape[0], x.shape[1], x.stride(0)
+
+
+def _workspace(nbytes: int, device, workspace):
+    if workspace is None:
+        return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    if workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} bytes, {nbytes} needed")
+    return workspace
+
+
+# ------------------------------------------------------------------ entry points
+
+def awq_abi_version() -> int:
+    return load_library().awq_abi_version()
+
+
+def awq_act_stats_workspace_bytes(dtype: int, n_tokens: int, d_in: int) -> int:
+    return load_library().awq_act_stats_workspace_bytes(dtype, n_tokens, d_in)
+
+
+def awq_act_stats(x: torch.Tensor, act_mean: torch.Tensor | None = None, workspace=None, stream=None):
+    """a1: float64 [d_in] mean of |x| over tokens."""
+    lib = load_library()
+    px, n, d, ld = _x_args(x)
+    dt = _dtype_code(x)
+    if act_mean is None:
+        act_mean = torch.empty(d, dtype=torch.float64, device=x.device)
+    ws = _workspace(lib.awq_act_stats_workspace_bytes(dt, n, d), x.device, workspace)
+    _check(lib.awq_act_stats(px, dt, n, d, ld, _dev(act_mean, "act_mean"), ws.data_ptr(),
+                             ws.numel() * ws.element_size(), _stream(stream)))
+    return act_mean
+
+
+def awq_candidate_scales(act_mean: torch.Tensor, n_grid: int, cand_scales=None, stream=None):
+    """a2: float64 [n_grid, d_in] candidate scales."""
+    lib = load_library()
+    d = act_mean.shape[0]
+    if cand_scales is None:
+        cand_scales = torch.empty((n_grid, d), dtype=torch.float64, device=act_mean.device)
+    _check(lib.awq_candidate_scales(_dev(act_mean, "act_mean"), d, n_grid, _dev(cand_scales, "cand_scales"),
+                                    _stream(stream)))
+    return cand_scales
+
+
+def awq_quant_delta(w_parts, cand_scales: torch.Tensor, group_size: int = GROUP_SIZE, delta=None, stream=None):
+    """a3: [n_cand, d_out, d_in] delta = What - W in the weights' dtype."""
+    lib = load_library()
+    parts, ptrs, rows, d_out = _parts(w_parts)
+    d_in = parts[0].shape[1]
+    n_cand = cand_scales.shape[0]
+    if delta is None:
+        delta = torch.empty((n_cand, d_out, d_in), dtype=parts[0].dtype, device=parts[0].device)
+    _check(lib.awq_quant_delta(ptrs, rows, len(parts), _dtype_code(parts[0]), d_in, group_size,
+                               _dev(cand_scales, "cand_scales"), n_cand, _dev(delta, "delta"), _stream(stream)))
+    return delta
+
+
+def awq_error_tiles(n_tokens: int, d_out: int) -> int:
+    return load_library().awq_error_tiles(n_tokens, d_out)
+
+
+def awq_error_sse(x: torch.Tensor, delta: torch.Tensor, tile_sse=None, stream=None):
+    """a4: float64 [n_cand, tiles] per-tile sums of squares of x @ delta_j^T."""
+    lib = load_library()
+    px, n, d, ld = _x_args(x)
+    n_cand, d_out, d_in = delta.shape
+    if d_in != d:
+        raise ValueError("x and delta disagree on d_in")
+    tiles = lib.awq_error_tiles(n, d_out)
+    if tile_sse is None:
+        tile_sse = torch.empty((n_cand, tiles), dtype=torch.float64, device=x.device)
+    _check(lib.awq_error_sse(px, ld, _dev(delta, "delta"), _dtype_code(x), n, d, d_out, n_cand,
+                             _dev(tile_sse, "tile_sse"), _stream(stream)))
+    return tile_sse
+
+
+def awq_loss_argmin(tile_sse: torch.Tensor, n_tokens: int, d_out: int, cand_scales: torch.Tensor,
+                    losses=None, best_scales=None, best_info=None, stream=None):
+    """a5: (losses [n_grid] f64, best_scales [d_in] f64, best_info [2] i32 = {k*, flags})."""
+    lib = load_library()
+    n_grid, tiles = tile_sse.shape
+    d_in = cand_scales.shape[1]
+    dev = tile_sse.device
+    losses = torch.empty(n_grid, dtype=torch.float64, device=dev) if losses is None else losses
+    best_scales = torch.empty(d_in, dtype=torch.float64, device=dev) if best_scales is None else best_scales
+    best_info = torch.empty(2, dtype=torch.int32, device=dev) if best_info is None else best_info
+    _check(lib.awq_loss_argmin(_dev(tile_sse, "tile_sse"), tiles, n_grid, n_tokens, d_out,
+                               _dev(cand_scales, "cand_scales"), d_in, _dev(losses, "losses"),
+                               _dev(best_scales, "best_scales"), _dev(best_info, "best_info"), _stream(stream)))
+    return losses, best_scales, best_info
+
+
+def awq_search_workspace_bytes(dtype: int, n_tokens: int, d_in: int, d_out: int, group_size: int,
+                               n_grid: int, cand_per_pass: int) -> int:
+    return load_library().awq_search_workspace_bytes(dtype, n_tokens, d_in, d_out, group_size, n_grid,
+                                                     cand_per_pass)
+
+
+def awq_search_scales(x: torch.Tensor, w_parts, act_mean: torch.Tensor, n_grid: int = 20,
+                      group_size: int = GROUP_SIZE, cand_per_pass: int | None = None, workspace=None,
+                      out=None, stream=None) -> dict:
+    """a2..a5 in one call. Returns device tensors: cand_scales, losses, best_scales, best_info."""
+    lib = load_library()
+    px, n, d, ld = _x_args(x)
+    parts, ptrs, rows, d_out = _parts(w_parts)
+    dt = _dtype_code(x)
+    if cand_per_pass is None:
+        cand_per_pass = n_grid
+    dev = x.device
+    out = out or {}
+    cand = out.get("cand_scales")
+    if cand is None:
+        cand = torch.empty((n_grid, d), dtype=torch.float64, device=dev)
+    losses = out.get("losses")
+    if losses is None:
+        losses = torch.empty(n_grid, dtype=torch.float64, device=dev)
+    best = out.get("best_scales")
+    if best is None:
+        best = torch.empty(d, dtype=torch.float64, device=dev)
+    info = out.get("best_info")
+    if info is None:
+        info = torch.empty(2, dtype=torch.int32, device=dev)
+    need = lib.awq_search_workspace_bytes(dt, n, d, d_out, group_size, n_grid, cand_per_pass)
+    ws = _workspace(need, dev, workspace)
+    _check(lib.awq_search_scales(px, ld, ptrs, rows, len(parts), dt, n, d, _dev(act_mean, "act_mean"),
+                                 group_size, n_grid, cand_per_pass, cand.data_ptr(), losses.data_ptr(),
+                                 best.data_ptr(), info.data_ptr(), ws.data_ptr(),
+                                 ws.numel() * ws.element_size(), _stream(stream)))
+    return {"cand_scales": cand, "losses": losses, "best_scales": best, "best_info": info}
+
+
+def awq_quantize_pack(w_parts, s: torch.Tensor, group_size: int = GROUP_SIZE, out=None, stream=None) -> dict:
+    """a6: codes [d_out, d_in/2] u8, qscales [d_out, d_in/128] f32, zeros [d_out, d_in/128] i32."""
+    lib = load_library()
+    parts, ptrs, rows, d_out = _parts(w_parts)
+    d_in = parts[0].shape[1]
+    dev = parts[0].device
+    out = out or {}
+    g = d_in // group_size
+    codes = out.get("codes")
+    if codes is None:
+        codes = torch.empty((d_out, d_in // 2), dtype=torch.uint8, device=dev)
+    qs = out.get("qscales")
+    if qs is None:
+        qs = torch.empty((d_out, g), dtype=torch.float32, device=dev)
+    zs = out.get("zeros")
+    if zs is None:
+        zs = torch.empty((d_out, g), dtype=torch.int32, device=dev)
+    _check(lib.awq_quantize_pack(ptrs, rows, len(parts), _dtype_code(parts[0]), d_in, group_size,
+                                 _dev(s, "s"), codes.data_ptr(), qs.data_ptr(), zs.data_ptr(), _stream(stream)))
+    return {"codes": codes, "qscales": qs, "zeros": zs}
+
+
+def awq_layer(x: torch.Tensor, w_parts, n_grid: int = 20, group_size: int = GROUP_SIZE,
+              cand_per_pass: int | None = None, stream=None) -> dict:
+    """The whole hot path for one layer: statistic, search, final quantize + pack."""
+    act_mean = awq_act_stats(x, stream=stream)
+    res = awq_search_scales(x, w_parts, act_mean, n_grid, group_size, cand_per_pass, stream=stream)
+    res.update(awq_quantize_pack(w_parts, res["best_scales"], group_size, stream=stream))
+    res["act_mean"] = act_mean
+    return res

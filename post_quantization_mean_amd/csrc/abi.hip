@@ -1,0 +1,286 @@
+// Host side of the C ABI declared in include/awq.h: argument checks (all before any HIP call),
+// workspace sizing, and the composition of the search from its steps. No allocation happens
+// here; every buffer belongs to the caller.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "awq.h"
+#include "internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return AWQ_OK;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(AWQ_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+size_t esize(int dtype) { return dtype == AWQ_DTYPE_BF16 ? 2 : 4; }
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// byte offsets inside a 256-row tile are 32-bit in the error GEMM's buffer descriptors
+constexpr int64_t kMaxTileBytes = (int64_t)1 << 31;
+
+int check_dtype(int dtype) {
+  if (dtype != AWQ_DTYPE_BF16 && dtype != AWQ_DTYPE_F32)
+    return fail(AWQ_ERR_UNSUPPORTED, "dtype %d is neither AWQ_DTYPE_F32 nor AWQ_DTYPE_BF16", dtype);
+  return AWQ_OK;
+}
+
+int check_group(int group_size, int64_t d_in) {
+  if (group_size != AWQ_GROUP_SIZE)
+    return fail(AWQ_ERR_UNSUPPORTED, "group_size %d: only %d is implemented", group_size, AWQ_GROUP_SIZE);
+  if (d_in <= 0 || d_in % group_size)
+    return fail(AWQ_ERR_SHAPE, "d_in %lld is not a positive multiple of group_size %d", (long long)d_in,
+                group_size);
+  return AWQ_OK;
+}
+
+int check_x(const void* x, int dtype, int64_t n_tokens, int64_t d_in, int64_t ld_x) {
+  if (!x) return fail(AWQ_ERR_NULL, "x is NULL");
+  if (n_tokens < 0) return fail(AWQ_ERR_SHAPE, "n_tokens %lld < 0", (long long)n_tokens);
+  if (n_tokens == 0) return fail(AWQ_ERR_NO_TOKENS, "n_tokens == 0: no activation mean");
+  if (ld_x < d_in) return fail(AWQ_ERR_ARG, "ld_x %lld < d_in %lld", (long long)ld_x, (long long)d_in);
+  if ((ld_x * (int64_t)esize(dtype)) % 16)
+    return fail(AWQ_ERR_UNSUPPORTED, "ld_x * element size must be a multiple of 16 bytes");
+  if (!aligned(x, 16)) return fail(AWQ_ERR_UNSUPPORTED, "x is not 16-byte aligned");
+  if ((int64_t)awq::kTileM * ld_x * (int64_t)esize(dtype) > kMaxTileBytes)
+    return fail(AWQ_ERR_UNSUPPORTED, "ld_x %lld too large for 32-bit tile offsets", (long long)ld_x);
+  return AWQ_OK;
+}
+
+int make_parts(const void* const* w_parts, const int64_t* part_rows, int n_parts, int64_t d_in,
+               awq::WParts* out) {
+  if (!w_parts || !part_rows) return fail(AWQ_ERR_NULL, "w_parts or part_rows is NULL");
+  if (n_parts < 1 || n_parts > AWQ_MAX_PARTS)
+    return fail(AWQ_ERR_ARG, "n_parts %d outside [1, %d]", n_parts, AWQ_MAX_PARTS);
+  memset(out, 0, sizeof *out);
+  out->n = n_parts;
+  int64_t rows = 0;
+  for (int p = 0; p < n_parts; ++p) {
+    if (!w_parts[p]) return fail(AWQ_ERR_NULL, "w_parts[%d] is NULL", p);
+    if (!aligned(w_parts[p], 16)) return fail(AWQ_ERR_UNSUPPORTED, "w_parts[%d] is not 16-byte aligned", p);
+    if (part_rows[p] <= 0) return fail(AWQ_ERR_SHAPE, "part_rows[%d] = %lld must be > 0", p, (long long)part_rows[p]);
+    out->ptr[p] = w_parts[p];
+    out->row_begin[p] = rows;
+    rows += part_rows[p];
+  }
+  for (int p = n_parts; p <= AWQ_MAX_PARTS; ++p) out->row_begin[p] = rows;
+  if (rows > ((int64_t)65535 * 128)) return fail(AWQ_ERR_UNSUPPORTED, "d_out %lld too large", (long long)rows);
+  (void)d_in;
+  return AWQ_OK;
+}
+
+int check_d_in_bytes(int dtype, int64_t d_in) {
+  if ((int64_t)awq::kTileN * d_in * (int64_t)esize(dtype) > kMaxTileBytes)
+    return fail(AWQ_ERR_UNSUPPORTED, "d_in %lld too large for 32-bit tile offsets", (long long)d_in);
+  if (d_in / AWQ_GROUP_SIZE > 65535) return fail(AWQ_ERR_UNSUPPORTED, "d_in %lld too large", (long long)d_in);
+  return AWQ_OK;
+}
+
+#define TRY(expr)              \
+  do {                         \
+    int _s = (expr);           \
+    if (_s != AWQ_OK) return _s; \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int awq_abi_version(void) { return AWQ_ABI_VERSION; }
+
+const char* awq_status_string(int status) {
+  switch (status) {
+    case AWQ_OK: return "AWQ_OK";
+    case AWQ_ERR_NULL: return "AWQ_ERR_NULL";
+    case AWQ_ERR_SHAPE: return "AWQ_ERR_SHAPE";
+    case AWQ_ERR_NO_TOKENS: return "AWQ_ERR_NO_TOKENS";
+    case AWQ_ERR_ARG: return "AWQ_ERR_ARG";
+    case AWQ_ERR_UNSUPPORTED: return "AWQ_ERR_UNSUPPORTED";
+    case AWQ_ERR_WORKSPACE: return "AWQ_ERR_WORKSPACE";
+    case AWQ_ERR_HIP: return "AWQ_ERR_HIP";
+    default: return "AWQ_STATUS_UNKNOWN";
+  }
+}
+
+const char* awq_last_error(void) { return g_err; }
+
+size_t awq_act_stats_workspace_bytes(int dtype, int64_t n_tokens, int64_t d_in) {
+  if ((dtype != AWQ_DTYPE_BF16 && dtype != AWQ_DTYPE_F32) || n_tokens <= 0 || d_in <= 0 ||
+      d_in % AWQ_GROUP_SIZE)
+    return 0;
+  const awq::ActStatsPlan p = awq::act_stats_plan(dtype, n_tokens, d_in);
+  return round_up((size_t)p.row_chunks * (size_t)d_in * sizeof(double), 256);
+}
+
+int awq_act_stats(const void* x, int dtype, int64_t n_tokens, int64_t d_in, int64_t ld_x,
+                  double* act_mean, void* workspace, size_t workspace_bytes, void* stream) {
+  TRY(check_dtype(dtype));
+  TRY(check_group(AWQ_GROUP_SIZE, d_in));
+  TRY(check_x(x, dtype, n_tokens, d_in, ld_x));
+  if (!act_mean) return fail(AWQ_ERR_NULL, "act_mean is NULL");
+  const size_t need = awq_act_stats_workspace_bytes(dtype, n_tokens, d_in);
+  if (!workspace || workspace_bytes < need)
+    return fail(AWQ_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace ? workspace_bytes : 0, need);
+  if (!aligned(workspace, 256)) return fail(AWQ_ERR_UNSUPPORTED, "workspace is not 256-byte aligned");
+  const awq::ActStatsPlan p = awq::act_stats_plan(dtype, n_tokens, d_in);
+  hipError_t e = awq::launch_act_stats(x, dtype, n_tokens, d_in, ld_x, act_mean,
+                                       static_cast<double*>(workspace), p, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "act_stats launch");
+  return ok();
+}
+
+int awq_candidate_scales(const double* act_mean, int64_t d_in, int n_grid, double* cand_scales,
+                         void* stream) {
+  if (!act_mean || !cand_scales) return fail(AWQ_ERR_NULL, "act_mean or cand_scales is NULL");
+  if (d_in <= 0) return fail(AWQ_ERR_SHAPE, "d_in %lld must be > 0", (long long)d_in);
+  if (n_grid < 1 || n_grid > 65535) return fail(AWQ_ERR_ARG, "n_grid %d outside [1, 65535]", n_grid);
+  hipError_t e = awq::launch_candidate_scales(act_mean, d_in, n_grid, cand_scales, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "candidate_scales launch");
+  return ok();
+}
+
+int awq_quant_delta(const void* const* w_parts, const int64_t* part_rows, int n_parts, int dtype,
+                    int64_t d_in, int group_size, const double* cand_scales, int n_cand,
+                    void* delta, void* stream) {
+  TRY(check_dtype(dtype));
+  TRY(check_group(group_size, d_in));
+  TRY(check_d_in_bytes(dtype, d_in));
+  awq::WParts w;
+  TRY(make_parts(w_parts, part_rows, n_parts, d_in, &w));
+  if (!cand_scales || !delta) return fail(AWQ_ERR_NULL, "cand_scales or delta is NULL");
+  if (n_cand < 1) return fail(AWQ_ERR_ARG, "n_cand %d < 1", n_cand);
+  if (!aligned(delta, 16)) return fail(AWQ_ERR_UNSUPPORTED, "delta is not 16-byte aligned");
+  hipError_t e = awq::launch_quant_delta(w, dtype, d_in, cand_scales, n_cand, delta, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "quant_delta launch");
+  return ok();
+}
+
+int64_t awq_error_tiles(int64_t n_tokens, int64_t d_out) {
+  if (n_tokens <= 0 || d_out <= 0) return 0;
+  return ((n_tokens + awq::kTileM - 1) / awq::kTileM) * ((d_out + awq::kTileN - 1) / awq::kTileN);
+}
+
+int awq_error_sse(const void* x, int64_t ld_x, const void* delta, int dtype, int64_t n_tokens,
+                  int64_t d_in, int64_t d_out, int n_cand, double* tile_sse, void* stream) {
+  TRY(check_dtype(dtype));
+  TRY(check_group(AWQ_GROUP_SIZE, d_in));
+  TRY(check_d_in_bytes(dtype, d_in));
+  TRY(check_x(x, dtype, n_tokens, d_in, ld_x));
+  if (!delta || !tile_sse) return fail(AWQ_ERR_NULL, "delta or tile_sse is NULL");
+  if (!aligned(delta, 16)) return fail(AWQ_ERR_UNSUPPORTED, "delta is not 16-byte aligned");
+  if (d_out <= 0) return fail(AWQ_ERR_SHAPE, "d_out %lld must be > 0", (long long)d_out);
+  if (n_cand < 1) return fail(AWQ_ERR_ARG, "n_cand %d < 1", n_cand);
+  const int64_t blocks = awq_error_tiles(n_tokens, d_out) * n_cand;
+  if (blocks > 0x7FFFFFFF) return fail(AWQ_ERR_UNSUPPORTED, "%lld tiles exceed one launch", (long long)blocks);
+  hipError_t e = awq::launch_error_sse(x, ld_x, delta, dtype, n_tokens, d_in, d_out, n_cand, tile_sse,
+                                       (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "error_sse launch");
+  return ok();
+}
+
+int awq_loss_argmin(const double* tile_sse, int64_t tiles_per_cand, int n_grid, int64_t n_tokens,
+                    int64_t d_out, const double* cand_scales, int64_t d_in, double* losses,
+                    double* best_scales, int32_t* best_info, void* stream) {
+  if (!tile_sse || !cand_scales || !losses || !best_scales || !best_info)
+    return fail(AWQ_ERR_NULL, "a required pointer is NULL");
+  if (tiles_per_cand <= 0 || n_tokens <= 0 || d_out <= 0 || d_in <= 0)
+    return fail(AWQ_ERR_SHAPE, "sizes must be > 0");
+  if (n_grid < 1 || n_grid > 65535) return fail(AWQ_ERR_ARG, "n_grid %d outside [1, 65535]", n_grid);
+  hipError_t e = awq::launch_loss_argmin(tile_sse, tiles_per_cand, n_grid, n_tokens, d_out, cand_scales,
+                                         d_in, losses, best_scales, best_info, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "loss_argmin launch");
+  return ok();
+}
+
+size_t awq_search_workspace_bytes(int dtype, int64_t n_tokens, int64_t d_in, int64_t d_out,
+                                  int group_size, int n_grid, int cand_per_pass) {
+  if ((dtype != AWQ_DTYPE_BF16 && dtype != AWQ_DTYPE_F32) || n_tokens <= 0 || d_in <= 0 || d_out <= 0 ||
+      group_size != AWQ_GROUP_SIZE || d_in % group_size || n_grid < 1 || cand_per_pass < 1 ||
+      cand_per_pass > n_grid)
+    return 0;
+  const size_t delta = round_up((size_t)cand_per_pass * (size_t)d_out * (size_t)d_in * esize(dtype), 256);
+  const size_t sse = round_up((size_t)n_grid * (size_t)awq_error_tiles(n_tokens, d_out) * sizeof(double), 256);
+  return delta + sse;
+}
+
+int awq_search_scales(const void* x, int64_t ld_x, const void* const* w_parts,
+                      const int64_t* part_rows, int n_parts, int dtype, int64_t n_tokens,
+                      int64_t d_in, const double* act_mean, int group_size, int n_grid,
+                      int cand_per_pass, double* cand_scales, double* losses,
+                      double* best_scales, int32_t* best_info, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  TRY(check_dtype(dtype));
+  TRY(check_group(group_size, d_in));
+  TRY(check_d_in_bytes(dtype, d_in));
+  TRY(check_x(x, dtype, n_tokens, d_in, ld_x));
+  awq::WParts w;
+  TRY(make_parts(w_parts, part_rows, n_parts, d_in, &w));
+  const int64_t d_out = w.row_begin[w.n];
+  if (!act_mean || !cand_scales || !losses || !best_scales || !best_info)
+    return fail(AWQ_ERR_NULL, "a required pointer is NULL");
+  if (n_grid < 1 || n_grid > 65535) return fail(AWQ_ERR_ARG, "n_grid %d outside [1, 65535]", n_grid);
+  if (cand_per_pass < 1 || cand_per_pass > n_grid)
+    return fail(AWQ_ERR_ARG, "cand_per_pass %d outside [1, n_grid]", cand_per_pass);
+  const int64_t tiles = awq_error_tiles(n_tokens, d_out);
+  if (tiles * cand_per_pass > 0x7FFFFFFF)
+    return fail(AWQ_ERR_UNSUPPORTED, "too many tiles for one launch; lower cand_per_pass");
+  const size_t need = awq_search_workspace_bytes(dtype, n_tokens, d_in, d_out, group_size, n_grid, cand_per_pass);
+  if (!workspace || workspace_bytes < need)
+    return fail(AWQ_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace ? workspace_bytes : 0, need);
+  if (!aligned(workspace, 256)) return fail(AWQ_ERR_UNSUPPORTED, "workspace is not 256-byte aligned");
+
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = static_cast<char*>(workspace);
+  void* delta = ws;
+  double* tile_sse = reinterpret_cast<double*>(
+      ws + round_up((size_t)cand_per_pass * (size_t)d_out * (size_t)d_in * esize(dtype), 256));
+
+  hipError_t e = awq::launch_candidate_scales(act_mean, d_in, n_grid, cand_scales, st);
+  if (e != hipSuccess) return hip_fail(e, "candidate_scales launch");
+  for (int k0 = 0; k0 < n_grid; k0 += cand_per_pass) {
+    const int nk = n_grid - k0 < cand_per_pass ? n_grid - k0 : cand_per_pass;
+    e = awq::launch_quant_delta(w, dtype, d_in, cand_scales + (int64_t)k0 * d_in, nk, delta, st);
+    if (e != hipSuccess) return hip_fail(e, "quant_delta launch");
+    e = awq::launch_error_sse(x, ld_x, delta, dtype, n_tokens, d_in, d_out, nk, tile_sse + (int64_t)k0 * tiles, st);
+    if (e != hipSuccess) return hip_fail(e, "error_sse launch");
+  }
+  e = awq::launch_loss_argmin(tile_sse, tiles, n_grid, n_tokens, d_out, cand_scales, d_in, losses,
+                              best_scales, best_info, st);
+  if (e != hipSuccess) return hip_fail(e, "loss_argmin launch");
+  return ok();
+}
+
+int awq_quantize_pack(const void* const* w_parts, const int64_t* part_rows, int n_parts, int dtype,
+                      int64_t d_in, int group_size, const double* s, uint8_t* codes,
+                      float* qscales, int32_t* zeros, void* stream) {
+  TRY(check_dtype(dtype));
+  TRY(check_group(group_size, d_in));
+  TRY(check_d_in_bytes(dtype, d_in));
+  awq::WParts w;
+  TRY(make_parts(w_parts, part_rows, n_parts, d_in, &w));
+  if (!s || !codes || !qscales || !zeros) return fail(AWQ_ERR_NULL, "s, codes, qscales or zeros is NULL");
+  if (!aligned(codes, 16) || !aligned(qscales, 4) || !aligned(zeros, 4))
+    return fail(AWQ_ERR_UNSUPPORTED, "codes must be 16-byte aligned, qscales and zeros 4-byte aligned");
+  hipError_t e = awq::launch_quantize_pack(w, dtype, d_in, s, codes, qscales, zeros, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "quantize_pack launch");
+  return ok();
+}
+
+}  // extern "C"

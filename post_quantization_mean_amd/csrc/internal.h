@@ -1,0 +1,56 @@
+// Internal declarations shared by the host-side C ABI (abi.hip) and the kernel files.
+// Not part of the public interface (include/awq.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace awq {
+
+constexpr int kMaxParts = 8;
+constexpr int kGroup = 128;  // channels per quantization group (one row, consecutive)
+
+// A fused set of weight matrices whose rows are stacked: part p covers stacked rows
+// [row_begin[p], row_begin[p+1]) and points at a contiguous [rows, d_in] matrix.
+struct WParts {
+  const void* ptr[kMaxParts];
+  int64_t row_begin[kMaxParts + 1];
+  int n;
+};
+
+// ---- a1: activation statistic
+struct ActStatsPlan {
+  int lanes_per_row;   // lanes that cover one row slice (16, 32 or 64)
+  int64_t col_blocks;  // blocks along d_in
+  int64_t row_chunks;  // blocks along n_tokens (partial sums kept per chunk)
+  int64_t rows_per_chunk;
+};
+ActStatsPlan act_stats_plan(int dtype, int64_t n_tokens, int64_t d_in);
+hipError_t launch_act_stats(const void* x, int dtype, int64_t n_tokens, int64_t d_in, int64_t ld_x,
+                            double* act_mean, double* partial, const ActStatsPlan& plan,
+                            hipStream_t stream);
+
+// ---- a2 / a5
+hipError_t launch_candidate_scales(const double* act_mean, int64_t d_in, int n_grid,
+                                   double* cand_scales, hipStream_t stream);
+hipError_t launch_loss_argmin(const double* tile_sse, int64_t tiles_per_cand, int n_grid,
+                              int64_t n_tokens, int64_t d_out, const double* cand_scales,
+                              int64_t d_in, double* losses, double* best_scales,
+                              int32_t* best_info, hipStream_t stream);
+
+// ---- a3 / a6
+hipError_t launch_quant_delta(const WParts& w, int dtype, int64_t d_in, const double* cand_scales,
+                              int n_cand, void* delta, hipStream_t stream);
+hipError_t launch_quantize_pack(const WParts& w, int dtype, int64_t d_in, const double* s,
+                                uint8_t* codes, float* qscales, int32_t* zeros,
+                                hipStream_t stream);
+
+// ---- a4
+constexpr int kTileM = 256;  // tokens per error-GEMM tile
+constexpr int kTileN = 256;  // weight rows per error-GEMM tile
+hipError_t launch_error_sse(const void* x, int64_t ld_x, const void* delta, int dtype,
+                            int64_t n_tokens, int64_t d_in, int64_t d_out, int n_cand,
+                            double* tile_sse, hipStream_t stream);
+
+}  // namespace awq
