@@ -52,9 +52,9 @@ int check_group(int group_size, int64_t d_in) {
 }
 
 int check_x(const void* x, int dtype, int64_t n_tokens, int64_t d_in, int64_t ld_x) {
-  if (!x) return fail(AWQ_ERR_NULL, "x is NULL");
   if (n_tokens < 0) return fail(AWQ_ERR_SHAPE, "n_tokens %lld < 0", (long long)n_tokens);
   if (n_tokens == 0) return fail(AWQ_ERR_NO_TOKENS, "n_tokens == 0: no activation mean");
+  if (!x) return fail(AWQ_ERR_NULL, "x is NULL");
   if (ld_x < d_in) return fail(AWQ_ERR_ARG, "ld_x %lld < d_in %lld", (long long)ld_x, (long long)d_in);
   if ((ld_x * (int64_t)esize(dtype)) % 16)
     return fail(AWQ_ERR_UNSUPPORTED, "ld_x * element size must be a multiple of 16 bytes");
