@@ -88,14 +88,31 @@ __global__ __launch_bounds__(kThreads) void act_stats_partial_kernel(
   }
 }
 
+// One block per 64 channels: wave w adds the chunks w, w+4, w+8, ... of its lane's channel
+// (independent loads, eight in flight), then the four waves are added in order.
 __global__ __launch_bounds__(kThreads) void act_stats_finalize_kernel(
     const double* __restrict__ partial, int64_t n_chunks, int64_t d_in, int64_t n_tokens,
     double* __restrict__ act_mean) {
-  const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (c >= d_in) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t c = (int64_t)blockIdx.x * 64 + lane;
   double s = 0.0;
-  for (int64_t k = 0; k < n_chunks; ++k) s += partial[k * d_in + c];
-  act_mean[c] = s / (double)n_tokens;
+  if (c < d_in) {
+    int64_t k = wave;
+    for (; k + 28 < n_chunks; k += 32) {
+      double v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = partial[(k + 4 * i) * d_in + c];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s += v[i];
+    }
+    for (; k < n_chunks; k += 4) s += partial[k * d_in + c];
+  }
+  __shared__ double red[kThreads / 64][64];
+  red[wave][lane] = s;
+  __syncthreads();
+  if (wave == 0 && c < d_in)
+    act_mean[c] = (((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane]) / (double)n_tokens;
 }
 
 template <typename T, int LC>
@@ -116,8 +133,9 @@ ActStatsPlan act_stats_plan(int dtype, int64_t n_tokens, int64_t d_in) {
   p.lanes_per_row = (vec_lanes % 64 == 0) ? 64 : (vec_lanes % 32 == 0) ? 32 : 16;
   p.col_blocks = d_in / (p.lanes_per_row * vec);
   const int64_t rows_per_iter = (64 / p.lanes_per_row) * (kThreads / 64);
-  // aim for ~2048 blocks (8 per CU) while keeping >= kUnroll row steps per block
-  const int64_t max_chunks = (n_tokens + rows_per_iter * kUnroll - 1) / (rows_per_iter * kUnroll);
+  // aim for ~2048 blocks (8 per CU) while giving every block >= 64 rows
+  const int64_t min_rows = rows_per_iter * kUnroll > 64 ? rows_per_iter * kUnroll : 64;
+  const int64_t max_chunks = (n_tokens + min_rows - 1) / min_rows;
   int64_t chunks = (2048 + p.col_blocks - 1) / p.col_blocks;
   if (chunks > max_chunks) chunks = max_chunks;
   if (chunks < 1) chunks = 1;
@@ -144,7 +162,7 @@ hipError_t launch_act_stats(const void* x, int dtype, int64_t n_tokens, int64_t 
                                 : launch_partial<float, 16>(x, ld_x, n_tokens, d_in, partial, p, st);
   }
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(act_stats_finalize_kernel, dim3((unsigned)((d_in + kThreads - 1) / kThreads)),
+  hipLaunchKernelGGL(act_stats_finalize_kernel, dim3((unsigned)((d_in + 63) / 64)),
                      dim3(kThreads), 0, st, partial, p.row_chunks, d_in, n_tokens, act_mean);
   return hipGetLastError();
 }

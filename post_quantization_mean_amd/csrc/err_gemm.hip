@@ -8,14 +8,15 @@
 // reduction runs in the GEMM epilogue on the accumulators.
 //
 // Both operands are K-contiguous ([rows, d_in] row-major): M = tokens, N = candidate rows
-// (candidates stacked along N), K = d_in. Tiles are 256 x 256 with a K step of 128 bytes
-// (64 bf16 / 32 f32), four waves in a 2 x 2 arrangement, each wave a 128 x 128 sub-tile held as
-// 8 x 8 accumulators of the 16x16 matrix-core instruction (v_mfma_f32_16x16x32_bf16 for bf16,
-// v_mfma_f32_16x16x4_f32 for f32). Operands move global -> LDS with buffer loads that write LDS
+// (candidates stacked along N), K = d_in. Tiles are 256 x 256 with a K step of 64 bytes
+// (32 bf16 / 16 f32), four waves in a 2 x 2 arrangement, each wave a 128 x 128 sub-tile held as
+// 4 x 4 accumulators of the 32x32 matrix-core instruction (v_mfma_f32_32x32x16_bf16 for bf16,
+// v_mfma_f32_32x32x2_f32 for f32). Operands move global -> LDS with buffer loads that write LDS
 // directly (16 bytes per lane); rows past the end of X or of a candidate's delta lie outside the
-// buffer's range and read as zero, which adds nothing to a sum of squares. Two LDS stages hold
-// the next K step while the current one is consumed. The 16-byte chunks of each 128-byte LDS row
-// are XOR-swizzled by row so that the 16 lanes of a fragment read hit distinct banks.
+// buffer's range and read as zero, which adds nothing to a sum of squares. A ring of five LDS
+// stages (all 160 KiB) keeps four K steps of loads in flight while one is consumed, enough to
+// cover the latency of the L2 / Infinity-cache / HBM path. The 16-byte chunks of each LDS row
+// are XOR-swizzled by row so that any 16 consecutive lanes of a fragment read hit distinct banks.
 //
 // Tile order: workgroups are dealt round-robin to the 8 XCDs, so block ids are first mapped to
 // a contiguous logical range per XCD, then that range walks groups of 8 token tiles across all
@@ -28,64 +29,136 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int BM = kTileM, BN = kTileN;
-constexpr int KB = 128;                      // bytes of K per LDS row per stage
-constexpr int kStageBytes = (BM + BN) * KB;  // 64 KiB
-constexpr int kLdsBytes = 2 * kStageBytes;   // 128 KiB of the 160 KiB per CU
-constexpr int kGroupM = 8;
+constexpr int KB = 64;                       // bytes of K per LDS row per stage (32 bf16 / 16 f32)
+constexpr int kStageBytes = (BM + BN) * KB;  // 32 KiB
+#ifndef AWQ_GEMM_STAGES
+#define AWQ_GEMM_STAGES 5
+#endif
+constexpr int kStages = AWQ_GEMM_STAGES;     // ring of stages; kStages - 1 in flight
+constexpr int kLdsBytes = kStages * kStageBytes;  // 160 KiB: all of a CU's LDS
+constexpr int kLoadsPerStage = 8;            // buffer->LDS loads per wave per stage (4 A + 4 B)
+#ifndef AWQ_GEMM_GROUP_M
+#define AWQ_GEMM_GROUP_M 8
+#endif
+constexpr int kGroupM = AWQ_GEMM_GROUP_M;  // token tiles per group of the tile order
 constexpr int kXcds = 8;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+// 16-byte slot of K chunk c in LDS row r is c ^ swz(r): any 16 consecutive rows read at the same
+// chunk then cover all 64 banks, and any 8 consecutive rows cover distinct 128-byte halves.
+__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
 
-// Issue the 8 buffer->LDS loads that fill one operand's 256 x 128-byte stage slice.
-// Wave w, load j covers LDS rows 8*(4j+w) .. +7; lane i of it fills row 8*(4j+w) + i/8,
-// 16-byte slot i%8, which holds K chunk (i%8) ^ swz(row).
-template <int ESZ>
-__device__ __forceinline__ void load_stage(__amdgpu_buffer_rsrc_t rsrc, char* lds_stage, int ld_bytes,
-                                           int k_byte, int wave, int lane) {
+// s_waitcnt immediate for "at most n vector-memory operations outstanding" (gfx9 encoding;
+// expcnt and lgkmcnt left at their maxima).
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+// Per-lane byte offsets of the 4 buffer->LDS loads that fill one operand's 256 x 64-byte stage
+// slice. Wave w, load j covers LDS rows 16*(4j+w) .. +15; lane i of it fills row 16*(4j+w) + i/4,
+// 16-byte slot i%4, which holds K chunk (i%4) ^ swz(row). The K position of the stage is added
+// as the scalar offset at issue time.
+__device__ __forceinline__ void load_offsets(int ld_bytes, int wave, int lane, int (&voff)[4]) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int rb = 4 * j + wave;
-    const int row = rb * 8 + (lane >> 3);
-    const int chunk = (lane & 7) ^ swz(row);
-    const int voff = row * ld_bytes + k_byte + chunk * 16;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(lds_stage + rb * 8 * KB), 16, voff, 0, 0, 0);
+  for (int j = 0; j < 4; ++j) {
+    const int row = (4 * j + wave) * 16 + (lane >> 2);
+    voff[j] = row * ld_bytes + (((lane & 3) ^ swz(row)) << 4);
+  }
+}
+
+// One 16-byte-per-lane buffer load that writes LDS directly (M0 = the wave's LDS destination).
+// It is issued from inline assembly so that the compiler does not treat it as a possible
+// writer of every later LDS read and wait for it there: this kernel synchronises the stages
+// itself (s_waitcnt vmcnt + barrier). The instruction has no register results. M0 is set in
+// the same statement; nothing else in this kernel uses M0 (no LDS-DMA builtins, GWS or
+// message sends), so the compiler holds no value there across it.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void dma_load16(i32x4 rsrc, uint32_t lds_addr, int voff, int soff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "buffer_load_dwordx4 %1, %2, %3 offen lds"
+      :
+      : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff)
+      : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_address(const char* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// lds_stage: LDS byte address of the operand's slice in the stage (wave-uniform).
+__device__ __forceinline__ void load_stage(i32x4 rsrc, uint32_t lds_stage, const int (&voff)[4], int k_byte,
+                                           int wave) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    dma_load16(rsrc, __builtin_amdgcn_readfirstlane(lds_stage + (4 * j + wave) * 16 * KB), voff[j], k_byte);
+}
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Raw buffer descriptor (gfx9 layout): 48-bit base, stride 0, num_records bytes; reads at byte
+// offsets >= num_records return zero. Word 3 selects 32-bit data format, no swizzle.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, int num_records) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  i32x4 r;
+  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xFFFF);
+  r.z = __builtin_amdgcn_readfirstlane(num_records);
+  r.w = 0x00020000;
+  return r;
+}
+
+// One 16-byte fragment pair: a 32 x 32 x (16 bf16 | 8 f32) product into one accumulator.
+template <typename T>
+__device__ __forceinline__ void mma_pair(const uint4& a, const uint4& b, f32x16& c) {
+  if constexpr (sizeof(T) == 2) {
+    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                0, 0, 0);
+  } else {
+    // four K=2 steps; lane half h contributes K index 4h+e of the 8-wide chunk pair in step e,
+    // identically for both operands
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
   }
 }
 
 template <typename T>
-__device__ __forceinline__ void mma_chunk(const uint4 (&a)[8], const uint4 (&b)[8], f32x4 (&acc)[8][8]) {
+__device__ __forceinline__ void mma_all(const uint4 (&a)[4], const uint4 (&b)[4], f32x16 (&acc)[4][4]) {
 #pragma unroll
-  for (int fm = 0; fm < 8; ++fm) {
+  for (int fm = 0; fm < 4; ++fm)
 #pragma unroll
-    for (int fn = 0; fn < 8; ++fn) {
-      if constexpr (sizeof(T) == 2) {
-        acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[fm]),
-                                                              __builtin_bit_cast(bf16x8, b[fn]),
-                                                              acc[fm][fn], 0, 0, 0);
-      } else {
-        // four K=4 steps; lane group g contributes K index 4g+e of the 16-wide chunk in step e,
-        // identically for both operands
-        acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[fm].x), __uint_as_float(b[fn].x), acc[fm][fn], 0, 0, 0);
-        acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[fm].y), __uint_as_float(b[fn].y), acc[fm][fn], 0, 0, 0);
-        acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[fm].z), __uint_as_float(b[fn].z), acc[fm][fn], 0, 0, 0);
-        acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[fm].w), __uint_as_float(b[fn].w), acc[fm][fn], 0, 0, 0);
-      }
-    }
+    for (int fn = 0; fn < 4; ++fn) mma_pair<T>(a[fm], b[fn], acc[fm][fn]);
+}
+
+// The 8 fragment reads of one 32-byte K sub-step (two per 64-byte stage row): rows f*32 + lane%32
+// of the wave's A and B strips; pa / pb already hold the lane's row and swizzled slot, so each read is an immediate
+// offset of f * 32 rows.
+__device__ __forceinline__ void read_frags(const char* pa, const char* pb, uint4 (&a)[4], uint4 (&b)[4]) {
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    a[f] = *reinterpret_cast<const uint4*>(pa + f * 32 * KB);
+    b[f] = *reinterpret_cast<const uint4*>(pb + f * 32 * KB);
   }
 }
+
+// Scheduling hint: spread n_ds fragment reads evenly among n_mfma matrix instructions.
+#define SCHED_INTERLEAVE(n_mfma, n_ds)                                 \
+  _Pragma("unroll") for (int _i = 0; _i < (n_ds); ++_i) {              \
+    __builtin_amdgcn_sched_group_barrier(0x008, (n_mfma) / (n_ds), 0); \
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                 \
+  }
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void error_sse_kernel(const T* __restrict__ x, int64_t ld_x, const T* __restrict__ delta,
                       int64_t n_tokens, int64_t d_in, int64_t d_out, int tiles_m, int tiles_n,
                       int n_cols, double* __restrict__ tile_sse) {
+  constexpr int MPP = sizeof(T) == 2 ? 1 : 4;  // matrix instructions per fragment pair
   __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
   // ---- block id -> (candidate, token tile, row tile)
   const int nblk = gridDim.x;
@@ -108,71 +181,115 @@ void error_sse_kernel(const T* __restrict__ x, int64_t ld_x, const T* __restrict
   const int rows_a = (int)min((int64_t)BM, n_tokens - m0);
   const int rows_b = (int)min((int64_t)BN, d_out - n0);
   const int lda_bytes = (int)(ld_x * (int64_t)sizeof(T));
-  const int ldb_bytes = (int)(d_in * (int64_t)sizeof(T));
   const int row_bytes = (int)(d_in * (int64_t)sizeof(T));
   const T* a_base = x + m0 * ld_x;
   const T* b_base = delta + ((int64_t)cand * d_out + n0) * d_in;
-  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)a_base, 0, (rows_a - 1) * lda_bytes + row_bytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)b_base, 0, (rows_b - 1) * ldb_bytes + row_bytes, 0x00020000);
+  const i32x4 ra = make_rsrc(a_base, (rows_a - 1) * lda_bytes + row_bytes);
+  const i32x4 rb = make_rsrc(b_base, (rows_b - 1) * row_bytes + row_bytes);
+  int voff_a[4], voff_b[4];
+  load_offsets(lda_bytes, wave, lane, voff_a);
+  load_offsets(row_bytes, wave, lane, voff_b);
 
-
-  f32x4 acc[8][8];
+  f32x16 acc[4][4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
+  // The lane's fragment row and swizzled 16-byte slot for sub-steps 0 and 1 of a stage: row
+  // 32f + lane%32 of the wave's strip, K chunk 2s + lane/32. swz(row) depends only on
+  // lane % 16, because fragment rows start at multiples of 32.
   const int wm = wave >> 1, wn = wave & 1;
-  const int fr = lane & 15;  // row within a 16-row fragment
-  const int fg = lane >> 4;  // 16-byte K chunk within a 64-byte sub-step
-  const int k_steps = row_bytes / KB;
+  const int fr = lane & 31;
+  const int fh = lane >> 5;
+  const int ra_off = (wm * 128 + fr) * KB;
+  const int rb_off = BM * KB + (wn * 128 + fr) * KB;
+  const int slot0 = ((0 + fh) ^ swz(fr)) << 4;
+  const int slot1 = ((2 + fh) ^ swz(fr)) << 4;
+  const int k_steps = row_bytes / KB;  // >= 4: d_in is a positive multiple of 128
 
-  load_stage<sizeof(T)>(ra, lds, lda_bytes, 0, wave, lane);
-  load_stage<sizeof(T)>(rb, lds + BM * KB, ldb_bytes, 0, wave, lane);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  // Pipeline over a ring of kStages LDS stages, one K step (two 32 x 32 x 16 sub-steps) each.
+  // Per K step kt:
+  //   phase 1: sub-step 0's MFMAs run while sub-step 1's fragments are read from LDS;
+  //   wait until stage kt+1 has landed (the kStages-2 younger stages may stay in flight) and
+  //   barrier, after which every wave is also done reading stage kt-1;
+  //   issue the loads of stage kt+kStages-1 into that freed buffer;
+  //   phase 2: sub-step 1's MFMAs run while stage kt+1's first fragments are read.
+  // So kStages-1 stages of loads are in flight while the matrix cores work, and no fragment
+  // read is waited on. The loop without loads at the end waits for everything instead.
+  uint4 fa0[4], fb0[4], fa1[4], fb1[4];
+  const uint32_t lds_base = __builtin_amdgcn_readfirstlane(lds_address(lds));
+  static_assert(kStages >= 3 && kStages <= 5, "the prologue fills kStages-1 <= 4 <= k_steps stages");
+#pragma unroll
+  for (int q = 0; q < kStages - 1; ++q) {
+    load_stage(ra, lds_base + q * kStageBytes, voff_a, q * KB, wave);
+    load_stage(rb, lds_base + q * kStageBytes + BM * KB, voff_b, q * KB, wave);
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm((kStages - 2) * kLoadsPerStage));  // stage 0 has landed
   __syncthreads();
+  read_frags(lds + ra_off + slot0, lds + rb_off + slot0, fa0, fb0);
 
-  for (int kt = 0; kt < k_steps; ++kt) {
-    const int st = kt & 1;
-    if (kt + 1 < k_steps) {
-      char* nxt = lds + (st ^ 1) * kStageBytes;
-      load_stage<sizeof(T)>(ra, nxt, lda_bytes, (kt + 1) * KB, wave, lane);
-      load_stage<sizeof(T)>(rb, nxt + BM * KB, ldb_bytes, (kt + 1) * KB, wave, lane);
-    }
-    const char* As = lds + st * kStageBytes;
-    const char* Bs = As + BM * KB;
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      uint4 a[8], b[8];
-      const int chunk = s * 4 + fg;
-#pragma unroll
-      for (int f = 0; f < 8; ++f) {
-        const int ra_row = wm * 128 + f * 16 + fr;
-        const int rb_row = wn * 128 + f * 16 + fr;
-        a[f] = *reinterpret_cast<const uint4*>(As + ra_row * KB + ((chunk ^ swz(ra_row)) << 4));
-        b[f] = *reinterpret_cast<const uint4*>(Bs + rb_row * KB + ((chunk ^ swz(rb_row)) << 4));
-      }
-      mma_chunk<T>(a, b, acc);
-    }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's loads of the next stage have landed
+  int kt = 0;
+  int buf = 0;  // kt % kStages
+  for (; kt + kStages - 1 < k_steps; ++kt) {
+    char* cur = lds + buf * kStageBytes;
+    const int nbuf = buf + 1 == kStages ? 0 : buf + 1;
+    const int fbuf = buf == 0 ? kStages - 1 : buf - 1;
+    char* nxt = lds + nbuf * kStageBytes;
+    const uint32_t fre = lds_base + fbuf * kStageBytes;
+    read_frags(cur + ra_off + slot1, cur + rb_off + slot1, fa1, fb1);
+    mma_all<T>(fa0, fb0, acc);
+    SCHED_INTERLEAVE(16 * MPP, 8)
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((kStages - 2) * kLoadsPerStage));
     __syncthreads();
+    load_stage(ra, fre, voff_a, (kt + kStages - 1) * KB, wave);
+    load_stage(rb, fre + BM * KB, voff_b, (kt + kStages - 1) * KB, wave);
+    read_frags(nxt + ra_off + slot0, nxt + rb_off + slot0, fa0, fb0);
+    mma_all<T>(fa1, fb1, acc);
+    SCHED_INTERLEAVE(16 * MPP, 8)
+    buf = nbuf;
+  }
+  for (; kt < k_steps - 1; ++kt) {
+    char* cur = lds + buf * kStageBytes;
+    const int nbuf = buf + 1 == kStages ? 0 : buf + 1;
+    char* nxt = lds + nbuf * kStageBytes;
+    read_frags(cur + ra_off + slot1, cur + rb_off + slot1, fa1, fb1);
+    mma_all<T>(fa0, fb0, acc);
+    SCHED_INTERLEAVE(16 * MPP, 8)
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();
+    read_frags(nxt + ra_off + slot0, nxt + rb_off + slot0, fa0, fb0);
+    mma_all<T>(fa1, fb1, acc);
+    SCHED_INTERLEAVE(16 * MPP, 8)
+    buf = nbuf;
+  }
+  {  // K step k_steps-1
+    char* cur = lds + buf * kStageBytes;
+    read_frags(cur + ra_off + slot1, cur + rb_off + slot1, fa1, fb1);
+    mma_all<T>(fa0, fb0, acc);
+    SCHED_INTERLEAVE(16 * MPP, 8)
+    mma_all<T>(fa1, fb1, acc);
   }
 
   // ---- epilogue: sum of squares of the 128 x 128 wave tile, float64
+  // one accumulator tile row at a time, so only 64 values leave the accumulator registers at once
   double ss = 0.0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
+      for (int e = 0; e < 16; ++e) {
         const double v = (double)acc[i][j][e];
         ss = fma(v, v, ss);
       }
+    __builtin_amdgcn_sched_barrier(0);
+  }
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
+  __syncthreads();  // every wave is done reading the last stage before LDS is reused
   double* red = reinterpret_cast<double*>(lds);
   if (lane == 0) red[wave] = ss;
   __syncthreads();

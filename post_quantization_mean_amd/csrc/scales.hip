@@ -13,11 +13,12 @@ namespace awq {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kScaleThreads = 1024;
 
 // One block per ratio. The clamped powers are written first, then divided by the
 // normaliser once the block knows the maximum and minimum. NaN in any channel makes the
 // normaliser NaN (the maximum and minimum of a vector holding NaN are NaN).
-__global__ __launch_bounds__(kThreads) void candidate_scales_kernel(const double* __restrict__ a,
+__global__ __launch_bounds__(kScaleThreads) void candidate_scales_kernel(const double* __restrict__ a,
                                                                     int64_t d_in, int n_grid,
                                                                     double* __restrict__ out) {
   const int k = blockIdx.x;
@@ -25,7 +26,7 @@ __global__ __launch_bounds__(kThreads) void candidate_scales_kernel(const double
   double* row = out + (int64_t)k * d_in;
   double mx = -INFINITY, mn = INFINITY;
   int has_nan = 0;
-  for (int64_t c = threadIdx.x; c < d_in; c += kThreads) {
+  for (int64_t c = threadIdx.x; c < d_in; c += kScaleThreads) {
     double v = (k == 0) ? 1.0 : pow(a[c], r);
     if (!(v != v) && v < 1e-4) v = 1e-4;
     row[c] = v;
@@ -36,13 +37,13 @@ __global__ __launch_bounds__(kThreads) void candidate_scales_kernel(const double
       mn = fmin(mn, v);
     }
   }
-  __shared__ double smx[kThreads], smn[kThreads];
-  __shared__ int snan[kThreads];
+  __shared__ double smx[kScaleThreads], smn[kScaleThreads];
+  __shared__ int snan[kScaleThreads];
   smx[threadIdx.x] = mx;
   smn[threadIdx.x] = mn;
   snan[threadIdx.x] = has_nan;
   __syncthreads();
-  for (int s = kThreads / 2; s > 0; s >>= 1) {
+  for (int s = kScaleThreads / 2; s > 0; s >>= 1) {
     if (threadIdx.x < s) {
       smx[threadIdx.x] = fmax(smx[threadIdx.x], smx[threadIdx.x + s]);
       smn[threadIdx.x] = fmin(smn[threadIdx.x], smn[threadIdx.x + s]);
@@ -51,7 +52,7 @@ __global__ __launch_bounds__(kThreads) void candidate_scales_kernel(const double
     __syncthreads();
   }
   const double norm = snan[0] ? (double)NAN : sqrt(smx[0] * smn[0]);
-  for (int64_t c = threadIdx.x; c < d_in; c += kThreads) row[c] = row[c] / norm;
+  for (int64_t c = threadIdx.x; c < d_in; c += kScaleThreads) row[c] = row[c] / norm;
 }
 
 // One block per ratio: the fixed-order float64 sum of that ratio's tile sums.
@@ -101,7 +102,7 @@ __global__ __launch_bounds__(kThreads) void argmin_kernel(const double* __restri
 
 hipError_t launch_candidate_scales(const double* act_mean, int64_t d_in, int n_grid,
                                    double* cand_scales, hipStream_t st) {
-  hipLaunchKernelGGL(candidate_scales_kernel, dim3(n_grid), dim3(kThreads), 0, st, act_mean, d_in,
+  hipLaunchKernelGGL(candidate_scales_kernel, dim3(n_grid), dim3(kScaleThreads), 0, st, act_mean, d_in,
                      n_grid, cand_scales);
   return hipGetLastError();
 }
