@@ -46,9 +46,10 @@ constexpr int kXcds = 8;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-// 16-byte slot of K chunk c in LDS row r is c ^ swz(r): any 16 consecutive rows read at the same
-// chunk then cover all 64 banks, and any 8 consecutive rows cover distinct 128-byte halves.
-__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+// 16-byte slot of K chunk c in a 64-byte LDS row r is c ^ swz(r). With this choice the fragment
+// reads below (lane l: row l%32, chunk 2s + l/32) show no LDS bank-conflict cycles on gfx950
+// (SQ_LDS_BANK_CONFLICT = 0); the other permutations tried stall 50-75% of LDS cycles.
+__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
 
 // s_waitcnt immediate for "at most n vector-memory operations outstanding" (gfx9 encoding;
 // expcnt and lgkmcnt left at their maxima).
@@ -213,15 +214,15 @@ void error_sse_kernel(const T* __restrict__ x, int64_t ld_x, const T* __restrict
   // Pipeline over a ring of kStages LDS stages, one K step (two 32 x 32 x 16 sub-steps) each.
   // Per K step kt:
   //   phase 1: sub-step 0's MFMAs run while sub-step 1's fragments are read from LDS;
-  //   wait until stage kt+1 has landed (the kStages-2 younger stages may stay in flight) and
-  //   barrier, after which every wave is also done reading stage kt-1;
-  //   issue the loads of stage kt+kStages-1 into that freed buffer;
-  //   phase 2: sub-step 1's MFMAs run while stage kt+1's first fragments are read.
+  //   wait until stage kt+1 has landed (the kStages-3 younger stages already issued may stay in
+  //   flight) and barrier, after which every wave is also done reading stage kt-1;
+  //   phase 2: sub-step 1's MFMAs run while the loads of stage kt+kStages-1 go into that freed
+  //   buffer and stage kt+1's first fragments are read.
   // So kStages-1 stages of loads are in flight while the matrix cores work, and no fragment
   // read is waited on. The loop without loads at the end waits for everything instead.
   uint4 fa0[4], fb0[4], fa1[4], fb1[4];
   const uint32_t lds_base = __builtin_amdgcn_readfirstlane(lds_address(lds));
-  static_assert(kStages >= 3 && kStages <= 5, "the prologue fills kStages-1 <= 4 <= k_steps stages");
+  static_assert(kStages >= 4 && kStages <= 5, "the prologue fills kStages-1 <= 4 <= k_steps stages");
 #pragma unroll
   for (int q = 0; q < kStages - 1; ++q) {
     load_stage(ra, lds_base + q * kStageBytes, voff_a, q * KB, wave);
@@ -239,16 +240,31 @@ void error_sse_kernel(const T* __restrict__ x, int64_t ld_x, const T* __restrict
     const int fbuf = buf == 0 ? kStages - 1 : buf - 1;
     char* nxt = lds + nbuf * kStageBytes;
     const uint32_t fre = lds_base + fbuf * kStageBytes;
+    const int kload = (kt + kStages - 1) * KB;
     read_frags(cur + ra_off + slot1, cur + rb_off + slot1, fa1, fb1);
     mma_all<T>(fa0, fb0, acc);
     SCHED_INTERLEAVE(16 * MPP, 8)
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm((kStages - 2) * kLoadsPerStage));
+    // stages kt+1 .. kt+kStages-2 are in flight; kt+1 must have landed
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((kStages - 3) * kLoadsPerStage));
     __syncthreads();
-    load_stage(ra, fre, voff_a, (kt + kStages - 1) * KB, wave);
-    load_stage(rb, fre + BM * KB, voff_b, (kt + kStages - 1) * KB, wave);
-    read_frags(nxt + ra_off + slot0, nxt + rb_off + slot0, fa0, fb0);
-    mma_all<T>(fa1, fb1, acc);
-    SCHED_INTERLEAVE(16 * MPP, 8)
+    // sub-step 1's MFMAs, with the 8 loads of stage kt+kStages-1 and the 8 fragment reads of
+    // stage kt+1's sub-step 0 placed between them (a burst of loads would stall MFMA issue)
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      const int fm = g >> 1;
+      mma_pair<T>(fa1[fm], fb1[(g & 1) * 2], acc[fm][(g & 1) * 2]);
+      mma_pair<T>(fa1[fm], fb1[(g & 1) * 2 + 1], acc[fm][(g & 1) * 2 + 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (g < 4) {
+        dma_load16(ra, __builtin_amdgcn_readfirstlane(fre + (4 * g + wave) * 16 * KB), voff_a[g], kload);
+        fa0[g] = *reinterpret_cast<const uint4*>(nxt + ra_off + slot0 + g * 32 * KB);
+      } else {
+        dma_load16(rb, __builtin_amdgcn_readfirstlane(fre + BM * KB + (4 * (g - 4) + wave) * 16 * KB),
+                   voff_b[g - 4], kload);
+        fb0[g - 4] = *reinterpret_cast<const uint4*>(nxt + rb_off + slot0 + (g - 4) * 32 * KB);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
     buf = nbuf;
   }
   for (; kt < k_steps - 1; ++kt) {
