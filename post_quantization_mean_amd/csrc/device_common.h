@@ -48,41 +48,75 @@ __device__ __forceinline__ void store8(float* p, const float (&v)[8]) {
   *reinterpret_cast<f32x4*>(p + 4) = b;
 }
 
-// Step, zero point and reciprocal step of one 128-channel group. The 16 lanes of a row
-// slice (lanes 16j .. 16j+15 of a wave) each hold 8 consecutive values y of the group.
-struct GroupStep {
-  double step, zero, inv;
-};
+// ---- the quantizer on one row of one 128-channel group held by 8 lanes x 16 channels
 
-__device__ __forceinline__ GroupStep group_step16(const double (&y)[8]) {
-  double mn = y[0], mx = y[0];
+// 64-bit lane exchange inside groups of 8 lanes (DPP quad permutes and the half-row mirror).
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+  return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within each 8 lanes
+
+constexpr int kDppRowMirror = 0x140;  // lane i <-> 15-i within each 16 lanes
+
+// Minimum and maximum of the group's 128 values, held as E values per lane by 128/E
+// consecutive lanes (all 64 lanes must execute this).
+template <int E>
+__device__ __forceinline__ void group_minmax(const double (&y)[E], double& mn, double& mx) {
+  static_assert(E == 8 || E == 16, "8 or 16 channels per lane");
+  mn = y[0];
+  mx = y[0];
 #pragma unroll
-  for (int j = 1; j < 8; ++j) {
+  for (int j = 1; j < E; ++j) {
     mn = fmin(mn, y[j]);
     mx = fmax(mx, y[j]);
   }
-#pragma unroll
-  for (int m = 8; m >= 1; m >>= 1) {
-    mn = fmin(mn, __shfl_xor(mn, m, 16));
-    mx = fmax(mx, __shfl_xor(mx, m, 16));
+  mn = fmin(mn, dpp_f64<kDppXor1>(mn));
+  mx = fmax(mx, dpp_f64<kDppXor1>(mx));
+  mn = fmin(mn, dpp_f64<kDppXor2>(mn));
+  mx = fmax(mx, dpp_f64<kDppXor2>(mx));
+  mn = fmin(mn, dpp_f64<kDppHalfMirror>(mn));
+  mx = fmax(mx, dpp_f64<kDppHalfMirror>(mx));
+  if constexpr (E == 8) {
+    mn = fmin(mn, dpp_f64<kDppRowMirror>(mn));
+    mx = fmax(mx, dpp_f64<kDppRowMirror>(mx));
   }
-  GroupStep g;
-  double st = (mx - mn) / 15.0;       // 16 levels between the group's extremes
-  g.step = st < 1e-8 ? 1e-8 : st;     // floor on the step (NaN passes through)
-  g.zero = rint(-mn / g.step);        // zero point, round half to even, not clamped
-  g.inv = 1.0 / g.step;
-  return g;
 }
 
-// Code of one value: clip(round(y / step) + zero, 0, 15), round half to even. y * (1/step)
-// is within two ulps of the correctly rounded quotient, so it decides every value that is
-// not within 1e-6 of a half-integer; those few use the exactly rounded y / step, which makes
-// the result identical to evaluating the definition in float64.
-__device__ __forceinline__ double quant_code(double y, const GroupStep& g) {
-  double t = y * g.inv;
-  double r = rint(t);
-  if (fabs(t - r) > 0.5 - 1e-6) r = rint(y / g.step);
-  double q = r + g.zero;
+// 1/x to within an ulp: hardware estimate plus one Newton step.
+__device__ __forceinline__ double rcp_nr(double x) {
+  const double r = __builtin_amdgcn_rcp(x);
+  return fma(r, fma(-x, r, 1.0), r);
+}
+
+// The group's step (max - min)/15 floored at 1e-8, exactly as the definition divides.
+__device__ __forceinline__ double group_step(double mn, double mx) {
+  const double st = (mx - mn) / 15.0;
+  return st < 1e-8 ? 1e-8 : st;  // NaN passes through
+}
+
+// How far the quantizer's decisions may be from a rounding tie before the fast path, which
+// uses y * (1/step) instead of y / step, is no longer guaranteed to decide like the exact
+// float64 quotient (the two differ by a few ulps; the fast path is only taken for values of
+// magnitude below about 1e6, where that is below 1e-9).
+constexpr double kTieGuard = 0.5 - 1e-6;
+
+// Fast-path preconditions for a group: the zero point -min/step is not within 1e-6 of a
+// half-integer, is below 1e6 in magnitude, and the step is not the floor. Then every code round(y/step) + zero lies in
+// [0, 15] without clamping (the minimum maps to 0 and the maximum to 15 or less), so
+// q - zero = round(t) for every element.
+__device__ __forceinline__ bool group_fast_ok(double zt, double zr, double step) {
+  return fabs(zt - zr) <= kTieGuard && step > 1e-8 && fabs(zt) < 1e6;
+}
+
+// Exact codes of the definition: clip(round(y / step) + zero, 0, 15), zero = round(-min/step).
+__device__ __forceinline__ double exact_code(double y, double step, double zero) {
+  double q = rint(y / step) + zero;
   q = q < 0.0 ? 0.0 : q;
   q = q > 15.0 ? 15.0 : q;
   return q;

@@ -37,6 +37,10 @@ constexpr int kStageBytes = (BM + BN) * KB;  // 32 KiB
 constexpr int kStages = AWQ_GEMM_STAGES;     // ring of stages; kStages - 1 in flight
 constexpr int kLdsBytes = kStages * kStageBytes;  // 160 KiB: all of a CU's LDS
 constexpr int kLoadsPerStage = 8;            // buffer->LDS loads per wave per stage (4 A + 4 B)
+#ifndef AWQ_GEMM_P1LOADS
+#define AWQ_GEMM_P1LOADS 4
+#endif
+constexpr int kLoadsPhase1 = AWQ_GEMM_P1LOADS;  // of those, issued before the mid-step barrier
 #ifndef AWQ_GEMM_GROUP_M
 #define AWQ_GEMM_GROUP_M 8
 #endif
@@ -241,28 +245,46 @@ void error_sse_kernel(const T* __restrict__ x, int64_t ld_x, const T* __restrict
     char* nxt = lds + nbuf * kStageBytes;
     const uint32_t fre = lds_base + fbuf * kStageBytes;
     const int kload = (kt + kStages - 1) * KB;
-    read_frags(cur + ra_off + slot1, cur + rb_off + slot1, fa1, fb1);
-    mma_all<T>(fa0, fb0, acc);
-    SCHED_INTERLEAVE(16 * MPP, 8)
-    // stages kt+1 .. kt+kStages-2 are in flight; kt+1 must have landed
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm((kStages - 3) * kLoadsPerStage));
+    // The 8 loads of stage kt+kStages-1 (its buffer was freed at the previous barrier): load i
+    // fills A slice i (i < 4) or B slice i-4.
+    auto issue_load = [&](int i) {
+      if (i < 4)
+        dma_load16(ra, __builtin_amdgcn_readfirstlane(fre + (4 * i + wave) * 16 * KB), voff_a[i], kload);
+      else
+        dma_load16(rb, __builtin_amdgcn_readfirstlane(fre + BM * KB + (4 * (i - 4) + wave) * 16 * KB),
+                   voff_b[i - 4], kload);
+    };
+    // phase 1: sub-step 0's MFMAs; between MFMA pairs, sub-step 1's fragment reads and the first
+    // kLoadsPhase1 loads (spread out: a burst of loads would stall MFMA issue)
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      const int fm = g >> 1;
+      mma_pair<T>(fa0[fm], fb0[(g & 1) * 2], acc[fm][(g & 1) * 2]);
+      mma_pair<T>(fa0[fm], fb0[(g & 1) * 2 + 1], acc[fm][(g & 1) * 2 + 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (g < kLoadsPhase1) issue_load(g);
+      if (g < 4)
+        fa1[g] = *reinterpret_cast<const uint4*>(cur + ra_off + slot1 + g * 32 * KB);
+      else
+        fb1[g - 4] = *reinterpret_cast<const uint4*>(cur + rb_off + slot1 + (g - 4) * 32 * KB);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // stages kt+1 .. kt+kStages-2 and the phase-1 loads are in flight; kt+1 must have landed
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((kStages - 3) * kLoadsPerStage + kLoadsPhase1));
     __syncthreads();
-    // sub-step 1's MFMAs, with the 8 loads of stage kt+kStages-1 and the 8 fragment reads of
-    // stage kt+1's sub-step 0 placed between them (a burst of loads would stall MFMA issue)
+    // phase 2: sub-step 1's MFMAs; between MFMA pairs, the remaining loads and stage kt+1's
+    // sub-step-0 fragment reads
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
       const int fm = g >> 1;
       mma_pair<T>(fa1[fm], fb1[(g & 1) * 2], acc[fm][(g & 1) * 2]);
       mma_pair<T>(fa1[fm], fb1[(g & 1) * 2 + 1], acc[fm][(g & 1) * 2 + 1]);
       __builtin_amdgcn_sched_barrier(0);
-      if (g < 4) {
-        dma_load16(ra, __builtin_amdgcn_readfirstlane(fre + (4 * g + wave) * 16 * KB), voff_a[g], kload);
+      if (kLoadsPhase1 + g < kLoadsPerStage) issue_load(kLoadsPhase1 + g);
+      if (g < 4)
         fa0[g] = *reinterpret_cast<const uint4*>(nxt + ra_off + slot0 + g * 32 * KB);
-      } else {
-        dma_load16(rb, __builtin_amdgcn_readfirstlane(fre + BM * KB + (4 * (g - 4) + wave) * 16 * KB),
-                   voff_b[g - 4], kload);
+      else
         fb0[g - 4] = *reinterpret_cast<const uint4*>(nxt + rb_off + slot0 + (g - 4) * 32 * KB);
-      }
       __builtin_amdgcn_sched_barrier(0);
     }
     buf = nbuf;

@@ -153,7 +153,15 @@ def test_delta_and_tile_sums_against_oracle(B):
         pk = O.quantize_pack(W, s, 128)
         em, _ = P.exempt_masks(pk.t, pk.zt)
         err = np.abs(d_gpu[k] - d_or)
-        assert np.all((err <= 2.0 ** -8 * np.abs(d_or) + 1e-30) | em)
+        # bf16 rounding of delta (2^-8 relative), plus the float64 error of forming delta from
+        # y * (1/step): a few ulps of t scaled by step/s, i.e. about 2^-50 |w| (2^-40 |w| allowed)
+        bad = ~((err <= 2.0 ** -8 * np.abs(d_or) + 2.0 ** -40 * np.abs(W)) | em)
+        if bad.any():
+            r, c = np.argwhere(bad)[0]
+            print(f"  k={k}: {int(bad.sum())} delta elements off, first at ({r},{c}): gpu {d_gpu[k][r, c]!r} "
+                  f"oracle {d_or[r, c]!r} w {W[r, c]!r} t {pk.t[r, c]!r} zt {pk.zt[r, c // 128]!r} "
+                  f"step {pk.qscales[r, c // 128]!r}", flush=True)
+        assert not bad.any()
         E = X @ d_or.T
         for tm in range(3):
             for tn in range(tiles_n):
