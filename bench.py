@@ -48,6 +48,36 @@ def _copy_probe(nbytes: int, reps: int) -> None:
     print(json.dumps({"copy_probe_bytes": nbytes, "reps": reps}))
 
 
+def _source_digest(*paths) -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+GEMM_SOURCES = ("post_quantization_mean_amd/csrc/err_gemm.hip", "post_quantization_mean_amd/csrc/internal.h")
+
+
+def measured_traffic(workload_name: str):
+    """HBM bytes per error-GEMM launch from the committed rocprofv3 counter summary (FETCH_SIZE and
+    WRITE_SIZE, scaled by a plain copy's readings), or None when the kernel source has changed
+    since the counters were taken or no summary exists for this workload."""
+    path = os.path.join(ROOT, "profiles", f"error_sse_{workload_name.replace('-', '_')}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    rec = None
+    with open(path, encoding="utf-8") as f:
+        for line in f:
+            if line.startswith("<!-- traffic:"):
+                rec = json.loads(line[len("<!-- traffic:"):].rsplit("-->", 1)[0])
+    if not rec or rec.get("kernel_digest") != _source_digest(*GEMM_SOURCES):
+        return None
+    return rec["hbm_bytes_per_launch"]
+
+
 def cpu_baseline(wl, x_np, w_np, target_s: float) -> dict:
     """The CPU oracle as it stands on a row sample of the layer, scaled to the whole layer."""
     from oracle import awq_oracle as O
@@ -90,8 +120,12 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe", type=int, default=0, help="only run a device copy of this many bytes")
+    ap.add_argument("--print-digest", action="store_true", help="print the error-GEMM source digest and exit")
     args = ap.parse_args()
 
+    if args.print_digest:
+        print(_source_digest(*GEMM_SOURCES))
+        return 0
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the search shards by weight "
               "rows with one tiny loss exchange, which this single-GPU build does not implement.",
@@ -212,7 +246,7 @@ def main() -> int:
         "config": {"workload": wl.name, "n_tokens": wl.n_tokens, "d_in": wl.d_in, "d_out": wl.d_out,
                    "parts": parts, "group_size": wl.group_size, "n_grid": wl.n_grid, "cand_per_pass": cpp},
         "roofline": {"bound": "mfma", "kernel": "error_sse_kernel", "achieved": achieved, "peak": peak,
-                     "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,
+                     "unit": "TFLOP/s", "frac": achieved / peak, "traffic": measured_traffic(wl.name),
                      "launch_ms": gemm_ms, "flops_per_launch": flops_launch},
         "search_ms": ms_step,
         "error_gemm_tflops": achieved,
