@@ -48,7 +48,8 @@ __device__ __forceinline__ void store8(float* p, const float (&v)[8]) {
   *reinterpret_cast<f32x4*>(p + 4) = b;
 }
 
-// ---- the quantizer on one row of one 128-channel group held by 8 lanes x 16 channels
+// ---- the quantizer on one row of one 128-channel group held by 16 lanes x 8 channels
+// (or 8 lanes x 16 channels)
 
 // 64-bit lane exchange inside groups of 8 lanes (DPP quad permutes and the half-row mirror).
 template <int CTRL>

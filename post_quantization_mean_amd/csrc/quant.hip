@@ -13,9 +13,9 @@
 // decides identically unless a value lies within 1e-6 of a rounding tie; a lane whose row
 // segment has such a value (or whose group has a floored step) redoes it with exact divisions.
 //
-// Thread layout: 8 lanes hold one 128-channel group of a row, 16 consecutive channels each; a
-// wave covers 8 consecutive groups (1024 channels) of kRows consecutive rows, the block's four
-// waves 4 * kRows rows. Each lane keeps its weights in registers and loops over the
+// Thread layout: 128 / kChans lanes hold one 128-channel group of a row, kChans consecutive
+// channels each (by default 16 lanes x 8 channels); a wave covers 64 * kChans consecutive
+// channels of kRows consecutive rows, the block's four waves 4 * kRows rows. Each lane keeps its weights in registers and loops over the
 // candidates, so W is read from HBM once however many candidates are evaluated, and a
 // candidate's scales are read once per kRows rows (prefetched one candidate ahead).
 //
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(kThreads) void quant_delta_kernel(WParts w, int64_t
   const int wave = threadIdx.x >> 6;
   const int64_t c0 = (int64_t)blockIdx.x * kChansPerBlock + (lane / kLanesPerGroup) * kGroup +
                      (lane % kLanesPerGroup) * E;
-  const bool col_ok = c0 < d_in;  // groups are whole, so the lane's 16 channels are all in range
+  const bool col_ok = c0 < d_in;  // groups are whole, so all of the lane's channels are in range
   const int64_t row0 = (int64_t)blockIdx.y * kRowsPerBlock + wave * kRows;
 
   RowE<T, E> wv[kRows];
