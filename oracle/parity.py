@@ -11,6 +11,7 @@ Rules (floating point deciding an integer is compared where the decision is uniq
   group whose -min/step lies within 1e-5 of a half-integer (all of its codes shift with it).
 * Per-group steps within 1e-6 relative of the oracle's float64 step (they are exported as
   float32).
+* delta = What - W (an intermediate) element-wise within delta_tolerance below.
 """
 from __future__ import annotations
 
@@ -21,6 +22,22 @@ LOSS_RTOL = 1e-3
 ACT_RTOL = 1e-5
 KSTAR_RTOL = 1e-6
 STEP_RTOL = 1e-6
+
+
+def delta_tolerance(d_or, W, qscales, s, group_size: int = 128) -> np.ndarray:
+    """Allowed |delta_gpu - delta_oracle| per element, where delta = What - W is an intermediate
+    of the search (it feeds the error GEMM) and is stored in the input dtype:
+    * 2^-8 |delta| for the bfloat16 rounding of the stored value;
+    * 2^-16 step / s for evaluating t = y / step in float32: when every decision agrees with
+      the float64 definition, |t32 - t| < 1.3e-5, so the restored value -(t - round t) step / s
+      is that close in units of step / s;
+    * 2^-40 |w| for forming delta as -(t - round t) step / s rather than What - W, which leaves a
+      residue of order 1e-16 |w| where the oracle's difference is exactly zero (weights already
+      on the quantization grid).
+    Elements whose oracle decision sits within TIE_BAND of a rounding tie are exempt as usual."""
+    step = np.repeat(np.asarray(qscales, np.float64), group_size, axis=1)
+    return (2.0 ** -8 * np.abs(d_or) + 2.0 ** -16 * step / np.asarray(s, np.float64)[None, :]
+            + 2.0 ** -40 * np.abs(W))
 
 
 def near_half(v: np.ndarray, band: float = TIE_BAND) -> np.ndarray:

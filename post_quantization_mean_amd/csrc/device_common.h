@@ -33,12 +33,20 @@ __device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
   v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
+// Two floats -> two bfloat16 (round to nearest even) in one register, first in the low half.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
 __device__ __forceinline__ void store8(uint16_t* p, const float (&v)[8]) {
   uint4 u;
-  u.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
-  u.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
-  u.z = f32_to_bf16(v[4]) | (f32_to_bf16(v[5]) << 16);
-  u.w = f32_to_bf16(v[6]) | (f32_to_bf16(v[7]) << 16);
+  u.x = pack_bf16x2(v[0], v[1]);
+  u.y = pack_bf16x2(v[2], v[3]);
+  u.z = pack_bf16x2(v[4], v[5]);
+  u.w = pack_bf16x2(v[6], v[7]);
   *reinterpret_cast<uint4*>(p) = u;
 }
 __device__ __forceinline__ void store8(float* p, const float (&v)[8]) {

@@ -153,9 +153,7 @@ def test_delta_and_tile_sums_against_oracle(B):
         pk = O.quantize_pack(W, s, 128)
         em, _ = P.exempt_masks(pk.t, pk.zt)
         err = np.abs(d_gpu[k] - d_or)
-        # bf16 rounding of delta (2^-8 relative), plus the float64 error of forming delta from
-        # y * (1/step): a few ulps of t scaled by step/s, i.e. about 2^-50 |w| (2^-40 |w| allowed)
-        bad = ~((err <= 2.0 ** -8 * np.abs(d_or) + 2.0 ** -40 * np.abs(W)) | em)
+        bad = ~((err <= P.delta_tolerance(d_or, W, pk.qscales, s)) | em)
         if bad.any():
             r, c = np.argwhere(bad)[0]
             print(f"  k={k}: {int(bad.sum())} delta elements off, first at ({r},{c}): gpu {d_gpu[k][r, c]!r} "

@@ -145,7 +145,7 @@ def _check(B, cid, full_row_losses=False):
         pq = O.quantize_pack(W_s, S[kk], 128)
         em, _ = P.exempt_masks(pq.t, pq.zt)
         err = np.abs(d_gpu - d_or)
-        assert np.all((err <= 2.0 ** -8 * np.abs(d_or) + 2.0 ** -40 * np.abs(W_s)) | em)
+        assert np.all((err <= P.delta_tolerance(d_or, W_s, pq.qscales, S[kk])) | em)
 
     # final codes, steps and zero points on sampled rows
     pq = O.quantize_pack(W_s, S[k], 128)
