@@ -26,10 +26,10 @@
 // is within 1e-5 * step / s of the float64 value (below the bfloat16 rounding of delta for all
 // but the smallest elements).
 //
-// quantize_pack (the final export) evaluates the quantizer in float64: 16 lanes x 8 channels
-// per group, the fast path dividing by multiplying with a reciprocal accurate to an ulp, which
-// decides identically unless a value lies within 1e-6 of a rounding tie; a lane whose row
-// segment has such a value (or whose group has a floored step) redoes it with exact divisions.
+// quantize_pack (the final export, one scale vector) uses the same layout, float32 fast path and
+// proof: its codes are r + zero, and flagged groups are redone by the whole wave in float64.
+#include <algorithm>
+
 #include "internal.h"
 #include "device_common.h"
 
@@ -40,16 +40,11 @@ constexpr int kThreads = 256;
 constexpr int kRows = 4;               // rows per wave (per lane)
 constexpr int kRowsPerBlock = 4 * kRows;
 
-// quant_delta layout: 16 channels per lane, 8 lanes per group, 1024 channels per block
-constexpr int kDeltaChans = 16;
-constexpr int kDeltaChansPerBlock = 64 * kDeltaChans;
+// Layout of both kernels: 16 channels per lane, 8 lanes per group, 1024 channels per block
+constexpr int kChans = 16;
+constexpr int kChansPerBlock = 64 * kChans;
 
-// quantize_pack layout: 8 channels per lane, 16 lanes per group, 512 channels per block
-constexpr int kPackChans = 8;
-constexpr int kPackLanesPerGroup = kGroup / kPackChans;
-constexpr int kPackChansPerBlock = 64 * kPackChans;
-
-// Float32 fast path of quant_delta. With y32 = fl(w * fl(s)) (relative error 2^-23), the group's
+// The float32 fast path. With y32 = fl(w * fl(s)) (relative error 2^-23), the group's
 // min/max taken on y32, step32 = fl(fl(max - min) * fl(1/15)) (relative error 2^-22 A/R +
 // 3 * 2^-24, A = max |y| of the group, R = max - min) and r = round(y32 * rcp(step32)), the
 // kernel forms e = fl(y32 - r * step32) with one rounding. A zero point -min/step in [-0.5, 15.5]
@@ -64,15 +59,6 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
-
-__device__ __forceinline__ float elem_f32(const uint16_t* p) { return bf16_to_f32(*p); }
-__device__ __forceinline__ float elem_f32(const float* p) { return *p; }
-template <typename T>
-__device__ __forceinline__ T from_f32(float v);
-template <>
-__device__ __forceinline__ uint16_t from_f32<uint16_t>(float v) { return (uint16_t)f32_to_bf16(v); }
-template <>
-__device__ __forceinline__ float from_f32<float>(float v) { return v; }
 
 template <typename T>
 __device__ __forceinline__ const T* row_ptr(const WParts& w, int64_t o, int64_t d_in) {
@@ -104,6 +90,9 @@ struct RowE<uint16_t, E> {
   __device__ __forceinline__ float operator[](int j) const {
     return (j & 1) ? __uint_as_float(b[j >> 1] & 0xFFFF0000u) : __uint_as_float(b[j >> 1] << 16);
   }
+  __device__ __forceinline__ void set(int h, const uint4& u) {
+    b[4 * h] = u.x; b[4 * h + 1] = u.y; b[4 * h + 2] = u.z; b[4 * h + 3] = u.w;
+  }
 };
 template <int E>
 struct RowE<float, E> {
@@ -120,6 +109,34 @@ struct RowE<float, E> {
     for (int j = 0; j < E; ++j) v[j] = 0.f;
   }
   __device__ __forceinline__ float operator[](int j) const { return v[j]; }
+  __device__ __forceinline__ void set(int h, const uint4& u) {
+    v[4 * h] = __uint_as_float(u.x); v[4 * h + 1] = __uint_as_float(u.y);
+    v[4 * h + 2] = __uint_as_float(u.z); v[4 * h + 3] = __uint_as_float(u.w);
+  }
+};
+
+// A wave's 1024-channel slice of one row loaded with consecutive lanes on consecutive 16 bytes
+// (whole cache lines per instruction; a lane stride of 32 bytes reads about 30 % slower), then
+// regrouped through the wave's LDS slot into each lane's 16 consecutive channels.
+template <typename T, int E>
+struct RawRow {
+  static constexpr int NV = E * (int)sizeof(T) / 16;  // 16-byte words per lane
+  uint4 u[NV];
+  __device__ __forceinline__ void load(const T* row_slice, int valid16, int lane) {
+    const uint4* q = reinterpret_cast<const uint4*>(row_slice);
+#pragma unroll
+    for (int v = 0; v < NV; ++v) u[v] = (v * 64 + lane < valid16) ? q[v * 64 + lane] : make_uint4(0u, 0u, 0u, 0u);
+  }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int v = 0; v < NV; ++v) u[v] = make_uint4(0u, 0u, 0u, 0u);
+  }
+  __device__ __forceinline__ void regroup(uint4* slot, int lane, RowE<T, E>& dst) const {
+#pragma unroll
+    for (int v = 0; v < NV; ++v) slot[v * 64 + lane] = u[v];
+#pragma unroll
+    for (int h = 0; h < NV; ++h) dst.set(h, slot[lane * NV + h]);
+  }
 };
 
 template <typename T, int E>
@@ -133,19 +150,35 @@ __device__ __forceinline__ void storeE(T* p, const float (&v)[E]) {
   }
 }
 
+// Float32 quantizer parameters of one row's group, whose 128 values y are held by 8 lanes x 16:
+// min/max over the group, step = (max - min) / 15, its reciprocal and the zero point -min/step.
+// `ok` holds when the zero point is at least kGuard32 from a rounding tie and lies in
+// [-0.5, 15.5], and the step is normal and above the floor (false for NaN).
+struct FastGroup {
+  float step, inv, zt;
+  bool ok;
+};
 template <int E>
-__device__ __forceinline__ void load_scales(const double* p, bool ok, double (&s)[E]) {
-  if (ok) {
+__device__ __forceinline__ FastGroup fast_group(const float (&y)[E]) {
+  float mn = y[0], mx = y[0];
 #pragma unroll
-    for (int j = 0; j < E; j += 2) {
-      const double2 v = *reinterpret_cast<const double2*>(p + j);
-      s[j] = v.x;
-      s[j + 1] = v.y;
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < E; ++j) s[j] = 1.0;
+  for (int j = 1; j < E; ++j) {
+    mn = fminf(mn, y[j]);
+    mx = fmaxf(mx, y[j]);
   }
+  mn = fminf(mn, dpp_f32<kDppXor1>(mn));
+  mx = fmaxf(mx, dpp_f32<kDppXor1>(mx));
+  mn = fminf(mn, dpp_f32<kDppXor2>(mn));
+  mx = fmaxf(mx, dpp_f32<kDppXor2>(mx));
+  mn = fminf(mn, dpp_f32<kDppHalfMirror>(mn));
+  mx = fmaxf(mx, dpp_f32<kDppHalfMirror>(mx));
+  FastGroup g;
+  g.step = (mx - mn) * (1.0f / 15.0f);
+  g.inv = __builtin_amdgcn_rcpf(g.step);
+  g.zt = -mn * g.inv;
+  g.ok = fabsf(g.zt - rintf(g.zt)) <= kHalfGuard32 && g.step >= 2e-8f && g.step <= 1e30f && g.zt >= -0.5f &&
+         g.zt <= 15.5f;
+  return g;
 }
 
 // One group of one row by a whole wave, in float64 exactly as the definition is written, 2
@@ -178,13 +211,8 @@ __device__ __forceinline__ double readlane_f64(double v, int l) {
   return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
-template <typename T>
-__device__ __forceinline__ void exact_group(float wa, float wb, const double* s_lds, T* dst) {
-  const double w0 = wa, w1 = wb;
-  const double s0 = s_lds[0], s1 = s_lds[1];
-  const double y0 = w0 * s0, y1 = w1 * s1;
-  double mn = fmin(y0, y1), mx = fmax(y0, y1);
-  // minimum and maximum over the wave: within rows of 16 lanes, then across the 4 rows
+// Minimum and maximum over the whole wave: within rows of 16 lanes, then across the 4 rows.
+__device__ __forceinline__ void wave_minmax_f64(double& mn, double& mx) {
   mn = fmin(mn, dpp_f64<kDppXor1>(mn));
   mx = fmax(mx, dpp_f64<kDppXor1>(mx));
   mn = fmin(mn, dpp_f64<kDppXor2>(mn));
@@ -195,6 +223,15 @@ __device__ __forceinline__ void exact_group(float wa, float wb, const double* s_
   mx = fmax(mx, dpp_f64<kDppRowMirror>(mx));
   mn = fmin(fmin(readlane_f64(mn, 0), readlane_f64(mn, 16)), fmin(readlane_f64(mn, 32), readlane_f64(mn, 48)));
   mx = fmax(fmax(readlane_f64(mx, 0), readlane_f64(mx, 16)), fmax(readlane_f64(mx, 32), readlane_f64(mx, 48)));
+}
+
+template <typename T>
+__device__ __forceinline__ void exact_group(float wa, float wb, const double* s_lds, T* dst) {
+  const double w0 = wa, w1 = wb;
+  const double s0 = s_lds[0], s1 = s_lds[1];
+  const double y0 = w0 * s0, y1 = w1 * s1;
+  double mn = fmin(y0, y1), mx = fmax(y0, y1);
+  wave_minmax_f64(mn, mx);
   const double st = group_step(mn, mx);
   const double zero = rint(-mn / st);
   const double q0 = exact_code(y0, st, zero), q1 = exact_code(y1, st, zero);
@@ -205,15 +242,15 @@ template <typename T>
 __global__ __launch_bounds__(kThreads) void quant_delta_kernel(WParts w, int64_t d_in, int64_t d_out,
                                                                const double* __restrict__ cand,
                                                                int n_cand, T* __restrict__ delta) {
-  constexpr int E = kDeltaChans;
-  __shared__ __attribute__((aligned(16))) float sc_s[2][kDeltaChansPerBlock];
-  __shared__ __attribute__((aligned(16))) float sc_i[2][kDeltaChansPerBlock];  // -1/s
-  __shared__ __attribute__((aligned(16))) double sc_d[2][kDeltaChansPerBlock];  // for the exact path
+  constexpr int E = kChans;
+  __shared__ __attribute__((aligned(16))) float sc_s[2][kChansPerBlock];
+  __shared__ __attribute__((aligned(16))) float sc_i[2][kChansPerBlock];  // -1/s
+  __shared__ __attribute__((aligned(16))) double sc_d[2][kChansPerBlock];  // for the exact path
   __shared__ __attribute__((aligned(16))) float xpose[4][kGroup];  // per wave: one group's weights
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int64_t cb = (int64_t)blockIdx.x * kDeltaChansPerBlock;
+  const int64_t cb = (int64_t)blockIdx.x * kChansPerBlock;
   const int cl = lane * E;  // group lane/8, 16-channel slice lane%8: channels cb + 16*lane ..
   const int64_t c0 = cb + cl;
   const bool col_ok = c0 < d_in;  // groups are whole, so all of the lane's channels are in range
@@ -273,21 +310,8 @@ __global__ __launch_bounds__(kThreads) void quant_delta_kernel(WParts w, int64_t
       float y[E];
 #pragma unroll
       for (int j = 0; j < E; ++j) y[j] = wv[i][j] * s[j];
-      float mn = y[0], mx = y[0];
-#pragma unroll
-      for (int j = 1; j < E; ++j) {
-        mn = fminf(mn, y[j]);
-        mx = fmaxf(mx, y[j]);
-      }
-      mn = fminf(mn, dpp_f32<kDppXor1>(mn));
-      mx = fmaxf(mx, dpp_f32<kDppXor1>(mx));
-      mn = fminf(mn, dpp_f32<kDppXor2>(mn));
-      mx = fmaxf(mx, dpp_f32<kDppXor2>(mx));
-      mn = fminf(mn, dpp_f32<kDppHalfMirror>(mn));
-      mx = fmaxf(mx, dpp_f32<kDppHalfMirror>(mx));
-      const float step = (mx - mn) * (1.0f / 15.0f);
-      const float inv = __builtin_amdgcn_rcpf(step);
-      const float zt = -mn * inv;
+      const FastGroup fg = fast_group<E>(y);
+      const float step = fg.step, inv = fg.inv;
       // r = round(y / step); e = y - r step (one rounding); delta = (r step - y) / s = e * (-1/s)
       float em = 0.f;
       float out[E];
@@ -301,8 +325,7 @@ __global__ __launch_bounds__(kThreads) void quant_delta_kernel(WParts w, int64_t
       // past the last row or channel never take the exact path
       const int64_t o = row0 + i;
       const bool live = col_ok && o < d_out;
-      const bool ok = em <= kHalfGuard32 * step && fabsf(zt - rintf(zt)) <= kHalfGuard32 && step >= 2e-8f &&
-                      step <= 1e30f && zt >= -0.5f && zt <= 15.5f;
+      const bool ok = fg.ok && em <= kHalfGuard32 * step;
       bad[i] = group_mask(__ballot(live && !ok));
       if (live && !((bad[i] >> lane) & 1)) storeE<T, E>(dk + o * d_in, out);
       __builtin_amdgcn_sched_barrier(0);  // one row's temporaries live at a time
@@ -331,82 +354,133 @@ __global__ __launch_bounds__(kThreads) void quant_delta_kernel(WParts w, int64_t
   }
 }
 
+// The exact path of the pack for one group of one row, by the whole wave (2 channels per lane,
+// w0/w1 with scales s[0..1]): codes of the float64 definition into one byte (even channel in the
+// low nibble), and lane 0 writes the group's step (as float32) and zero point (saturated to int32).
+__device__ __forceinline__ void exact_pack_group(float wa, float wb, const double* s, uint8_t* code, float* qs,
+                                                 int32_t* zp, int lane) {
+  const double y0 = (double)wa * s[0], y1 = (double)wb * s[1];
+  double mn = fmin(y0, y1), mx = fmax(y0, y1);
+  wave_minmax_f64(mn, mx);
+  const double st = group_step(mn, mx);
+  const double zero = rint(-mn / st);
+  double q0 = exact_code(y0, st, zero), q1 = exact_code(y1, st, zero);
+  q0 = q0 == q0 ? q0 : 0.0;  // a NaN code (non-finite input) packs as 0
+  q1 = q1 == q1 ? q1 : 0.0;
+  *code = (uint8_t)((uint32_t)q0 | ((uint32_t)q1 << 4));
+  if (lane == 0) {
+    *qs = (float)st;
+    double z = zero;
+    z = z > 2147483647.0 ? 2147483647.0 : (z < -2147483648.0 ? -2147483648.0 : z);
+    *zp = (z == z) ? (int32_t)z : 0;
+  }
+}
+
+// a6: codes of W * s packed two per byte, with each group's step and zero point. Same layout and
+// float32 fast path as quant_delta (one scale vector, so no candidate loop): q = round(y / step)
+// + zero, proved equal to the float64 definition by the residual and zero-point checks; flagged
+// groups are redone by the whole wave in float64.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(WParts w, int64_t d_in, int64_t d_out,
                                                                  const double* __restrict__ s_in,
                                                                  uint8_t* __restrict__ codes,
                                                                  float* __restrict__ qscales,
                                                                  int32_t* __restrict__ zeros) {
-  constexpr int E = kPackChans;
+  constexpr int E = kChans;
+  __shared__ __attribute__((aligned(16))) float xpose[4][kGroup];  // per wave: one group's weights
+  __shared__ uint4 slot[4][RawRow<T, E>::NV * 64];                 // per wave: one row slice
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int64_t c0 = (int64_t)blockIdx.x * kPackChansPerBlock + (lane / kPackLanesPerGroup) * kGroup +
-                     (lane % kPackLanesPerGroup) * E;
+  const int64_t cb = (int64_t)blockIdx.x * kChansPerBlock;
+  const int64_t c0 = cb + lane * E;
   const bool col_ok = c0 < d_in;
-  const int64_t grp = c0 / kGroup;
   const int64_t n_groups = d_in / kGroup;
-  const int64_t row0 = (int64_t)blockIdx.y * kRowsPerBlock + wave * kRows;
+  const int64_t n_rb = (d_out + kRowsPerBlock - 1) / kRowsPerBlock;
+  // Row blocks blockIdx.y, blockIdx.y + gridDim.y, ...; the next one's weights are loaded while
+  // the current one is quantized.
+  const int valid16 = (int)((std::min<int64_t>(d_in - cb, kChansPerBlock) * (int64_t)sizeof(T)) / 16);
+  auto load_rows = [&](RawRow<T, E>(&dst)[kRows], int64_t rb) {
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) {
+      const int64_t o = rb * kRowsPerBlock + wave * kRows + i;
+      if (o < d_out)
+        dst[i].load(row_ptr<T>(w, o, d_in) + cb, valid16, lane);
+      else
+        dst[i].zero();
+    }
+  };
+  RawRow<T, E> raw[kRows], rawn[kRows];
+  load_rows(raw, blockIdx.y);
+  float s[E];
+#pragma unroll
+  for (int j = 0; j < E; j += 2) {
+    double2 v = {1.0, 1.0};
+    if (col_ok) v = *reinterpret_cast<const double2*>(s_in + c0 + j);
+    s[j] = (float)v.x;
+    s[j + 1] = (float)v.y;
+  }
 
-  double s[E];
-  load_scales(s_in + c0, col_ok, s);
+  for (int64_t rb = blockIdx.y; rb < n_rb; rb += gridDim.y) {
+    const int64_t row0 = rb * kRowsPerBlock + wave * kRows;
+    RowE<T, E> wv[kRows];
 #pragma unroll
-  for (int i = 0; i < kRows; ++i) {
-    const int64_t o = row0 + i;
-    const bool ok = col_ok && o < d_out;
-    RowE<T, E> wv;
-    if (ok)
-      wv.load(row_ptr<T>(w, o, d_in) + c0);
-    else
-      wv.zero();
-    double y[E];
+    for (int i = 0; i < kRows; ++i) raw[i].regroup(slot[wave], lane, wv[i]);
+    if (rb + gridDim.y < n_rb) load_rows(rawn, rb + gridDim.y);
+    uint64_t bad[kRows];
 #pragma unroll
-    for (int j = 0; j < E; ++j) y[j] = (double)wv[j] * s[j];
-    double mn, mx;
-    group_minmax<E>(y, mn, mx);
-    const double step = group_step(mn, mx);
-    const double inv = rcp_nr(step);
-    const double zt = -mn * inv;
-    double zero = rint(zt);
-    double q[E];
-    double dmax = 0.0;
+    for (int i = 0; i < kRows; ++i) {
+      float y[E];
 #pragma unroll
-    for (int j = 0; j < E; ++j) {
-      const double t = y[j] * inv;
-      const double r = rint(t);
-      dmax = fmax(dmax, fabs(t - r));
-      q[j] = r + zero;
-    }
-    if (!(group_fast_ok(zt, zero, step) && dmax <= kTieGuard)) {
-      zero = rint(-mn / step);
+      for (int j = 0; j < E; ++j) y[j] = wv[i][j] * s[j];
+      const FastGroup fg = fast_group<E>(y);
+      const float z = rintf(fg.zt);
+      float em = 0.f;
+      uint32_t pk[E / 8] = {};
 #pragma unroll
-      for (int j = 0; j < E; ++j) q[j] = exact_code(y[j], step, zero);
-    }
-    uint32_t pk[E / 8];
-#pragma unroll
-    for (int h = 0; h < E / 8; ++h) {
-      pk[h] = 0u;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const double v = q[8 * h + j];
-        pk[h] |= ((v >= 0.0 && v <= 15.0) ? (uint32_t)v : 0u) << (4 * j);
+      for (int j = 0; j < E; ++j) {
+        const float r = rintf(y[j] * fg.inv);
+        const float e = fmaf(-r, fg.step, y[j]);
+        em = j == 0 ? fabsf(e) : fmaxf(em, fabsf(e));
+        pk[j / 8] |= (uint32_t)(r + z) << (4 * (j % 8));  // in [0, 15] when the checks pass
       }
-    }
-    if (ok) {
-      if constexpr (E == 16) {
+      const int64_t o = row0 + i;
+      const bool live = col_ok && o < d_out;
+      const bool ok = fg.ok && em <= kHalfGuard32 * fg.step;
+      bad[i] = group_mask(__ballot(live && !ok));
+      if (live && !((bad[i] >> lane) & 1)) {
         uint2 v;
         v.x = pk[0];
         v.y = pk[1];
         *reinterpret_cast<uint2*>(codes + o * (d_in / 2) + c0 / 2) = v;
-      } else {
-        *reinterpret_cast<uint32_t*>(codes + o * (d_in / 2) + c0 / 2) = pk[0];
+        if ((lane & 7) == 0) {
+          qscales[o * n_groups + c0 / kGroup] = fg.step;
+          zeros[o * n_groups + c0 / kGroup] = (int32_t)z;
+        }
       }
-      if (lane % kPackLanesPerGroup == 0) {
-        qscales[o * n_groups + grp] = (float)step;
-        double z = zero;
-        z = z > 2147483647.0 ? 2147483647.0 : (z < -2147483648.0 ? -2147483648.0 : z);
-        zeros[o * n_groups + grp] = (z == z) ? (int32_t)z : 0;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) {
+      uint64_t m = bad[i];
+      const int64_t o = row0 + i;
+      while (m) {
+        const int g = __builtin_ctzll(m) >> 3;
+        m &= ~(0xFFull << (8 * g));
+        if ((lane >> 3) == g) {
+#pragma unroll
+          for (int h = 0; h < E / 4; ++h) {
+            const f32x4 v = {wv[i][4 * h], wv[i][4 * h + 1], wv[i][4 * h + 2], wv[i][4 * h + 3]};
+            *reinterpret_cast<f32x4*>(&xpose[wave][(lane & 7) * E + 4 * h]) = v;
+          }
+        }
+        const float2 wp = *reinterpret_cast<const float2*>(&xpose[wave][2 * lane]);
+        const int64_t c = cb + g * kGroup + 2 * lane;
+        const int64_t gi = o * n_groups + (cb + g * kGroup) / kGroup;
+        exact_pack_group(wp.x, wp.y, s_in + c, codes + o * (d_in / 2) + c / 2, qscales + gi, zeros + gi, lane);
       }
     }
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) raw[i] = rawn[i];
   }
 }
 
@@ -415,7 +489,7 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(WParts w, int64
 hipError_t launch_quant_delta(const WParts& w, int dtype, int64_t d_in, const double* cand_scales,
                               int n_cand, void* delta, hipStream_t st) {
   const int64_t d_out = w.row_begin[w.n];
-  dim3 grid((unsigned)((d_in + kDeltaChansPerBlock - 1) / kDeltaChansPerBlock),
+  dim3 grid((unsigned)((d_in + kChansPerBlock - 1) / kChansPerBlock),
             (unsigned)((d_out + kRowsPerBlock - 1) / kRowsPerBlock));
   if (dtype == 1)
     hipLaunchKernelGGL(quant_delta_kernel<uint16_t>, grid, dim3(kThreads), 0, st, w, d_in, d_out,
@@ -429,8 +503,11 @@ hipError_t launch_quant_delta(const WParts& w, int dtype, int64_t d_in, const do
 hipError_t launch_quantize_pack(const WParts& w, int dtype, int64_t d_in, const double* s,
                                 uint8_t* codes, float* qscales, int32_t* zeros, hipStream_t st) {
   const int64_t d_out = w.row_begin[w.n];
-  dim3 grid((unsigned)((d_in + kPackChansPerBlock - 1) / kPackChansPerBlock),
-            (unsigned)((d_out + kRowsPerBlock - 1) / kRowsPerBlock));
+  // about three resident blocks per compute unit, each looping over row blocks
+  const int64_t col_blocks = (d_in + kChansPerBlock - 1) / kChansPerBlock;
+  const int64_t row_blocks = (d_out + kRowsPerBlock - 1) / kRowsPerBlock;
+  const int64_t ry = std::max<int64_t>(1, std::min<int64_t>(row_blocks, 768 / col_blocks));
+  dim3 grid((unsigned)col_blocks, (unsigned)ry);
   if (dtype == 1)
     hipLaunchKernelGGL(quantize_pack_kernel<uint16_t>, grid, dim3(kThreads), 0, st, w, d_in, d_out, s,
                        codes, qscales, zeros);
