@@ -23,17 +23,16 @@
 // the loads are placed between MFMA pairs. The 16-byte chunks of each LDS row are XOR-swizzled
 // by row, which leaves the fragment reads free of bank conflicts.
 //
-// Tile order: workgroups are dealt round-robin to the 8 XCDs, so block ids are first mapped to
-// a contiguous logical range per XCD, then that range walks groups of 8 token tiles across all
-// candidate-row tiles; the concurrently running tiles of an XCD then share operand K-slices in
-// its L2.
+// Tile order: the 256 concurrently running tiles form a 16 x 16 super-block, split 8 x 4 per XCD
+// (see the kernel), so operand K-slices are shared inside each XCD's L2 and across the XCDs in the
+// memory-side cache.
 #include "internal.h"
 
 namespace awq {
 namespace {
 
 constexpr int BM = kTileM, BN = kTileN;
-constexpr int kGroupM = 8;  // token tiles per group of the tile order
+constexpr int kSuper = 16;  // super-block side of the tile order, in tiles
 constexpr int kXcds = 8;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -115,17 +114,31 @@ void error_sse_kernel(const T* __restrict__ x, int64_t ld_x, const T* __restrict
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-  const int nblk = gridDim.x;
-  const int bid = blockIdx.x;
-  const int xcd = bid % kXcds, jx = bid / kXcds;
-  const int qx = nblk / kXcds, rx = nblk % kXcds;
-  const int L = xcd * qx + min(xcd, rx) + jx;
-  const int span = kGroupM * n_cols;
-  const int first_m = (L / span) * kGroupM;
-  const int gsize = min(tiles_m - first_m, kGroupM);
-  const int in_g = L % span;
-  const int tm = first_m + in_g % gsize;
-  const int col = in_g / gsize;
+  // Tile order. Workgroups are dealt round-robin to the 8 XCDs, so the 256 tiles with block ids
+  // [256 t, 256 t + 256) run at about the same time, 32 per XCD. They form one 16 x 16 super-block
+  // of (token tile, candidate-row tile) pairs; XCD x takes the 8 x 4 sub-block at (x / 4, x % 4),
+  // so each XCD's L2 sees 8 token and 4 row K-slices per step, and the 8 XCDs together read 16 + 16
+  // slices from memory instead of 8 x (8 + 4). Super-blocks sweep the candidate-row tiles within a
+  // band of 16 token tiles; ragged super-blocks at the edges are walked token-fastest.
+  int tm, col;
+  {
+    const int G = blockIdx.x;
+    const int n_sbm = (tiles_m + kSuper - 1) / kSuper, n_sbn = (n_cols + kSuper - 1) / kSuper;
+    const int r = min(G / (kSuper * n_cols), n_sbm - 1);
+    const int G1 = G - kSuper * r * n_cols;
+    const int h = min(kSuper, tiles_m - kSuper * r);
+    const int c = min(G1 / (h * kSuper), n_sbn - 1);
+    const int G2 = G1 - c * h * kSuper;
+    const int w = min(kSuper, n_cols - kSuper * c);
+    if (h == kSuper && w == kSuper) {
+      const int x = G2 % kXcds, q = G2 / kXcds;
+      tm = kSuper * r + (x / 4) * 8 + q % 8;
+      col = kSuper * c + (x % 4) * 4 + q / 8;
+    } else {
+      tm = kSuper * r + G2 % h;
+      col = kSuper * c + G2 / h;
+    }
+  }
   const int cand = col / tiles_n;
   const int tn = col % tiles_n;
 
