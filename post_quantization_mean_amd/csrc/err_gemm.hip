@@ -26,6 +26,8 @@
 // Tile order: the 256 concurrently running tiles form a 16 x 16 super-block, split 8 x 4 per XCD
 // (see the kernel), so operand K-slices are shared inside each XCD's L2 and across the XCDs in the
 // memory-side cache.
+#include <algorithm>
+
 #include "internal.h"
 
 namespace awq {
@@ -104,54 +106,69 @@ constexpr int kSplit = 8;
 // l%32, chunk 2s + l/32) then show no LDS bank-conflict cycles on gfx950.
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
-template <typename T>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void error_sse_kernel(const T* __restrict__ x, int64_t ld_x, const T* __restrict__ delta,
-                            int64_t n_tokens, int64_t d_in, int64_t d_out, int tiles_m, int tiles_n,
-                            int n_cols, double* __restrict__ tile_sse) {
-  constexpr int FM = 4, FN = 4, NR = 8;
-  __shared__ __attribute__((aligned(1024))) char lds[2 * kStageBytes];
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-
-  // Tile order. Workgroups are dealt round-robin to the 8 XCDs, so the 256 tiles with block ids
-  // [256 t, 256 t + 256) run at about the same time, 32 per XCD. They form one 16 x 16 super-block
-  // of (token tile, candidate-row tile) pairs; XCD x takes the 8 x 4 sub-block at (x / 4, x % 4),
-  // so each XCD's L2 sees 8 token and 4 row K-slices per step, and the 8 XCDs together read 16 + 16
-  // slices from memory instead of 8 x (8 + 4). Super-blocks sweep the candidate-row tiles within a
-  // band of 16 token tiles; ragged super-blocks at the edges are walked token-fastest.
-  int tm, col;
-  {
-    const int G = blockIdx.x;
-    const int n_sbm = (tiles_m + kSuper - 1) / kSuper, n_sbn = (n_cols + kSuper - 1) / kSuper;
-    const int r = min(G / (kSuper * n_cols), n_sbm - 1);
-    const int G1 = G - kSuper * r * n_cols;
-    const int h = min(kSuper, tiles_m - kSuper * r);
-    const int c = min(G1 / (h * kSuper), n_sbn - 1);
-    const int G2 = G1 - c * h * kSuper;
-    const int w = min(kSuper, n_cols - kSuper * c);
-    if (h == kSuper && w == kSuper) {
-      const int x = G2 % kXcds, q = G2 / kXcds;
-      tm = kSuper * r + (x / 4) * 8 + q % 8;
-      col = kSuper * c + (x % 4) * 4 + q / 8;
-    } else {
-      tm = kSuper * r + G2 % h;
-      col = kSuper * c + G2 / h;
-    }
+// The tile of linear index G (see the tile order above): token tile tm, column col (candidate
+// col / tiles_n, row tile col % tiles_n).
+__device__ __forceinline__ void tile_of(int G, int tiles_m, int n_cols, int& tm, int& col) {
+  const int n_sbm = (tiles_m + kSuper - 1) / kSuper, n_sbn = (n_cols + kSuper - 1) / kSuper;
+  const int r = min(G / (kSuper * n_cols), n_sbm - 1);
+  const int G1 = G - kSuper * r * n_cols;
+  const int h = min(kSuper, tiles_m - kSuper * r);
+  const int c = min(G1 / (h * kSuper), n_sbn - 1);
+  const int G2 = G1 - c * h * kSuper;
+  const int w = min(kSuper, n_cols - kSuper * c);
+  if (h == kSuper && w == kSuper) {
+    const int x = G2 % kXcds, q = G2 / kXcds;
+    tm = kSuper * r + (x / 4) * 8 + q % 8;
+    col = kSuper * c + (x % 4) * 4 + q / 8;
+  } else {
+    tm = kSuper * r + G2 % h;
+    col = kSuper * c + G2 / h;
   }
+}
+
+// Operand descriptors of one tile: A = its 256 token rows of X, B = its 256 rows of the
+// candidate's delta, each a raw buffer whose range ends at the last valid row.
+struct TileOps {
+  i32x4 ra, rb;
+  int idx;  // tile_sse index
+};
+template <typename T>
+__device__ __forceinline__ TileOps tile_ops(int G, const T* x, int64_t ld_x, const T* delta, int64_t n_tokens,
+                                            int64_t d_in, int64_t d_out, int tiles_m, int tiles_n, int n_cols) {
+  int tm, col;
+  tile_of(G, tiles_m, n_cols, tm, col);
   const int cand = col / tiles_n;
   const int tn = col % tiles_n;
-
   const int64_t m0 = (int64_t)tm * BM;
   const int64_t n0 = (int64_t)tn * BN;
   const int rows_a = (int)min((int64_t)BM, n_tokens - m0);
   const int rows_b = (int)min((int64_t)BN, d_out - n0);
   const int lda_bytes = (int)(ld_x * (int64_t)sizeof(T));
   const int row_bytes = (int)(d_in * (int64_t)sizeof(T));
-  const T* a_base = x + m0 * ld_x;
-  const T* b_base = delta + ((int64_t)cand * d_out + n0) * d_in;
-  const i32x4 ra = make_rsrc(a_base, (rows_a - 1) * lda_bytes + row_bytes);
-  const i32x4 rb = make_rsrc(b_base, (rows_b - 1) * row_bytes + row_bytes);
+  TileOps t;
+  t.ra = make_rsrc(x + m0 * ld_x, (rows_a - 1) * lda_bytes + row_bytes);
+  t.rb = make_rsrc(delta + ((int64_t)cand * d_out + n0) * d_in, (rows_b - 1) * row_bytes + row_bytes);
+  t.idx = cand * tiles_m * tiles_n + tm * tiles_n + tn;
+  return t;
+}
+
+// Persistent: one workgroup per compute unit walks tiles G = blockIdx.x, + gridDim.x, ... The
+// next tile's first K stage is loaded into the free LDS buffer during the current tile's last K
+// step, so its load latency hides behind that step and the epilogue.
+template <typename T>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void error_sse_kernel(const T* __restrict__ x, int64_t ld_x, const T* __restrict__ delta,
+                      int64_t n_tokens, int64_t d_in, int64_t d_out, int tiles_m, int tiles_n,
+                      int n_cols, double* __restrict__ tile_sse) {
+  constexpr int FM = 4, FN = 4, NR = 8;
+  __shared__ __attribute__((aligned(1024))) char lds[2 * kStageBytes];
+  __shared__ double red[4];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nblk = tiles_m * n_cols;
+
+  const int lda_bytes = (int)(ld_x * (int64_t)sizeof(T));
+  const int row_bytes = (int)(d_in * (int64_t)sizeof(T));
   // 8 loads per operand per wave per stage: load j of wave w covers rows 8*(4j+w) .. +7; lane i
   // fills row 8*(4j+w) + i/8, slot i%8, which holds K chunk (i%8) ^ swz(row)
   int voff_a[8], voff_b[8];
@@ -163,21 +180,14 @@ void error_sse_kernel(const T* __restrict__ x, int64_t ld_x, const T* __restrict
     voff_b[j] = row * row_bytes + sl;
   }
   const uint32_t lds_base = __builtin_amdgcn_readfirstlane(lds_address(lds));
-  auto issue = [&](uint32_t stage, int i, int kbyte) {  // load i of 16 (8 A, then 8 B)
+  // load i of 16 (8 of A, then 8 of B) of the stage at LDS address `stage`, K offset kbyte
+  auto issue = [&](const TileOps& t, uint32_t stage, int i, int kbyte) {
     if (i < 8)
-      dma_load16(ra, __builtin_amdgcn_readfirstlane(stage + (4 * i + wave) * 8 * KB), voff_a[i], kbyte);
+      dma_load16(t.ra, __builtin_amdgcn_readfirstlane(stage + (4 * i + wave) * 8 * KB), voff_a[i], kbyte);
     else
-      dma_load16(rb, __builtin_amdgcn_readfirstlane(stage + BM * KB + (4 * (i - 8) + wave) * 8 * KB),
+      dma_load16(t.rb, __builtin_amdgcn_readfirstlane(stage + BM * KB + (4 * (i - 8) + wave) * 8 * KB),
                  voff_b[i - 8], kbyte);
   };
-
-  f32x16 acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   const int wm = wave >> 1, wn = wave & 1;
   const int fr = lane & 31;
@@ -189,93 +199,115 @@ void error_sse_kernel(const T* __restrict__ x, int64_t ld_x, const T* __restrict
   for (int q = 0; q < 4; ++q) slot[q] = ((2 * q + fh) ^ swz(fr)) << 4;
   const int k_steps = row_bytes / KB;  // >= 2: d_in is a positive multiple of 128
 
+  f32x16 acc[FM][FN];
   auto frag = [&](const char* stage, int sl, int r) -> uint4 {
     const int off = r < FM ? ra_off + r * 32 * KB : rb_off + (r - FM) * 32 * KB;
     return *reinterpret_cast<const uint4*>(stage + off + sl);
   };
   // one sub-step: 16 MFMAs on `use`; between MFMA pairs, the next sub-step's 8 fragment reads
-  // (if `reads`) and loads [l0, l1) of `fstage` at K offset kbyte
+  // (if `reads`) and loads [l0, l1) of tile `lt`'s stage at LDS address `fstage`, K offset kbyte
   auto substep = [&](const uint4 (&use)[NR], uint4 (&nxt)[NR], const char* src, int sl, bool reads,
-                     uint32_t fstage, int kbyte, int l0, int l1) {
+                     const TileOps& lt, uint32_t fstage, int kbyte, int l0, int l1) {
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
       const int fm = g >> 1, fn = (g & 1) * 2;
       mma_pair<T>(use[fm], use[FM + fn], acc[fm][fn]);
       mma_pair<T>(use[fm], use[FM + fn + 1], acc[fm][fn + 1]);
       __builtin_amdgcn_sched_barrier(0);
-      if (l0 + 2 * g < l1) issue(fstage, l0 + 2 * g, kbyte);
-      if (l0 + 2 * g + 1 < l1) issue(fstage, l0 + 2 * g + 1, kbyte);
+      if (l0 + 2 * g < l1) issue(lt, fstage, l0 + 2 * g, kbyte);
+      if (l0 + 2 * g + 1 < l1) issue(lt, fstage, l0 + 2 * g + 1, kbyte);
       if (reads) nxt[g] = frag(src, sl, g);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  uint4 f0[NR], f1[NR];
-  // prologue: stage 0, and the first kSplit loads of stage 1 (k_steps >= 2); wait for stage 0
+  int G = blockIdx.x;
+  if (G >= nblk) return;
+  TileOps cur_t = tile_ops<T>(G, x, ld_x, delta, n_tokens, d_in, d_out, tiles_m, tiles_n, n_cols);
+  int par = 0;  // LDS buffer holding the tile's K stage 0
 #pragma unroll
-  for (int i = 0; i < 16; ++i) issue(lds_base, i, 0);
-#pragma unroll
-  for (int i = 0; i < kSplit; ++i) issue(lds_base + kStageBytes, i, KB);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(kSplit));
-  __syncthreads();
-#pragma unroll
-  for (int r = 0; r < NR; ++r) f0[r] = frag(lds, slot[0], r);
+  for (int i = 0; i < 16; ++i) issue(cur_t, lds_base, i, 0);
 
-  int kt = 0;
-  for (; kt + 2 < k_steps; ++kt) {
-    const int b = kt & 1;
-    char* cur = lds + b * kStageBytes;
-    char* nxt = lds + (b ^ 1) * kStageBytes;
-    const uint32_t fre = lds_base + b * kStageBytes;  // stage kt's buffer, refilled with stage kt+2
-    // the rest of stage kt+1's loads (its buffer was freed by the barrier of step kt-1)
-    substep(f0, f1, cur, slot[1], true, lds_base + (b ^ 1) * kStageBytes, (kt + 1) * KB, kSplit, 16);
-    substep(f1, f0, cur, slot[2], true, 0, 0, 0, 0);
-    substep(f0, f1, cur, slot[3], true, 0, 0, 0, 0);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // stage kt+1 has landed
-    __syncthreads();                           // and every wave has read all of stage kt
-    substep(f1, f0, nxt, slot[0], true, fre, (kt + 2) * KB, 0, kSplit);
-  }
-  {  // K step k_steps-2: only the rest of stage k_steps-1 left to load
-    const int b = kt & 1;
-    char* cur = lds + b * kStageBytes;
-    char* nxt = lds + (b ^ 1) * kStageBytes;
-    substep(f0, f1, cur, slot[1], true, lds_base + (b ^ 1) * kStageBytes, (kt + 1) * KB, kSplit, 16);
-    substep(f1, f0, cur, slot[2], true, 0, 0, 0, 0);
-    substep(f0, f1, cur, slot[3], true, 0, 0, 0, 0);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  for (;;) {
+    const int Gn = G + (int)gridDim.x;
+    const bool has_next = Gn < nblk;
+    const TileOps nxt_t =
+        tile_ops<T>(has_next ? Gn : G, x, ld_x, delta, n_tokens, d_in, d_out, tiles_m, tiles_n, n_cols);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+    uint4 f0[NR], f1[NR];
+    // stage 0 is in flight in buffer par; the first kSplit loads of stage 1 go to the other
+    // buffer (free: every wave passed the previous tile's final barrier); wait for stage 0
+#pragma unroll
+    for (int i = 0; i < kSplit; ++i) issue(cur_t, lds_base + (par ^ 1) * kStageBytes, i, KB);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kSplit));
     __syncthreads();
-    substep(f1, f0, nxt, slot[0], true, 0, 0, 0, 0);
-    ++kt;
-  }
-  {  // K step k_steps-1
-    char* cur = lds + (kt & 1) * kStageBytes;
-    substep(f0, f1, cur, slot[1], true, 0, 0, 0, 0);
-    substep(f1, f0, cur, slot[2], true, 0, 0, 0, 0);
-    substep(f0, f1, cur, slot[3], true, 0, 0, 0, 0);
-    substep(f1, f0, cur, slot[0], false, 0, 0, 0, 0);
-  }
+#pragma unroll
+    for (int r = 0; r < NR; ++r) f0[r] = frag(lds + par * kStageBytes, slot[0], r);
 
-  double ss = 0.0;
+    int kt = 0;
+    for (; kt + 2 < k_steps; ++kt) {
+      const int b = (kt + par) & 1;
+      char* cur = lds + b * kStageBytes;
+      char* nxt = lds + (b ^ 1) * kStageBytes;
+      const uint32_t fre = lds_base + b * kStageBytes;  // stage kt's buffer, refilled with stage kt+2
+      // the rest of stage kt+1's loads (its buffer was freed by the barrier of step kt-1)
+      substep(f0, f1, cur, slot[1], true, cur_t, lds_base + (b ^ 1) * kStageBytes, (kt + 1) * KB, kSplit, 16);
+      substep(f1, f0, cur, slot[2], true, cur_t, 0, 0, 0, 0);
+      substep(f0, f1, cur, slot[3], true, cur_t, 0, 0, 0, 0);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // stage kt+1 has landed
+      __syncthreads();                           // and every wave has read all of stage kt
+      substep(f1, f0, nxt, slot[0], true, cur_t, fre, (kt + 2) * KB, 0, kSplit);
+    }
+    {  // K step k_steps-2: only the rest of stage k_steps-1 left to load
+      const int b = (kt + par) & 1;
+      char* cur = lds + b * kStageBytes;
+      char* nxt = lds + (b ^ 1) * kStageBytes;
+      substep(f0, f1, cur, slot[1], true, cur_t, lds_base + (b ^ 1) * kStageBytes, (kt + 1) * KB, kSplit, 16);
+      substep(f1, f0, cur, slot[2], true, cur_t, 0, 0, 0, 0);
+      substep(f0, f1, cur, slot[3], true, cur_t, 0, 0, 0, 0);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      __syncthreads();  // every wave has read all of stage k_steps-2: its buffer is free
+      substep(f1, f0, nxt, slot[0], true, cur_t, 0, 0, 0, 0);
+      ++kt;
+    }
+    {  // K step k_steps-1; the next tile's stage 0 goes into the buffer just freed
+      const int b = (kt + par) & 1;
+      char* cur = lds + b * kStageBytes;
+      const uint32_t fre = lds_base + (b ^ 1) * kStageBytes;
+      const int nl = has_next ? 16 : 0;
+      substep(f0, f1, cur, slot[1], true, nxt_t, fre, 0, 0, min(nl, 8));
+      substep(f1, f0, cur, slot[2], true, nxt_t, fre, 0, 8, nl);
+      substep(f0, f1, cur, slot[3], true, nxt_t, 0, 0, 0, 0);
+      substep(f1, f0, cur, slot[0], false, nxt_t, 0, 0, 0, 0);
+      par = b ^ 1;
+    }
+
+    double ss = 0.0;
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
+    for (int i = 0; i < FM; ++i) {
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const double v = (double)acc[i][j][e];
-        ss = fma(v, v, ss);
-      }
-    __builtin_amdgcn_sched_barrier(0);
-  }
+        for (int e = 0; e < 16; ++e) {
+          const double v = (double)acc[i][j][e];
+          ss = fma(v, v, ss);
+        }
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
-  __syncthreads();
-  double* red = reinterpret_cast<double*>(lds);
-  if (lane == 0) red[wave] = ss;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const double t = (red[0] + red[1]) + (red[2] + red[3]);
-    tile_sse[(int64_t)cand * tiles_m * tiles_n + (int64_t)tm * tiles_n + tn] = t;
+    for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
+    if (lane == 0) red[wave] = ss;
+    __syncthreads();  // red is complete, and every wave has read the last stage
+    if (threadIdx.x == 0) tile_sse[cur_t.idx] = (red[0] + red[1]) + (red[2] + red[3]);
+    if (!has_next) break;
+    G = Gn;
+    cur_t = nxt_t;
   }
 }
 
@@ -288,12 +320,21 @@ hipError_t launch_error_sse(const void* x, int64_t ld_x, const void* delta, int 
   const int tiles_n = (int)((d_out + BN - 1) / BN);
   const int n_cols = tiles_n * n_cand;
   const int64_t nblk = (int64_t)tiles_m * n_cols;
+  // one persistent workgroup per compute unit (the tile order assumes 8 XCDs dealt round-robin)
+  static thread_local int cus = 0;
+  if (cus == 0) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess || cus <= 0) cus = 256;
+  }
+  const unsigned grid = (unsigned)std::min<int64_t>(nblk, cus);
   if (dtype == 1)
-    hipLaunchKernelGGL((error_sse_kernel<uint16_t>), dim3((unsigned)nblk), dim3(kThreads), 0, st,
+    hipLaunchKernelGGL((error_sse_kernel<uint16_t>), dim3(grid), dim3(kThreads), 0, st,
                        static_cast<const uint16_t*>(x), ld_x, static_cast<const uint16_t*>(delta),
                        n_tokens, d_in, d_out, tiles_m, tiles_n, n_cols, tile_sse);
   else
-    hipLaunchKernelGGL((error_sse_kernel<float>), dim3((unsigned)nblk), dim3(kThreads), 0, st,
+    hipLaunchKernelGGL((error_sse_kernel<float>), dim3(grid), dim3(kThreads), 0, st,
                        static_cast<const float*>(x), ld_x, static_cast<const float*>(delta), n_tokens,
                        d_in, d_out, tiles_m, tiles_n, n_cols, tile_sse);
   return hipGetLastError();
