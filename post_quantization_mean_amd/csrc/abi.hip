@@ -64,7 +64,7 @@ int check_x(const void* x, int dtype, int64_t n_tokens, int64_t d_in, int64_t ld
   return AWQ_OK;
 }
 
-int make_parts(const void* const* w_parts, const int64_t* part_rows, int n_parts, int64_t d_in,
+int make_parts(const void* const* w_parts, const int64_t* part_rows, int n_parts, int dtype, int64_t d_in,
                awq::WParts* out) {
   if (!w_parts || !part_rows) return fail(AWQ_ERR_NULL, "w_parts or part_rows is NULL");
   if (n_parts < 1 || n_parts > AWQ_MAX_PARTS)
@@ -82,7 +82,19 @@ int make_parts(const void* const* w_parts, const int64_t* part_rows, int n_parts
   }
   for (int p = n_parts; p <= AWQ_MAX_PARTS; ++p) out->row_begin[p] = rows;
   if (rows > ((int64_t)65535 * 128)) return fail(AWQ_ERR_UNSUPPORTED, "d_out %lld too large", (long long)rows);
-  (void)d_in;
+  // parts that lie back to back in memory (row slices of one stacked matrix) are one matrix to
+  // the kernels, which then skip the per-row part lookup
+  bool contiguous = true;
+  const int64_t row_bytes = d_in * esize(dtype);
+  for (int p = 1; p < n_parts; ++p)
+    contiguous = contiguous && (const char*)w_parts[p] == (const char*)w_parts[0] + out->row_begin[p] * row_bytes;
+  if (contiguous && n_parts > 1) {
+    out->n = 1;
+    for (int p = 1; p <= AWQ_MAX_PARTS; ++p) {
+      if (p < AWQ_MAX_PARTS) out->ptr[p] = nullptr;
+      out->row_begin[p] = rows;
+    }
+  }
   return AWQ_OK;
 }
 
@@ -163,7 +175,7 @@ int awq_quant_delta(const void* const* w_parts, const int64_t* part_rows, int n_
   TRY(check_group(group_size, d_in));
   TRY(check_d_in_bytes(dtype, d_in));
   awq::WParts w;
-  TRY(make_parts(w_parts, part_rows, n_parts, d_in, &w));
+  TRY(make_parts(w_parts, part_rows, n_parts, dtype, d_in, &w));
   if (!cand_scales || !delta) return fail(AWQ_ERR_NULL, "cand_scales or delta is NULL");
   if (n_cand < 1) return fail(AWQ_ERR_ARG, "n_cand %d < 1", n_cand);
   if (!aligned(delta, 16)) return fail(AWQ_ERR_UNSUPPORTED, "delta is not 16-byte aligned");
@@ -231,7 +243,7 @@ int awq_search_scales(const void* x, int64_t ld_x, const void* const* w_parts,
   TRY(check_d_in_bytes(dtype, d_in));
   TRY(check_x(x, dtype, n_tokens, d_in, ld_x));
   awq::WParts w;
-  TRY(make_parts(w_parts, part_rows, n_parts, d_in, &w));
+  TRY(make_parts(w_parts, part_rows, n_parts, dtype, d_in, &w));
   const int64_t d_out = w.row_begin[w.n];
   if (!act_mean || !cand_scales || !losses || !best_scales || !best_info)
     return fail(AWQ_ERR_NULL, "a required pointer is NULL");
@@ -274,7 +286,7 @@ int awq_quantize_pack(const void* const* w_parts, const int64_t* part_rows, int 
   TRY(check_group(group_size, d_in));
   TRY(check_d_in_bytes(dtype, d_in));
   awq::WParts w;
-  TRY(make_parts(w_parts, part_rows, n_parts, d_in, &w));
+  TRY(make_parts(w_parts, part_rows, n_parts, dtype, d_in, &w));
   if (!s || !codes || !qscales || !zeros) return fail(AWQ_ERR_NULL, "s, codes, qscales or zeros is NULL");
   if (!aligned(codes, 16) || !aligned(qscales, 4) || !aligned(zeros, 4))
     return fail(AWQ_ERR_UNSUPPORTED, "codes must be 16-byte aligned, qscales and zeros 4-byte aligned");

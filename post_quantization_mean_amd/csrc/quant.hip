@@ -39,6 +39,15 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kRows = 4;               // rows per wave (per lane)
 constexpr int kRowsPerBlock = 4 * kRows;
+#ifndef AWQ_PACK_ROWS
+#define AWQ_PACK_ROWS 4
+#endif
+#ifndef AWQ_PACK_DEPTH
+#define AWQ_PACK_DEPTH 1
+#endif
+constexpr int kPackRows = AWQ_PACK_ROWS;    // pack: rows per wave per row block
+constexpr int kPackRowsPerBlock = 4 * kPackRows;
+constexpr int kPackDepth = AWQ_PACK_DEPTH;  // pack: row blocks in flight ahead of the current one
 
 // Layout of both kernels: 16 channels per lane, 8 lanes per group, 1024 channels per block
 constexpr int kChans = 16;
@@ -62,11 +71,15 @@ __device__ __forceinline__ float dpp_f32(float v) {
 
 template <typename T>
 __device__ __forceinline__ const T* row_ptr(const WParts& w, int64_t o, int64_t d_in) {
+  // stacked rows fit in 32 bits (the C ABI caps d_out); the part search stays in scalar
+  // registers when o is wave-uniform
+  const int o32 = (int)o;
+  if (w.n == 1) return static_cast<const T*>(w.ptr[0]) + (int64_t)o32 * d_in;
   int p = 0;
 #pragma unroll
   for (int i = 1; i < kMaxParts; ++i)
-    if (i < w.n && o >= w.row_begin[i]) p = i;
-  return static_cast<const T*>(w.ptr[p]) + (o - w.row_begin[p]) * d_in;
+    if (i < w.n && o32 >= (int)w.row_begin[i]) p = i;
+  return static_cast<const T*>(w.ptr[p]) + (int64_t)(o32 - (int)w.row_begin[p]) * d_in;
 }
 
 // A lane's E weights of one row, kept in their storage format (bf16 stays packed two per
@@ -249,7 +262,7 @@ __global__ __launch_bounds__(kThreads) void quant_delta_kernel(WParts w, int64_t
   __shared__ __attribute__((aligned(16))) float xpose[4][kGroup];  // per wave: one group's weights
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: row math stays scalar
   const int64_t cb = (int64_t)blockIdx.x * kChansPerBlock;
   const int cl = lane * E;  // group lane/8, 16-channel slice lane%8: channels cb + 16*lane ..
   const int64_t c0 = cb + cl;
@@ -390,27 +403,31 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(WParts w, int64
   __shared__ __attribute__((aligned(16))) float xpose[4][kGroup];  // per wave: one group's weights
   __shared__ uint4 slot[4][RawRow<T, E>::NV * 64];                 // per wave: one row slice
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: row math stays scalar
   const int64_t cb = (int64_t)blockIdx.x * kChansPerBlock;
   const int64_t c0 = cb + lane * E;
   const bool col_ok = c0 < d_in;
   const int64_t n_groups = d_in / kGroup;
-  const int64_t n_rb = (d_out + kRowsPerBlock - 1) / kRowsPerBlock;
-  // Row blocks blockIdx.y, blockIdx.y + gridDim.y, ...; the next one's weights are loaded while
-  // the current one is quantized.
+  const int64_t n_rb = (d_out + kPackRowsPerBlock - 1) / kPackRowsPerBlock;
+  // Row blocks blockIdx.y, blockIdx.y + gridDim.y, ...; the weights of the next kPackDepth row
+  // blocks are in flight while the current one is quantized.
   const int valid16 = (int)((std::min<int64_t>(d_in - cb, kChansPerBlock) * (int64_t)sizeof(T)) / 16);
-  auto load_rows = [&](RawRow<T, E>(&dst)[kRows], int64_t rb) {
+  auto load_rows = [&](RawRow<T, E>(&dst)[kPackRows], int64_t rb) {
 #pragma unroll
-    for (int i = 0; i < kRows; ++i) {
-      const int64_t o = rb * kRowsPerBlock + wave * kRows + i;
+    for (int i = 0; i < kPackRows; ++i) {
+      const int64_t o = rb * kPackRowsPerBlock + wave * kPackRows + i;
       if (o < d_out)
         dst[i].load(row_ptr<T>(w, o, d_in) + cb, valid16, lane);
       else
         dst[i].zero();
     }
   };
-  RawRow<T, E> raw[kRows], rawn[kRows];
-  load_rows(raw, blockIdx.y);
+  RawRow<T, E> raw[kPackDepth + 1][kPackRows];
+#pragma unroll
+  for (int d = 0; d <= kPackDepth; ++d) {
+    const int64_t rb = blockIdx.y + (int64_t)d * gridDim.y;
+    if (d < kPackDepth && rb < n_rb) load_rows(raw[d], rb);
+  }
   float s[E];
 #pragma unroll
   for (int j = 0; j < E; j += 2) {
@@ -421,14 +438,14 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(WParts w, int64
   }
 
   for (int64_t rb = blockIdx.y; rb < n_rb; rb += gridDim.y) {
-    const int64_t row0 = rb * kRowsPerBlock + wave * kRows;
-    RowE<T, E> wv[kRows];
+    const int64_t row0 = rb * kPackRowsPerBlock + wave * kPackRows;
+    RowE<T, E> wv[kPackRows];
 #pragma unroll
-    for (int i = 0; i < kRows; ++i) raw[i].regroup(slot[wave], lane, wv[i]);
-    if (rb + gridDim.y < n_rb) load_rows(rawn, rb + gridDim.y);
-    uint64_t bad[kRows];
+    for (int i = 0; i < kPackRows; ++i) raw[0][i].regroup(slot[wave], lane, wv[i]);
+    if (rb + (int64_t)kPackDepth * gridDim.y < n_rb) load_rows(raw[kPackDepth], rb + (int64_t)kPackDepth * gridDim.y);
+    uint64_t bad[kPackRows];
 #pragma unroll
-    for (int i = 0; i < kRows; ++i) {
+    for (int i = 0; i < kPackRows; ++i) {
       float y[E];
 #pragma unroll
       for (int j = 0; j < E; ++j) y[j] = wv[i][j] * s[j];
@@ -460,7 +477,7 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(WParts w, int64
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int i = 0; i < kRows; ++i) {
+    for (int i = 0; i < kPackRows; ++i) {
       uint64_t m = bad[i];
       const int64_t o = row0 + i;
       while (m) {
@@ -480,7 +497,9 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(WParts w, int64
       }
     }
 #pragma unroll
-    for (int i = 0; i < kRows; ++i) raw[i] = rawn[i];
+    for (int d = 0; d < kPackDepth; ++d)
+#pragma unroll
+      for (int i = 0; i < kPackRows; ++i) raw[d][i] = raw[d + 1][i];
   }
 }
 
@@ -505,7 +524,7 @@ hipError_t launch_quantize_pack(const WParts& w, int dtype, int64_t d_in, const 
   const int64_t d_out = w.row_begin[w.n];
   // about three resident blocks per compute unit, each looping over row blocks
   const int64_t col_blocks = (d_in + kChansPerBlock - 1) / kChansPerBlock;
-  const int64_t row_blocks = (d_out + kRowsPerBlock - 1) / kRowsPerBlock;
+  const int64_t row_blocks = (d_out + kPackRowsPerBlock - 1) / kPackRowsPerBlock;
   const int64_t ry = std::max<int64_t>(1, std::min<int64_t>(row_blocks, 768 / col_blocks));
   dim3 grid((unsigned)col_blocks, (unsigned)ry);
   if (dtype == 1)
