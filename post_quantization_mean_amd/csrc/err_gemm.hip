@@ -204,19 +204,22 @@ void error_sse_kernel(const T* __restrict__ x, int64_t ld_x, const T* __restrict
     const int off = r < FM ? ra_off + r * 32 * KB : rb_off + (r - FM) * 32 * KB;
     return *reinterpret_cast<const uint4*>(stage + off + sl);
   };
-  // one sub-step: 16 MFMAs on `use`; between MFMA pairs, the next sub-step's 8 fragment reads
-  // (if `reads`) and loads [l0, l1) of tile `lt`'s stage at LDS address `fstage`, K offset kbyte
+  // one sub-step: 16 MFMAs on `use`; between the two MFMAs of each of its 8 pairs, at most one
+  // load (of [l0, l1), tile `lt`'s stage at LDS address `fstage`, K offset kbyte) and one of the
+  // next sub-step's fragment reads (if `reads`). A load holds up the wave's issue for about as
+  // long as the texture unit takes to accept its 64 addresses, so one per MFMA keeps the matrix
+  // core fed (two back to back left it idle for ~10 % of the cycles).
   auto substep = [&](const uint4 (&use)[NR], uint4 (&nxt)[NR], const char* src, int sl, bool reads,
                      const TileOps& lt, uint32_t fstage, int kbyte, int l0, int l1) {
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
       const int fm = g >> 1, fn = (g & 1) * 2;
       mma_pair<T>(use[fm], use[FM + fn], acc[fm][fn]);
-      mma_pair<T>(use[fm], use[FM + fn + 1], acc[fm][fn + 1]);
       __builtin_amdgcn_sched_barrier(0);
-      if (l0 + 2 * g < l1) issue(lt, fstage, l0 + 2 * g, kbyte);
-      if (l0 + 2 * g + 1 < l1) issue(lt, fstage, l0 + 2 * g + 1, kbyte);
+      if (l0 + g < l1) issue(lt, fstage, l0 + g, kbyte);
       if (reads) nxt[g] = frag(src, sl, g);
+      __builtin_amdgcn_sched_barrier(0);
+      mma_pair<T>(use[fm], use[FM + fn + 1], acc[fm][fn + 1]);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
