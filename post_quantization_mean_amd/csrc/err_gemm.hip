@@ -27,6 +27,7 @@
 // (see the kernel), so operand K-slices are shared inside each XCD's L2 and across the XCDs in the
 // memory-side cache.
 #include <algorithm>
+#include <type_traits>
 
 #include "internal.h"
 
@@ -78,16 +79,19 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, int num_records) {
   return r;
 }
 
-// One 16-byte fragment pair: a 32 x 32 x (16 bf16 | 8 f32) product into one accumulator.
-template <typename T>
+// One 16-byte fragment pair: a 32 x 32 x (16 bf16 | 8 f32) product into one accumulator; with ZC
+// the accumulator's old value is not read (the matrix core adds to zero), which starts a tile
+// without clearing 256 accumulator registers.
+template <typename T, bool ZC = false>
 __device__ __forceinline__ void mma_pair(const uint4& a, const uint4& b, f32x16& c) {
+  const f32x16 zero = {};
   if constexpr (sizeof(T) == 2) {
-    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
-                                                0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                ZC ? zero : c, 0, 0, 0);
   } else {
     // four K=2 steps; lane half h contributes K index 4h+e of the 8-wide chunk pair in step e,
     // identically for both operands
-    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.x), __uint_as_float(b.x), ZC ? zero : c, 0, 0, 0);
     c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
     c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
     c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
@@ -209,20 +213,24 @@ void error_sse_kernel(const T* __restrict__ x, int64_t ld_x, const T* __restrict
   // next sub-step's fragment reads (if `reads`). A load holds up the wave's issue for about as
   // long as the texture unit takes to accept its 64 addresses, so one per MFMA keeps the matrix
   // core fed (two back to back left it idle for ~10 % of the cycles).
-  auto substep = [&](const uint4 (&use)[NR], uint4 (&nxt)[NR], const char* src, int sl, bool reads,
+  // (zc: the tile's first sub-step, which writes every accumulator once from zero)
+  auto substep = [&](auto zc, const uint4 (&use)[NR], uint4 (&nxt)[NR], const char* src, int sl, bool reads,
                      const TileOps& lt, uint32_t fstage, int kbyte, int l0, int l1) {
+    constexpr bool ZC = decltype(zc)::value;
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
       const int fm = g >> 1, fn = (g & 1) * 2;
-      mma_pair<T>(use[fm], use[FM + fn], acc[fm][fn]);
+      mma_pair<T, ZC>(use[fm], use[FM + fn], acc[fm][fn]);
       __builtin_amdgcn_sched_barrier(0);
       if (l0 + g < l1) issue(lt, fstage, l0 + g, kbyte);
       if (reads) nxt[g] = frag(src, sl, g);
       __builtin_amdgcn_sched_barrier(0);
-      mma_pair<T>(use[fm], use[FM + fn + 1], acc[fm][fn + 1]);
+      mma_pair<T, ZC>(use[fm], use[FM + fn + 1], acc[fm][fn + 1]);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
+  const std::false_type acc_in{};
+  const std::true_type acc_zero{};
 
   int G = blockIdx.x;
   if (G >= nblk) return;
@@ -236,13 +244,6 @@ void error_sse_kernel(const T* __restrict__ x, int64_t ld_x, const T* __restrict
     const bool has_next = Gn < nblk;
     const TileOps nxt_t =
         tile_ops<T>(has_next ? Gn : G, x, ld_x, delta, n_tokens, d_in, d_out, tiles_m, tiles_n, n_cols);
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-
     uint4 f0[NR], f1[NR];
     // stage 0 is in flight in buffer par; the first kSplit loads of stage 1 go to the other
     // buffer (free: every wave passed the previous tile's final barrier); wait for stage 0
@@ -253,54 +254,63 @@ void error_sse_kernel(const T* __restrict__ x, int64_t ld_x, const T* __restrict
 #pragma unroll
     for (int r = 0; r < NR; ++r) f0[r] = frag(lds + par * kStageBytes, slot[0], r);
 
+    // A K step is four sub-steps A B C D on fragment slots 0..3 (each sub-step reads the next
+    // one's fragments); the loop runs B C | barrier | D A', so that K step 0's A, which starts
+    // the accumulators, stays outside it. Loads: the rest of stage kt+1 in A(kt), the first
+    // kSplit of stage kt+2 in D(kt) into the buffer the barrier of step kt freed.
+    substep(acc_zero, f0, f1, lds + par * kStageBytes, slot[1], true, cur_t, lds_base + (par ^ 1) * kStageBytes, KB,
+            kSplit, 16);
     int kt = 0;
     for (; kt + 2 < k_steps; ++kt) {
       const int b = (kt + par) & 1;
       char* cur = lds + b * kStageBytes;
       char* nxt = lds + (b ^ 1) * kStageBytes;
       const uint32_t fre = lds_base + b * kStageBytes;  // stage kt's buffer, refilled with stage kt+2
-      // the rest of stage kt+1's loads (its buffer was freed by the barrier of step kt-1)
-      substep(f0, f1, cur, slot[1], true, cur_t, lds_base + (b ^ 1) * kStageBytes, (kt + 1) * KB, kSplit, 16);
-      substep(f1, f0, cur, slot[2], true, cur_t, 0, 0, 0, 0);
-      substep(f0, f1, cur, slot[3], true, cur_t, 0, 0, 0, 0);
+      substep(acc_in, f1, f0, cur, slot[2], true, cur_t, 0, 0, 0, 0);
+      substep(acc_in, f0, f1, cur, slot[3], true, cur_t, 0, 0, 0, 0);
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // stage kt+1 has landed
       __syncthreads();                           // and every wave has read all of stage kt
-      substep(f1, f0, nxt, slot[0], true, cur_t, fre, (kt + 2) * KB, 0, kSplit);
+      substep(acc_in, f1, f0, nxt, slot[0], true, cur_t, fre, (kt + 2) * KB, 0, kSplit);
+      substep(acc_in, f0, f1, nxt, slot[1], true, cur_t, fre, (kt + 2) * KB, kSplit, 16);
     }
-    {  // K step k_steps-2: only the rest of stage k_steps-1 left to load
+    {  // K step k_steps-2 (B C D), then A of the last step, which starts the next tile's stage 0
+      // in the buffer this step's barrier freed
       const int b = (kt + par) & 1;
       char* cur = lds + b * kStageBytes;
       char* nxt = lds + (b ^ 1) * kStageBytes;
-      substep(f0, f1, cur, slot[1], true, cur_t, lds_base + (b ^ 1) * kStageBytes, (kt + 1) * KB, kSplit, 16);
-      substep(f1, f0, cur, slot[2], true, cur_t, 0, 0, 0, 0);
-      substep(f0, f1, cur, slot[3], true, cur_t, 0, 0, 0, 0);
+      const uint32_t fre = lds_base + b * kStageBytes;
+      const int nl = has_next ? 16 : 0;
+      substep(acc_in, f1, f0, cur, slot[2], true, cur_t, 0, 0, 0, 0);
+      substep(acc_in, f0, f1, cur, slot[3], true, cur_t, 0, 0, 0, 0);
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       __syncthreads();  // every wave has read all of stage k_steps-2: its buffer is free
-      substep(f1, f0, nxt, slot[0], true, cur_t, 0, 0, 0, 0);
+      substep(acc_in, f1, f0, nxt, slot[0], true, cur_t, 0, 0, 0, 0);
+      substep(acc_in, f0, f1, nxt, slot[1], true, nxt_t, fre, 0, 0, min(nl, 8));
       ++kt;
     }
-    {  // K step k_steps-1; the next tile's stage 0 goes into the buffer just freed
+    {  // K step k_steps-1: B C D
       const int b = (kt + par) & 1;
       char* cur = lds + b * kStageBytes;
       const uint32_t fre = lds_base + (b ^ 1) * kStageBytes;
       const int nl = has_next ? 16 : 0;
-      substep(f0, f1, cur, slot[1], true, nxt_t, fre, 0, 0, min(nl, 8));
-      substep(f1, f0, cur, slot[2], true, nxt_t, fre, 0, 8, nl);
-      substep(f0, f1, cur, slot[3], true, nxt_t, 0, 0, 0, 0);
-      substep(f1, f0, cur, slot[0], false, nxt_t, 0, 0, 0, 0);
+      substep(acc_in, f1, f0, cur, slot[2], true, nxt_t, fre, 0, 8, nl);
+      substep(acc_in, f0, f1, cur, slot[3], true, nxt_t, 0, 0, 0, 0);
+      substep(acc_in, f1, f0, cur, slot[0], false, nxt_t, 0, 0, 0, 0);
       par = b ^ 1;
     }
 
+    // sum of squares: each accumulator's 16 values in float32 (relative error below 1e-6), the
+    // 16 accumulators and then lanes, waves in float64
     double ss = 0.0;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
+      for (int j = 0; j < FN; ++j) {
+        float s32 = 0.f;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const double v = (double)acc[i][j][e];
-          ss = fma(v, v, ss);
-        }
+        for (int e = 0; e < 16; ++e) s32 = fmaf(acc[i][j][e], acc[i][j][e], s32);
+        ss += (double)s32;
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
