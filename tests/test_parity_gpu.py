@@ -30,20 +30,31 @@ def _case(wl, parts=None):
     return x, w, parts
 
 
-def _gpu_parts(w, parts):
+def _gpu_parts(w, parts, separate=False):
+    """Row slices of one stacked device matrix, or (separate) copies placed apart in memory, which
+    makes the kernels look up each row's part."""
     wt = to_torch(w, "cuda")
     out, r = [], 0
+    if separate:
+        gap = 3  # rows of padding between parts
+        buf = torch.zeros((wt.shape[0] + gap * (len(parts) + 1), wt.shape[1]), dtype=wt.dtype, device="cuda")
+        for i, p in enumerate(parts):
+            o = r + gap * (i + 1)
+            buf[o:o + p].copy_(wt[r:r + p])
+            out.append(buf[o:o + p])
+            r += p
+        return out
     for p in parts:
-        out.append(wt[r:r + p].contiguous())
+        out.append(wt[r:r + p])
         r += p
     return out
 
 
-def _run_gpu(B, x, w, parts, n_grid, cand_per_pass=None):
+def _run_gpu(B, x, w, parts, n_grid, cand_per_pass=None, separate=False):
     print(f"[gpu case] x{tuple(x.shape)} {x.dtype} w{tuple(w.shape)} parts={parts} n_grid={n_grid} "
-          f"cpp={cand_per_pass}", flush=True)
+          f"cpp={cand_per_pass} separate={separate}", flush=True)
     xt = to_torch(x, "cuda")
-    wp = _gpu_parts(w, parts)
+    wp = _gpu_parts(w, parts, separate)
     act = B.awq_act_stats(xt)
     res = B.awq_search_scales(xt, wp, act, n_grid, cand_per_pass=cand_per_pass)
     pk = B.awq_quantize_pack(wp, res["best_scales"])
@@ -54,8 +65,8 @@ def _run_gpu(B, x, w, parts, n_grid, cand_per_pass=None):
     return out, xt, wp
 
 
-def _check_full(B, x, w, parts, n_grid, cand_per_pass=None, per_candidate_codes=True):
-    g, xt, wp = _run_gpu(B, x, w, parts, n_grid, cand_per_pass)
+def _check_full(B, x, w, parts, n_grid, cand_per_pass=None, per_candidate_codes=True, separate=False):
+    g, xt, wp = _run_gpu(B, x, w, parts, n_grid, cand_per_pass, separate)
     X, W = to_f32(x).astype(np.float64), to_f32(w).astype(np.float64)
     ref = O.search_scales(X, W, 128, n_grid)
     assert P.max_rel(g["act_mean"], ref.act_mean) < P.ACT_RTOL
@@ -93,10 +104,11 @@ def test_config1_tiny_fp32_end_to_end(B):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_ragged_fused_parts(B, dtype):
+@pytest.mark.parametrize("separate", [False, True])
+def test_ragged_fused_parts(B, dtype, separate):
     wl = custom_workload(600, 384, 520, dtype, n_grid=7, outlier_channels=4, config_id=101)
     x, w, parts = _case(wl, (200, 136, 184))
-    _check_full(B, x, w, parts, 7)
+    _check_full(B, x, w, parts, 7, separate=separate)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
