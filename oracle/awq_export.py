@@ -1,0 +1,116 @@
+"""CPU oracle for the steps either side of the AWQ search: the activation statistic gathered over
+several calibration batches, folding the inverse scales into the source operator, and the compact
+deployment form of the per-group quantization parameters.
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE. Only the tests, the smoke check and the CPU baseline leg
+of the benchmark may import or run this module. The GPU library never calls it and shares no code
+with it.
+
+Pages cited below, by title and section:
+
+* msModelSlim docs, "AWQ：激活感知权重量化算法说明": 预处理阶段 (forward hooks collect the
+  per-channel mean of |activation| while calibration batches run), 支持的子图类型 (after the
+  search the norm gets the inverse scaling and the linears the forward scaling — norm-linear;
+  linear1 inverse / linear2 forward — linear-linear; v_proj inverse / o_proj forward — ov;
+  up_proj inverse / down_proj forward — up-down).
+* gsyq.cn, "AWQ 离群激活平滑实操：逐通道等价缩放与 4-bit 精度无损转换", section 四 (fold
+  diag(s)^-1 into the preceding normalisation so that the equivalence X W^T =
+  (X diag(s)^-1)(W diag(s))^T holds without an extra operator).
+* bjdmk.com.cn AWQ article, section "GPU 硬件级反量化算子内联融合" (deployment: packed 4-bit
+  weights with FP16 per-group scales and offsets, unpacked from the low and high 4 bits).
+
+Readings taken where the pages are silent:
+
+* Statistic over batches: the mean over the concatenation of all batches, i.e. per-channel sums
+  of |X| accumulated batch by batch and divided by the total token count once.
+* Fold: row c of the source operator (the norm weight, or row c of the source linear's weight and
+  its bias) is divided by s[c]. The quotient is formed in float64, rounded to float32 and then to
+  the storage dtype (round to nearest even at each step), as a float32 computation stored in the
+  model's dtype would round it.
+* Deployment form: each float32 step rounded to float16 (nearest even); zero points packed two per
+  byte along the groups of a row, even group in the low nibble, clipped to [0, 15] (a zero point
+  outside that range — only one-signed groups have one — is counted, since the packed form cannot
+  hold it; the int32 zero points stay exact). Steps whose float16 value is not a normal number
+  (below 2^-14 or overflowing) are counted too.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def act_sums(X) -> np.ndarray:
+    """Per-channel sum of |X| over the tokens of one batch, in float64 (msModelSlim 预处理阶段)."""
+    X = np.asarray(X, dtype=np.float64)
+    if X.ndim != 2:
+        raise ValueError("X must be [tokens, d_in]")
+    return np.abs(X).sum(axis=0)
+
+
+def act_mean_batches(batches) -> np.ndarray:
+    """Mean of |X| over all tokens of all batches: the batch sums added, then divided once."""
+    total = None
+    n = 0
+    for X in batches:
+        s = act_sums(X)
+        total = s if total is None else total + s
+        n += np.asarray(X).shape[0]
+    if total is None or n == 0:
+        raise ValueError("no tokens")
+    return total / n
+
+
+def f32_to_bf16_rne(v) -> np.ndarray:
+    """float32 -> bfloat16 bits (uint16), round to nearest even; NaN stays a quiet NaN."""
+    a = np.ascontiguousarray(np.asarray(v, dtype=np.float32))
+    u = a.view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    nan = np.isnan(a)
+    out = rounded.astype(np.uint16)
+    out[nan] = ((u[nan] >> 16) | 0x40).astype(np.uint16)
+    return out
+
+
+def fold_scales(src, s, dtype: str):
+    """Source-side inverse scaling: row c of ``src`` ([rows, cols]) divided by s[c].
+
+    Returns the stored values: float32 for ``dtype == "f32"``, bfloat16 bits (uint16) for
+    ``dtype == "bf16"``; the quotient is float64, rounded to float32, then to the dtype."""
+    src = np.asarray(src, dtype=np.float64)
+    s = np.asarray(s, dtype=np.float64)
+    if src.ndim == 1:
+        src = src[:, None]
+    if src.shape[0] != s.shape[0]:
+        raise ValueError("one scale per source row")
+    with np.errstate(over="ignore", invalid="ignore", divide="ignore"):
+        q32 = (src / s[:, None]).astype(np.float32)
+    if dtype == "f32":
+        return q32
+    if dtype == "bf16":
+        return f32_to_bf16_rne(q32)
+    raise ValueError(dtype)
+
+
+def export_fp16(qscales_f32, zeros):
+    """Deployment form of the per-group parameters of a [rows, groups] export.
+
+    Returns (steps as float16 bits [rows, groups] uint16, zero points packed two per byte
+    [rows, ceil(groups / 2)] uint8, count of zero points outside [0, 15], count of steps whose
+    float16 value is not a normal number)."""
+    qs = np.asarray(qscales_f32, dtype=np.float32)
+    z = np.asarray(zeros, dtype=np.int64)
+    if qs.shape != z.shape or qs.ndim != 2:
+        raise ValueError("qscales and zeros must both be [rows, groups]")
+    with np.errstate(over="ignore", invalid="ignore"):
+        h = qs.astype(np.float16)
+    hb = h.view(np.uint16)
+    with np.errstate(invalid="ignore"):
+        bad_step = ~(np.isfinite(h) & (np.abs(h.astype(np.float32)) >= np.float32(2.0 ** -14)))
+    zc = np.clip(z, 0, 15)
+    bad_zero = z != zc
+    rows, g = z.shape
+    gp = (g + 1) // 2
+    packed = np.zeros((rows, gp), dtype=np.uint8)
+    packed |= zc[:, 0::2].astype(np.uint8)
+    if g > 1:
+        packed[:, : g // 2] |= (zc[:, 1::2].astype(np.uint8) << 4)
+    return hb, packed, int(bad_zero.sum()), int(bad_step.sum())

@@ -1,0 +1,88 @@
+"""Pins for the oracle of the steps either side of the search (statistic over batches, source
+fold, deployment form), from hand-worked values and identities of the pages (CPU only)."""
+import numpy as np
+import pytest
+
+from oracle import awq_export as X
+from oracle import awq_oracle as O
+
+
+def test_statistic_over_batches_hand_values():
+    # |X| over three tokens in two batches: channel 0 = (1 + 3 + 5) / 3, channel 1 = (2 + 4 + 6) / 3
+    b1 = np.array([[1.0, -2.0], [3.0, 4.0]])
+    b2 = np.array([[-5.0, 6.0]])
+    assert np.array_equal(X.act_sums(b1), [4.0, 6.0])
+    assert np.array_equal(X.act_mean_batches([b1, b2]), [3.0, 4.0])
+
+
+def test_statistic_does_not_depend_on_the_split():
+    rng = np.random.default_rng(3)
+    x = np.round(rng.standard_normal((97, 5)) * 64) / 64  # exact binary fractions: exact sums
+    whole = X.act_mean_batches([x])
+    for cuts in ([10, 50], [1, 2, 3, 96], [48]):
+        parts = np.split(x, cuts)
+        assert np.array_equal(X.act_mean_batches(parts), whole)
+    assert np.array_equal(whole, np.abs(x).sum(axis=0) / 97)
+    with pytest.raises(ValueError):
+        X.act_mean_batches([])
+
+
+def test_fold_hand_values_and_direction():
+    src = np.array([[1.0, 2.0], [3.0, 6.0]])
+    assert np.array_equal(X.fold_scales(src, [2.0, 3.0], "f32"), np.array([[0.5, 1.0], [1.0, 2.0]], np.float32))
+    # a vector (a norm weight) is one column
+    assert np.array_equal(X.fold_scales(np.array([4.0, 9.0]), [2.0, 3.0], "f32")[:, 0], [2.0, 3.0])
+
+
+def test_fold_bf16_rounding_hand_values():
+    # 1/3 in float32 is 0x3EAAAAAB -> low half 0xAAAB above the midpoint -> 0x3EAB
+    assert X.fold_scales(np.array([[1.0]]), [3.0], "bf16")[0, 0] == 0x3EAB
+    # exact ties go to the even neighbour: 0x3F808000 -> 0x3F80, 0x3F818000 -> 0x3F82
+    assert X.fold_scales(np.array([[1.00390625]]), [1.0], "bf16")[0, 0] == 0x3F80
+    assert X.fold_scales(np.array([[1.01171875]]), [1.0], "bf16")[0, 0] == 0x3F82
+    # overflow to infinity, NaN stays NaN
+    assert X.fold_scales(np.array([[3.0e38]]), [1e-3], "bf16")[0, 0] == 0x7F80
+    assert (X.fold_scales(np.array([[np.nan]]), [1.0], "bf16")[0, 0] & 0x7FC0) == 0x7FC0
+
+
+def test_fold_keeps_the_layer_output():
+    # gsyq section 四: (x * gamma) W^T == (x * gamma / s) (W * s)^T; the fold must divide the source
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((7, 16))
+    gamma = rng.uniform(0.5, 2.0, 16)
+    W = rng.standard_normal((9, 16))
+    s = rng.uniform(0.1, 10.0, 16)
+    ref = (x * gamma) @ W.T
+    g2 = X.fold_scales(gamma, s, "f32")[:, 0].astype(np.float64)
+    got = (x * g2) @ (W * s).T
+    assert np.allclose(got, ref, rtol=1e-5, atol=1e-6)
+    wrong = (x * gamma * s) @ (W * s).T
+    assert not np.allclose(wrong, ref, rtol=1e-2)
+    # the source linear of linear-linear / up-down: its output rows are divided
+    W1 = rng.standard_normal((16, 11))
+    h = rng.standard_normal((3, 11))
+    ref2 = (h @ W1.T) @ W.T
+    got2 = (h @ X.fold_scales(W1, s, "f32").astype(np.float64).T) @ (W * s).T
+    assert np.allclose(got2, ref2, rtol=1e-5, atol=1e-5)
+
+
+def test_export_fp16_hand_values():
+    qs = np.array([[0.1, 1e-5, 70000.0, 0.5]], np.float32)
+    zeros = np.array([[3, 16, -1, 15]])
+    hb, packed, bad_z, bad_s = X.export_fp16(qs, zeros)
+    assert list(hb[0]) == [0x2E66, 0x00A8, 0x7C00, 0x3800]
+    assert list(packed[0]) == [0x03 | (0x0F << 4), 0x00 | (0x0F << 4)]
+    assert bad_z == 2 and bad_s == 2
+    hb, packed, bad_z, bad_s = X.export_fp16(np.ones((1, 3), np.float32), np.array([[1, 2, 3]]))
+    assert list(packed[0]) == [0x21, 0x03] and bad_z == 0 and bad_s == 0
+
+
+def test_export_of_an_oracle_pack_unpacks_to_its_codes_parameters():
+    rng = np.random.default_rng(9)
+    W = rng.standard_normal((4, 256)) * 0.02
+    pq = O.quantize_pack(W, np.ones(256), 128)
+    hb, packed, bad_z, bad_s = X.export_fp16(pq.qscales.astype(np.float32), pq.zeros)
+    assert bad_z == 0 and bad_s == 0
+    lo, hi = packed & 0xF, packed >> 4
+    assert np.array_equal(np.stack([lo, hi], -1).reshape(4, -1)[:, :2], pq.zeros)
+    assert np.allclose(hb.view(np.float16).astype(np.float64), pq.qscales, rtol=2.0 ** -11)
