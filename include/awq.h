@@ -58,7 +58,7 @@ extern "C" {
 #define AWQ_API
 #endif
 
-#define AWQ_ABI_VERSION 1
+#define AWQ_ABI_VERSION 2
 #define AWQ_MAX_PARTS 8
 #define AWQ_GROUP_SIZE 128
 
@@ -124,7 +124,8 @@ AWQ_API int awq_candidate_scales(const double* act_mean, int64_t d_in, int n_gri
  *   y = W * s (per input channel), asymmetric INT4 group quantization of y (groups of 128
  *   consecutive channels of a row, gsyq section 二), dequantize, divide by s, and write
  *   delta[j, o, c] = What[o, c] - W[o, c]   in dtype (bfloat16 rounds to nearest even).
- * The quantizer decisions are taken in float64, exactly as the definition reads.
+ * Every quantizer decision (step, zero point, code) equals the float64 definition's; delta is
+ * within 1.6e-5 * step / s of the float64 value before its rounding to dtype.
  *   w_parts    host array of n_parts device pointers; part p is [part_rows[p], d_in] of dtype.
  *   part_rows  host array of n_parts row counts (d_out = their sum).
  *   cand_scales device, float64 [n_cand, d_in].
@@ -190,7 +191,8 @@ AWQ_API int awq_search_scales(const void* x, int64_t ld_x, const void* const* w_
 
 /* Quantize y = W * s with the same quantizer and emit, per row o and group j:
  *   codes[o, c/2]  = q[o, c] | (q[o, c+1] << 4) for even c (uint8, [d_out, d_in/2]),
- *   qscales[o, j]  = step (float32, [d_out, d_in/128]),
+ *   qscales[o, j]  = step (float32, [d_out, d_in/128]; within 1e-6 relative of the float64
+ *                    step),
  *   zeros[o, j]    = zero point (int32, [d_out, d_in/128]; not clamped to [0,15],
  *                    saturated to the int32 range),
  * so that W*s ~= (q - zero) * step. s is usually best_scales from the search; the caller
@@ -199,6 +201,47 @@ AWQ_API int awq_search_scales(const void* x, int64_t ld_x, const void* const* w_
 AWQ_API int awq_quantize_pack(const void* const* w_parts, const int64_t* part_rows, int n_parts, int dtype,
                       int64_t d_in, int group_size, const double* s, uint8_t* codes,
                       float* qscales, int32_t* zeros, void* stream);
+
+/* ------------------------------------------------------------------ around the search */
+
+/* The statistic over several calibration batches (msModelSlim 预处理阶段: hooks gather the
+ * per-channel mean of |activation| while the batches run): sums[c] += sum_i |X[i,c]| over this
+ * batch's rows, float64 in a fixed order. The caller zeroes sums before the first batch and keeps
+ * the total token count for awq_act_stats_finalize.
+ *   x, dtype, n_tokens, d_in, ld_x, workspace: as awq_act_stats.
+ *   sums   device, float64 [d_in], read and written. */
+AWQ_API int awq_act_stats_accumulate(const void* x, int dtype, int64_t n_tokens, int64_t d_in, int64_t ld_x,
+                             double* sums, void* workspace, size_t workspace_bytes, void* stream);
+
+/* act_mean[c] = sums[c] / total_tokens (float64). total_tokens == 0 returns AWQ_ERR_NO_TOKENS.
+ * sums and act_mean may be the same buffer. */
+AWQ_API int awq_act_stats_finalize(const double* sums, int64_t d_in, int64_t total_tokens, double* act_mean,
+                           void* stream);
+
+/* Source-side fold of the inverse scales (msModelSlim 支持的子图类型: after the search the norm
+ * of norm-linear, linear1 of linear-linear, v_proj of ov and up_proj of up-down get the inverse
+ * scaling; gsyq section 四): for the rows r of the source operator that produce input channel r
+ * of the searched linears,
+ *   dst[r, j] = src[r, j] / s[r]   (quotient in float64, rounded to float32, then to dtype,
+ *                                   nearest even at each step)
+ * — a norm weight or a bias is one column, a source linear's weight is [d_in, cols].
+ *   src, dst  device, [rows, ld_src] / [rows, ld_dst] of dtype; dst may equal src (in place).
+ *   s         device, float64 [rows] (usually best_scales). */
+AWQ_API int awq_fold_scales(const void* src, int64_t ld_src, int dtype, int64_t rows, int64_t cols,
+                    const double* s, void* dst, int64_t ld_dst, void* stream);
+
+/* Deployment form of an export from awq_quantize_pack (bjdmk "GPU 硬件级反量化算子内联融合":
+ * FP16 per-group scales, 4-bit values two per byte), for [rows, n_groups] qscales / zeros:
+ *   steps_f16[o, j]  = qscales[o, j] rounded to float16 (nearest even), as uint16 bits;
+ *   zeros_u4[o, j/2] = zero points clipped to [0, 15], even j in the low nibble
+ *                      (uint8, [rows, ceil(n_groups / 2)]);
+ *   counts[0]       += zero points outside [0, 15] (only one-signed groups have them; the packed
+ *                      form cannot hold them, the int32 zero points stay exact),
+ *   counts[1]       += steps whose float16 value is not a normal number (zero, subnormal,
+ *                      infinite or NaN).
+ *   counts  device, int32 [2], accumulated (the caller zeroes it). */
+AWQ_API int awq_export_fp16(const float* qscales, const int32_t* zeros, int64_t rows, int64_t n_groups,
+                    uint16_t* steps_f16, uint8_t* zeros_u4, int32_t* counts, void* stream);
 
 #ifdef __cplusplus
 }

@@ -39,6 +39,10 @@ _SIGNATURES = {
     "awq_search_scales": (_c_int, [_vp, _c_i64, _vp, _vp, _c_int, _c_int, _c_i64, _c_i64, _vp, _c_int,
                                    _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
     "awq_quantize_pack": (_c_int, [_vp, _vp, _c_int, _c_int, _c_i64, _c_int, _vp, _vp, _vp, _vp, _vp]),
+    "awq_act_stats_accumulate": (_c_int, [_vp, _c_int, _c_i64, _c_i64, _c_i64, _vp, _vp, _c_size, _vp]),
+    "awq_act_stats_finalize": (_c_int, [_vp, _c_i64, _c_i64, _vp, _vp]),
+    "awq_fold_scales": (_c_int, [_vp, _c_i64, _c_int, _c_i64, _c_i64, _vp, _vp, _c_i64, _vp]),
+    "awq_export_fp16": (_c_int, [_vp, _vp, _c_i64, _c_i64, _vp, _vp, _vp, _vp]),
 }
 
 _lib = None
@@ -265,6 +269,64 @@ def awq_quantize_pack(w_parts, s: torch.Tensor, group_size: int = GROUP_SIZE, ou
     _check(lib.awq_quantize_pack(ptrs, rows, len(parts), _dtype_code(parts[0]), d_in, group_size,
                                  _dev(s, "s"), codes.data_ptr(), qs.data_ptr(), zs.data_ptr(), _stream(stream)))
     return {"codes": codes, "qscales": qs, "zeros": zs}
+
+
+def awq_act_stats_accumulate(x: torch.Tensor, sums: torch.Tensor, workspace=None, stream=None):
+    """sums (float64 [d_in], device) += per-channel sum of |x| over this batch's tokens."""
+    lib = load_library()
+    px, n, d, ld = _x_args(x)
+    dt = _dtype_code(x)
+    ws = _workspace(lib.awq_act_stats_workspace_bytes(dt, n, d), x.device, workspace)
+    _check(lib.awq_act_stats_accumulate(px, dt, n, d, ld, _dev(sums, "sums"), ws.data_ptr(),
+                                        ws.numel() * ws.element_size(), _stream(stream)))
+    return sums
+
+
+def awq_act_stats_finalize(sums: torch.Tensor, total_tokens: int, act_mean=None, stream=None):
+    """act_mean = sums / total_tokens (float64 [d_in])."""
+    lib = load_library()
+    if act_mean is None:
+        act_mean = torch.empty_like(sums)
+    _check(lib.awq_act_stats_finalize(_dev(sums, "sums"), sums.shape[0], total_tokens, _dev(act_mean, "act_mean"),
+                                      _stream(stream)))
+    return act_mean
+
+
+def awq_fold_scales(src: torch.Tensor, s: torch.Tensor, dst=None, stream=None):
+    """Row r of src ([rows] or [rows, cols], bf16 or f32) divided by s[r] (float64 [rows])."""
+    lib = load_library()
+    src2 = src.unsqueeze(1) if src.dim() == 1 else src
+    if src2.dim() != 2 or src2.stride(1) != 1:
+        raise ValueError("src must be [rows] or a [rows, cols] matrix with unit stride along cols")
+    if dst is None:
+        dst = torch.empty_like(src)
+    dst2 = dst.unsqueeze(1) if dst.dim() == 1 else dst
+    if dst2.shape != src2.shape or dst2.stride(1) != 1 or dst2.dtype != src2.dtype:
+        raise ValueError("dst must match src")
+    rows, cols = src2.shape
+    _check(lib.awq_fold_scales(_dev(src2, "src"), src2.stride(0) if rows > 1 else cols, _dtype_code(src2), rows,
+                               cols, _dev(s, "s"), _dev(dst2, "dst"), dst2.stride(0) if rows > 1 else cols,
+                               _stream(stream)))
+    return dst
+
+
+def awq_export_fp16(qscales: torch.Tensor, zeros: torch.Tensor, out=None, stream=None) -> dict:
+    """Float16 steps (uint16 bits) and zero points packed two per byte, with the two counts."""
+    lib = load_library()
+    rows, g = qscales.shape
+    out = out or {}
+    steps = out.get("steps_f16")
+    if steps is None:
+        steps = torch.empty((rows, g), dtype=torch.int16, device=qscales.device)
+    zu4 = out.get("zeros_u4")
+    if zu4 is None:
+        zu4 = torch.empty((rows, (g + 1) // 2), dtype=torch.uint8, device=qscales.device)
+    counts = out.get("counts")
+    if counts is None:
+        counts = torch.zeros(2, dtype=torch.int32, device=qscales.device)
+    _check(lib.awq_export_fp16(_dev(qscales, "qscales"), _dev(zeros, "zeros"), rows, g, steps.data_ptr(),
+                               zu4.data_ptr(), counts.data_ptr(), _stream(stream)))
+    return {"steps_f16": steps, "zeros_u4": zu4, "counts": counts}
 
 
 def awq_layer(x: torch.Tensor, w_parts, n_grid: int = 20, group_size: int = GROUP_SIZE,

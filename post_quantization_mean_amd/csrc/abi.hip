@@ -295,4 +295,67 @@ int awq_quantize_pack(const void* const* w_parts, const int64_t* part_rows, int 
   return ok();
 }
 
+int awq_act_stats_accumulate(const void* x, int dtype, int64_t n_tokens, int64_t d_in, int64_t ld_x,
+                             double* sums, void* workspace, size_t workspace_bytes, void* stream) {
+  TRY(check_dtype(dtype));
+  TRY(check_group(AWQ_GROUP_SIZE, d_in));
+  TRY(check_x(x, dtype, n_tokens, d_in, ld_x));
+  if (!sums) return fail(AWQ_ERR_NULL, "sums is NULL");
+  const size_t need = awq_act_stats_workspace_bytes(dtype, n_tokens, d_in);
+  if (!workspace || workspace_bytes < need)
+    return fail(AWQ_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace ? workspace_bytes : 0, need);
+  if (!aligned(workspace, 256)) return fail(AWQ_ERR_UNSUPPORTED, "workspace is not 256-byte aligned");
+  const awq::ActStatsPlan p = awq::act_stats_plan(dtype, n_tokens, d_in);
+  hipError_t e = awq::launch_act_stats(x, dtype, n_tokens, d_in, ld_x, sums, static_cast<double*>(workspace), p,
+                                       (hipStream_t)stream, true);
+  if (e != hipSuccess) return hip_fail(e, "act_stats launch");
+  return ok();
+}
+
+int awq_act_stats_finalize(const double* sums, int64_t d_in, int64_t total_tokens, double* act_mean,
+                           void* stream) {
+  if (!sums || !act_mean) return fail(AWQ_ERR_NULL, "sums or act_mean is NULL");
+  if (d_in <= 0) return fail(AWQ_ERR_SHAPE, "d_in %lld must be > 0", (long long)d_in);
+  if (total_tokens < 0) return fail(AWQ_ERR_SHAPE, "total_tokens %lld < 0", (long long)total_tokens);
+  if (total_tokens == 0) return fail(AWQ_ERR_NO_TOKENS, "total_tokens is 0: no activation mean");
+  hipError_t e = awq::launch_act_mean_from_sums(sums, d_in, total_tokens, act_mean, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "act_stats_finalize launch");
+  return ok();
+}
+
+int awq_fold_scales(const void* src, int64_t ld_src, int dtype, int64_t rows, int64_t cols, const double* s,
+                    void* dst, int64_t ld_dst, void* stream) {
+  TRY(check_dtype(dtype));
+  if (!src || !s || !dst) return fail(AWQ_ERR_NULL, "src, s or dst is NULL");
+  if (rows <= 0 || cols <= 0) return fail(AWQ_ERR_SHAPE, "rows %lld and cols %lld must be > 0", (long long)rows,
+                                          (long long)cols);
+  if (ld_src < cols || ld_dst < cols)
+    return fail(AWQ_ERR_ARG, "ld_src %lld / ld_dst %lld < cols %lld", (long long)ld_src, (long long)ld_dst,
+                (long long)cols);
+  const size_t es = esize(dtype);
+  if (!aligned(src, es) || !aligned(dst, es)) return fail(AWQ_ERR_UNSUPPORTED, "src or dst is not element-aligned");
+  if (cols > ((int64_t)1 << 31) - 256) return fail(AWQ_ERR_UNSUPPORTED, "cols %lld too large", (long long)cols);
+  // 16-byte vectors when every row start is 16-byte aligned and the rows are whole vectors
+  const bool vec = cols % 8 == 0 && aligned(src, 16) && aligned(dst, 16) && (ld_src * (int64_t)es) % 16 == 0 &&
+                   (ld_dst * (int64_t)es) % 16 == 0;
+  hipError_t e = awq::launch_fold_scales(src, ld_src, dtype, rows, cols, s, dst, ld_dst, vec, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "fold_scales launch");
+  return ok();
+}
+
+int awq_export_fp16(const float* qscales, const int32_t* zeros, int64_t rows, int64_t n_groups, uint16_t* steps_f16,
+                    uint8_t* zeros_u4, int32_t* counts, void* stream) {
+  if (!qscales || !zeros || !steps_f16 || !zeros_u4 || !counts)
+    return fail(AWQ_ERR_NULL, "qscales, zeros, steps_f16, zeros_u4 or counts is NULL");
+  if (rows <= 0 || n_groups <= 0)
+    return fail(AWQ_ERR_SHAPE, "rows %lld and n_groups %lld must be > 0", (long long)rows, (long long)n_groups);
+  if (rows * ((n_groups + 1) / 2) > ((int64_t)1 << 40)) return fail(AWQ_ERR_UNSUPPORTED, "export too large");
+  if (!aligned(qscales, 4) || !aligned(zeros, 4) || !aligned(steps_f16, 2) || !aligned(counts, 4))
+    return fail(AWQ_ERR_UNSUPPORTED, "qscales, zeros, counts must be 4-byte and steps_f16 2-byte aligned");
+  hipError_t e = awq::launch_export_fp16(qscales, zeros, rows, n_groups, steps_f16, zeros_u4, counts,
+                                         (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "export_fp16 launch");
+  return ok();
+}
+
 }  // extern "C"

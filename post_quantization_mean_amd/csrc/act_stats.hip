@@ -90,9 +90,11 @@ __global__ __launch_bounds__(kThreads) void act_stats_partial_kernel(
 
 // One block per 64 channels: wave w adds the chunks w, w+4, w+8, ... of its lane's channel
 // (independent loads, eight in flight), then the four waves are added in order.
+// With `accumulate`, out[c] += sum (a running sum over calibration batches); otherwise
+// out[c] = sum / n_tokens.
 __global__ __launch_bounds__(kThreads) void act_stats_finalize_kernel(
     const double* __restrict__ partial, int64_t n_chunks, int64_t d_in, int64_t n_tokens,
-    double* __restrict__ act_mean) {
+    double* __restrict__ act_mean, int accumulate) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t c = (int64_t)blockIdx.x * 64 + lane;
@@ -111,8 +113,16 @@ __global__ __launch_bounds__(kThreads) void act_stats_finalize_kernel(
   __shared__ double red[kThreads / 64][64];
   red[wave][lane] = s;
   __syncthreads();
-  if (wave == 0 && c < d_in)
-    act_mean[c] = (((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane]) / (double)n_tokens;
+  if (wave == 0 && c < d_in) {
+    const double t = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+    act_mean[c] = accumulate ? act_mean[c] + t : t / (double)n_tokens;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void act_mean_from_sums_kernel(const double* sums, int64_t d_in,
+                                                                       int64_t total_tokens, double* act_mean) {
+  const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (c < d_in) act_mean[c] = sums[c] / (double)total_tokens;
 }
 
 template <typename T, int LC>
@@ -150,7 +160,7 @@ ActStatsPlan act_stats_plan(int dtype, int64_t n_tokens, int64_t d_in) {
 
 hipError_t launch_act_stats(const void* x, int dtype, int64_t n_tokens, int64_t d_in, int64_t ld_x,
                             double* act_mean, double* partial, const ActStatsPlan& p,
-                            hipStream_t st) {
+                            hipStream_t st, bool accumulate) {
   hipError_t e;
   if (dtype == 1) {
     e = p.lanes_per_row == 64 ? launch_partial<uint16_t, 64>(x, ld_x, n_tokens, d_in, partial, p, st)
@@ -163,7 +173,14 @@ hipError_t launch_act_stats(const void* x, int dtype, int64_t n_tokens, int64_t 
   }
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(act_stats_finalize_kernel, dim3((unsigned)((d_in + 63) / 64)),
-                     dim3(kThreads), 0, st, partial, p.row_chunks, d_in, n_tokens, act_mean);
+                     dim3(kThreads), 0, st, partial, p.row_chunks, d_in, n_tokens, act_mean, accumulate ? 1 : 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_act_mean_from_sums(const double* sums, int64_t d_in, int64_t total_tokens, double* act_mean,
+                                     hipStream_t st) {
+  hipLaunchKernelGGL(act_mean_from_sums_kernel, dim3((unsigned)((d_in + kThreads - 1) / kThreads)), dim3(kThreads),
+                     0, st, sums, d_in, total_tokens, act_mean);
   return hipGetLastError();
 }
 

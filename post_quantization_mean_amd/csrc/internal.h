@@ -27,9 +27,12 @@ struct ActStatsPlan {
   int64_t rows_per_chunk;
 };
 ActStatsPlan act_stats_plan(int dtype, int64_t n_tokens, int64_t d_in);
+// accumulate: act_mean[c] += sum_i |x[i,c]| instead of act_mean[c] = mean_i |x[i,c]|
 hipError_t launch_act_stats(const void* x, int dtype, int64_t n_tokens, int64_t d_in, int64_t ld_x,
                             double* act_mean, double* partial, const ActStatsPlan& plan,
-                            hipStream_t stream);
+                            hipStream_t stream, bool accumulate = false);
+hipError_t launch_act_mean_from_sums(const double* sums, int64_t d_in, int64_t total_tokens, double* act_mean,
+                                     hipStream_t stream);
 
 // ---- a2 / a5
 hipError_t launch_candidate_scales(const double* act_mean, int64_t d_in, int n_grid,
@@ -52,5 +55,11 @@ constexpr int kTileN = 256;  // weight rows per error-GEMM tile
 hipError_t launch_error_sse(const void* x, int64_t ld_x, const void* delta, int dtype,
                             int64_t n_tokens, int64_t d_in, int64_t d_out, int n_cand,
                             double* tile_sse, hipStream_t stream);
+
+// ---- around the search: source fold and deployment form
+hipError_t launch_fold_scales(const void* src, int64_t ld_src, int dtype, int64_t rows, int64_t cols,
+                              const double* s, void* dst, int64_t ld_dst, bool vec, hipStream_t stream);
+hipError_t launch_export_fp16(const float* qscales, const int32_t* zeros, int64_t rows, int64_t n_groups,
+                              uint16_t* steps_f16, uint8_t* zeros_u4, int32_t* counts, hipStream_t stream);
 
 }  // namespace awq

@@ -30,11 +30,11 @@ def _declared():
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
     names = _declared()
-    assert len(names) == 13
+    assert len(names) == 17
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(b.exported_symbols()) == names
-    assert lib.awq_abi_version() == 1
+    assert lib.awq_abi_version() == 2
 
 
 def test_status_strings(lib):
@@ -133,3 +133,32 @@ def test_search_workspace_and_validation(lib):
     assert call(bi=None) == 1
     assert call(g=32) == 5
     assert call(ws=FAKE_ODD) == 5
+
+
+def test_accumulate_finalize_validation(lib):
+    ws = lib.awq_act_stats_workspace_bytes(1, 1000, 256)
+    assert lib.awq_act_stats_accumulate(FAKE, 1, 1000, 256, 256, None, FAKE, ws, None) == 1
+    assert lib.awq_act_stats_accumulate(FAKE, 1, 0, 256, 256, FAKE, FAKE, ws, None) == 3
+    assert lib.awq_act_stats_accumulate(FAKE, 1, 1000, 256, 256, FAKE, FAKE, ws - 8, None) == 6
+    assert lib.awq_act_stats_accumulate(FAKE, 9, 1000, 256, 256, FAKE, FAKE, ws, None) == 5
+    assert lib.awq_act_stats_finalize(None, 256, 10, FAKE, None) == 1
+    assert lib.awq_act_stats_finalize(FAKE, 0, 10, FAKE, None) == 2
+    assert lib.awq_act_stats_finalize(FAKE, 256, 0, FAKE, None) == 3
+    assert "no activation mean" in _err(lib)
+    assert lib.awq_act_stats_finalize(FAKE, 256, -1, FAKE, None) == 2
+
+
+def test_fold_and_export_validation(lib):
+    assert lib.awq_fold_scales(None, 64, 1, 16, 64, FAKE, FAKE, 64, None) == 1
+    assert lib.awq_fold_scales(FAKE, 64, 1, 0, 64, FAKE, FAKE, 64, None) == 2
+    assert lib.awq_fold_scales(FAKE, 64, 1, 16, 0, FAKE, FAKE, 64, None) == 2
+    assert lib.awq_fold_scales(FAKE, 32, 1, 16, 64, FAKE, FAKE, 64, None) == 4
+    assert lib.awq_fold_scales(FAKE, 64, 1, 16, 64, FAKE, FAKE, 63, None) == 4
+    assert lib.awq_fold_scales(FAKE, 64, 4, 16, 64, FAKE, FAKE, 64, None) == 5
+    assert lib.awq_fold_scales(FAKE + 1, 64, 1, 16, 64, FAKE, FAKE, 64, None) == 5
+    assert lib.awq_fold_scales(FAKE + 2, 64, 0, 16, 64, FAKE, FAKE, 64, None) == 5  # f32 needs 4-byte alignment
+    assert lib.awq_export_fp16(None, FAKE, 4, 2, FAKE, FAKE, FAKE, None) == 1
+    assert lib.awq_export_fp16(FAKE, FAKE, 4, 2, FAKE, FAKE, None, None) == 1
+    assert lib.awq_export_fp16(FAKE, FAKE, 0, 2, FAKE, FAKE, FAKE, None) == 2
+    assert lib.awq_export_fp16(FAKE, FAKE, 4, -1, FAKE, FAKE, FAKE, None) == 2
+    assert lib.awq_export_fp16(FAKE + 2, FAKE, 4, 2, FAKE, FAKE, FAKE, None) == 5

@@ -1,0 +1,109 @@
+"""GPU parity of the steps either side of the search, through the C ABI: the statistic over
+several calibration batches, the source-side fold of the inverse scales, and the float16 /
+packed-zero deployment form. Every result is compared with the oracle element by element:
+bit-exact where the output is an integer or a rounded value, float64 sums within 1e-11."""
+import numpy as np
+import pytest
+
+from oracle import awq_export as X
+from oracle import awq_oracle as O
+from oracle import parity as P
+from workloads import custom_workload, f32_to_bf16_bits, make_w, make_x, to_f32, to_torch, workload
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def B():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from post_quantization_mean_amd import binding
+    binding.load_library()
+    return binding
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_statistic_over_batches(B, dtype):
+    wl = custom_workload(1000, 384, 128, dtype, outlier_channels=4, config_id=201)
+    x = make_x(wl)
+    cuts = [0, 1, 257, 700, 1000]  # batches of 1, 256, 443 and 300 tokens
+    sums = torch.zeros(384, dtype=torch.float64, device="cuda")
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        B.awq_act_stats_accumulate(to_torch(x[a:b], "cuda"), sums)
+    got = B.awq_act_stats_finalize(sums, 1000).cpu().numpy()
+    want = X.act_mean_batches([to_f32(x[a:b]).astype(np.float64) for a, b in zip(cuts[:-1], cuts[1:])])
+    print(f"[gpu export] statistic over 4 batches ({dtype}): max rel {P.max_rel(got, want):.2e}", flush=True)
+    assert P.max_rel(got, want) < 1e-11
+    # finalize in place (sums and act_mean the same buffer)
+    B.awq_act_stats_finalize(sums, 1000, act_mean=sums)
+    assert P.max_rel(sums.cpu().numpy(), want) < 1e-11
+
+
+def _fold_case(B, src_np, s_np, dtype, inplace=False):
+    src_t = to_torch(src_np, "cuda")
+    s_t = torch.from_numpy(s_np).cuda()
+    got_t = B.awq_fold_scales(src_t, s_t, dst=src_t if inplace else None)
+    torch.cuda.synchronize()
+    got = got_t.cpu()
+    got = got.view(torch.int16).numpy().view(np.uint16) if dtype == "bf16" else got.numpy()
+    want = X.fold_scales(to_f32(src_np).astype(np.float64), s_np, dtype)
+    if src_np.ndim == 1:
+        want = want[:, 0]
+    if dtype == "bf16":
+        assert np.array_equal(got, want), int((got != want).sum())
+    else:
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), int((got != want).sum())
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_fold_shapes(B, dtype):
+    rng = np.random.default_rng(11)
+    d_in = 384
+    # scales with the spread of a search: 1e-3 .. 1e3, full float64 mantissas
+    s = np.exp(rng.uniform(-7, 7, d_in))
+    wl = custom_workload(64, d_in, d_in, dtype, config_id=202)
+    base = make_w(wl)  # [d_in, d_in] of dtype storage
+    gamma = base[:, 0].copy()  # a norm weight: one column
+    print(f"[gpu export] fold ({dtype}): norm weight, source linear, ragged columns, in place", flush=True)
+    _fold_case(B, gamma, s, dtype)
+    _fold_case(B, base, s, dtype)                       # [d_in, 384]: 16-byte vectors
+    _fold_case(B, np.ascontiguousarray(base[:, :100]), s, dtype)  # 100 columns: element path
+    _fold_case(B, base.copy(), s, dtype, inplace=True)
+
+
+def test_fold_full_size_up_proj(B):
+    # the source of the 7B down_proj search is up_proj: [11008, 4096] bf16, one scale per row
+    wl = workload(3)
+    src = make_w(custom_workload(16, 4096, 11008, "bf16", config_id=203))
+    act = np.abs(to_f32(make_x(wl, row_range=(0, 2048))).astype(np.float64)).mean(axis=0)
+    s = O.candidate_scales(act, 0.35)
+    print("[gpu export] fold at full size: up_proj [11008, 4096] bf16", flush=True)
+    _fold_case(B, src, s, "bf16")
+
+
+def test_export_fp16(B):
+    wl = custom_workload(64, 512, 300, "bf16", config_id=204)
+    w = make_w(wl).copy()
+    w[5, :128] = f32_to_bf16_bits(np.abs(to_f32(w[5, :128])) + np.float32(0.05))  # one-signed: zero < 0
+    w[9, 128:256] = f32_to_bf16_bits(to_f32(w[9, 128:256]) * np.float32(1e-3))     # tiny steps: subnormal f16
+    w[11, :] = 0                                                                      # floor step 1e-8 -> 0
+    wp = [to_torch(w, "cuda")]
+    s = torch.ones(512, dtype=torch.float64, device="cuda")
+    pk = B.awq_quantize_pack(wp, s)
+    ex = B.awq_export_fp16(pk["qscales"], pk["zeros"])
+    torch.cuda.synchronize()
+    qs, zs = pk["qscales"].cpu().numpy(), pk["zeros"].cpu().numpy()
+    hb, packed, bad_z, bad_s = X.export_fp16(qs, zs)
+    got_h = ex["steps_f16"].cpu().numpy().view(np.uint16)
+    assert np.array_equal(got_h, hb)
+    assert np.array_equal(ex["zeros_u4"].cpu().numpy(), packed)
+    counts = ex["counts"].cpu().numpy()
+    print(f"[gpu export] fp16 export: counts gpu {list(counts)} oracle {[bad_z, bad_s]}", flush=True)
+    assert list(counts) == [bad_z, bad_s] and bad_z >= 1 and bad_s >= 2
+    # an odd number of groups per row
+    ex3 = B.awq_export_fp16(pk["qscales"][:, :3].contiguous(), pk["zeros"][:, :3].contiguous())
+    hb3, packed3, bz3, bs3 = X.export_fp16(qs[:, :3], zs[:, :3])
+    assert np.array_equal(ex3["steps_f16"].cpu().numpy().view(np.uint16), hb3)
+    assert np.array_equal(ex3["zeros_u4"].cpu().numpy(), packed3)
+    assert list(ex3["counts"].cpu().numpy()) == [bz3, bs3]
