@@ -253,10 +253,27 @@ def main() -> int:
         "quant_delta": isolated(lambda: B.awq_quant_delta(w_parts, cand[:cpp], wl.group_size, delta[:cpp])),
         "quantize_pack": isolated(lambda: B.awq_quantize_pack(w_parts, best, wl.group_size, pack_out)),
     }
+    # Around the search: the fold of best_scales into the source operator of this layer (the
+    # norm weight for a fused norm-linear set, the up_proj rows for a down_proj search), and the
+    # float16 / packed-zero export of the pack's output
+    src_rows = wl.d_in
+    src_cols = 1 if wl.parts else (4096 if wl.d_in == 11008 else 8192 if wl.d_in == 28672 else wl.d_in)
+    src_kind = "norm weight" if src_cols == 1 else f"up_proj [{src_rows}, {src_cols}]"
+    gen = torch.Generator(device=dev).manual_seed(wl.config_id)
+    fold_src = (torch.randn((src_rows, src_cols), generator=gen, device=dev, dtype=torch.float32) * 0.02).to(x.dtype)
+    fold_dst = torch.empty_like(fold_src)
+    iso_ms["fold_scales"] = isolated(lambda: B.awq_fold_scales(fold_src, best, dst=fold_dst))
+    exp_out = {"counts": torch.zeros(2, dtype=torch.int32, device=dev)}
+    exp_out.update(B.awq_export_fp16(pack_out["qscales"], pack_out["zeros"], out=exp_out))
+    iso_ms["export_fp16"] = isolated(lambda: B.awq_export_fp16(pack_out["qscales"], pack_out["zeros"], out=exp_out))
     del flush
+    f_bytes = 2 * src_rows * src_cols * esz + src_rows * 8
+    e_bytes = wl.d_out * G * (4 + 4 + 2) + wl.d_out * ((G + 1) // 2)
     iso_gbps = {"act_stats+finalize": a_bytes / (iso_ms["act_stats+finalize"] * 1e-3) / 1e9,
                 "quant_delta": q_bytes / (iso_ms["quant_delta"] * 1e-3) / 1e9,
-                "quantize_pack": p_bytes / (iso_ms["quantize_pack"] * 1e-3) / 1e9}
+                "quantize_pack": p_bytes / (iso_ms["quantize_pack"] * 1e-3) / 1e9,
+                "fold_scales": f_bytes / (iso_ms["fold_scales"] * 1e-3) / 1e9,
+                "export_fp16": e_bytes / (iso_ms["export_fp16"] * 1e-3) / 1e9}
 
     out = {
         "metric": METRIC,
@@ -282,7 +299,7 @@ def main() -> int:
                        "quantize_pack": pack_ms},
         "hbm_kernels": {"note": "each kernel alone, memory-side cache flushed before every repetition, median of 5; "
                                 "algorithmic bytes / time against 8000 GB/s",
-                        "ms": iso_ms, "gbps": iso_gbps,
+                        "fold_source": src_kind, "ms": iso_ms, "gbps": iso_gbps,
                         "frac_of_peak": {k: v / PEAK_HBM_GBPS for k, v in iso_gbps.items()}},
         "best_k": info_h[0],
     }
