@@ -58,9 +58,10 @@ extern "C" {
 #define AWQ_API
 #endif
 
-#define AWQ_ABI_VERSION 2
+#define AWQ_ABI_VERSION 3
 #define AWQ_MAX_PARTS 8
 #define AWQ_GROUP_SIZE 128
+#define AWQ_MAX_RATIOS 64
 
 typedef enum {
   AWQ_OK = 0,
@@ -78,8 +79,26 @@ typedef enum {
 
 typedef enum { AWQ_DTYPE_F32 = 0, AWQ_DTYPE_BF16 = 1 } awq_dtype;
 
+/* Candidate-scale formulas (awq_candidate_scales_ex), a = act_mean, r = a ratio of the list. */
+typedef enum {
+  AWQ_FORMULA_MSMODELSLIM = 0, /* max(a^r, 1e-4) / sqrt(max * min)            (msModelSlim 算法公式) */
+  AWQ_FORMULA_RMS = 1,         /* v = max(a, 1e-5)^r; max(v / sqrt(mean(v^2)), 1e-4)   (gsyq 二) */
+  AWQ_FORMULA_DUO = 2          /* v = max(a^r / (wm^(1-r) + 1e-6), 1e-4); v / sqrt(max * min),
+                                  wm = mean over output rows of |W|  (bjdmk AWQChannelScaler) */
+} awq_formula;
+
+/* Weight quantizers of the delta step (awq_quant_delta_ex). */
+typedef enum {
+  AWQ_QUANT_INT4_GROUP = 0,   /* asymmetric INT4, groups of 128 (the main quantizer, gsyq 二) */
+  AWQ_QUANT_INT4_ROW = 1,     /* per row: step = (max - min)/15, restored round(y/(step+1e-6))*step,
+                                 no zero point, no clamp (bjdmk AWQChannelScaler) */
+  AWQ_QUANT_INT8_ROW_SYM = 2  /* per row: step = max(max|y|/127, 1e-8),
+                                 restored clip(round(y/step), -127, 127)*step
+                                 (msModelSlim weight_qconfig: per-channel int8 symmetric min-max) */
+} awq_quantizer;
+
 /* Flag bits of best_info[1] (written on the device by awq_loss_argmin / awq_search_scales). */
-#define AWQ_INFO_ALL_NONFINITE 1 /* no loss was below +inf: k* = 0, whose scales are all 1 */
+#define AWQ_INFO_ALL_NONFINITE 1 /* no loss was below +inf: k* = 0 and best_scales are all 1 */
 
 /* ------------------------------------------------------------------ library */
 
@@ -159,7 +178,8 @@ AWQ_API int awq_error_sse(const void* x, int64_t ld_x, const void* delta, int dt
  *   tile_sse    device, float64 [n_grid, tiles_per_cand].
  *   cand_scales device, float64 [n_grid, d_in].
  *   losses      device, float64 [n_grid], written.
- *   best_scales device, float64 [d_in], written with cand_scales[k*, :].
+ *   best_scales device, float64 [d_in], written with cand_scales[k*, :], or with ones when no
+ *               loss is below +inf (the search's starting scales).
  *   best_info   device, int32 [2], written: {k*, flags (AWQ_INFO_*)}. */
 AWQ_API int awq_loss_argmin(const double* tile_sse, int64_t tiles_per_cand, int n_grid, int64_t n_tokens,
                     int64_t d_out, const double* cand_scales, int64_t d_in, double* losses,
@@ -242,6 +262,53 @@ AWQ_API int awq_fold_scales(const void* src, int64_t ld_src, int dtype, int64_t 
  *   counts  device, int32 [2], accumulated (the caller zeroes it). */
 AWQ_API int awq_export_fp16(const float* qscales, const int32_t* zeros, int64_t rows, int64_t n_groups,
                     uint16_t* steps_f16, uint8_t* zeros_u4, int32_t* counts, void* stream);
+
+/* ------------------------------------------------------------------ grid and quantizer variants */
+
+/* wm[c] = (1/d_out) * sum_o |W[o, c]| over the stacked rows of the parts, float64 in a fixed order
+ * (bjdmk AWQChannelScaler, weight_mean = mean of |weight| over the output dimension): the
+ * second statistic of AWQ_FORMULA_DUO.
+ *   w_parts, part_rows, n_parts, dtype, d_in: as awq_quant_delta.
+ *   w_mean    device, float64 [d_in], written.
+ *   workspace device, >= awq_act_stats_workspace_bytes(dtype, max_p part_rows[p], d_in) bytes. */
+AWQ_API int awq_weight_mean(const void* const* w_parts, const int64_t* part_rows, int n_parts, int dtype,
+                    int64_t d_in, double* w_mean, void* workspace, size_t workspace_bytes, void* stream);
+
+/* cand_scales[k, :] = the formula's scales at ratio ratios[k], k = 0 .. n_ratios-1 (float64).
+ *   act_mean  device, float64 [d_in].
+ *   w_mean    device, float64 [d_in] (from awq_weight_mean); read only by AWQ_FORMULA_DUO, may be
+ *             NULL otherwise.
+ *   ratios    HOST, float64 [n_ratios], each in [0, 1]; 1 <= n_ratios <= AWQ_MAX_RATIOS. The
+ *             pages' grids: k/n for k < n (msModelSlim), k/(n-1) for k < n (bjdmk linspace),
+ *             0.0, 0.1, ..., 1.0 (gsyq).
+ *   cand_scales device, float64 [n_ratios, d_in], written.
+ * NaN in a statistic makes the rows that depend on it NaN, as the formulas imply. */
+AWQ_API int awq_candidate_scales_ex(const double* act_mean, const double* w_mean, int64_t d_in,
+                            const double* ratios, int n_ratios, int formula, double* cand_scales,
+                            void* stream);
+
+/* awq_quant_delta with a choice of quantizer (awq_quantizer). AWQ_QUANT_INT4_GROUP is exactly
+ * awq_quant_delta. The per-row quantizers take every rounding decision as the float64
+ * definition does and write delta = restored / s - W rounded from float64 to float32 (then to
+ * bfloat16 for AWQ_DTYPE_BF16), nearest even. Weights must be finite. d_in a multiple of 128. */
+AWQ_API int awq_quant_delta_ex(const void* const* w_parts, const int64_t* part_rows, int n_parts, int dtype,
+                       int64_t d_in, int quantizer, const double* cand_scales, int n_cand, void* delta,
+                       void* stream);
+
+/* awq_search_scales over an explicit ratio list with a scale formula and a quantizer:
+ * awq_candidate_scales_ex, then awq_quant_delta_ex + the error GEMM per pass of cand_per_pass
+ * candidates, then awq_loss_argmin (k* indexes the list).
+ *   w_mean     device, float64 [d_in]; read only by AWQ_FORMULA_DUO, may be NULL otherwise.
+ *   ratios, n_ratios, formula: as awq_candidate_scales_ex.  quantizer: as awq_quant_delta_ex.
+ *   workspace  device, >= awq_search_workspace_bytes(dtype, n_tokens, d_in, d_out, 128, n_ratios,
+ *              cand_per_pass) bytes.
+ *   the other arguments as awq_search_scales. */
+AWQ_API int awq_search_scales_ex(const void* x, int64_t ld_x, const void* const* w_parts,
+                         const int64_t* part_rows, int n_parts, int dtype, int64_t n_tokens,
+                         int64_t d_in, const double* act_mean, const double* w_mean,
+                         const double* ratios, int n_ratios, int formula, int quantizer,
+                         int cand_per_pass, double* cand_scales, double* losses, double* best_scales,
+                         int32_t* best_info, void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -19,7 +19,14 @@ AWQ_DTYPE_F32 = 0
 AWQ_DTYPE_BF16 = 1
 AWQ_INFO_ALL_NONFINITE = 1
 AWQ_MAX_PARTS = 8
+AWQ_MAX_RATIOS = 64
 GROUP_SIZE = 128
+AWQ_FORMULA_MSMODELSLIM = 0
+AWQ_FORMULA_RMS = 1
+AWQ_FORMULA_DUO = 2
+AWQ_QUANT_INT4_GROUP = 0
+AWQ_QUANT_INT4_ROW = 1
+AWQ_QUANT_INT8_ROW_SYM = 2
 
 _c_int, _c_i64, _c_size, _vp = ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
 
@@ -43,6 +50,11 @@ _SIGNATURES = {
     "awq_act_stats_finalize": (_c_int, [_vp, _c_i64, _c_i64, _vp, _vp]),
     "awq_fold_scales": (_c_int, [_vp, _c_i64, _c_int, _c_i64, _c_i64, _vp, _vp, _c_i64, _vp]),
     "awq_export_fp16": (_c_int, [_vp, _vp, _c_i64, _c_i64, _vp, _vp, _vp, _vp]),
+    "awq_weight_mean": (_c_int, [_vp, _vp, _c_int, _c_int, _c_i64, _vp, _vp, _c_size, _vp]),
+    "awq_candidate_scales_ex": (_c_int, [_vp, _vp, _c_i64, _vp, _c_int, _c_int, _vp, _vp]),
+    "awq_quant_delta_ex": (_c_int, [_vp, _vp, _c_int, _c_int, _c_i64, _c_int, _vp, _c_int, _vp, _vp]),
+    "awq_search_scales_ex": (_c_int, [_vp, _c_i64, _vp, _vp, _c_int, _c_int, _c_i64, _c_i64, _vp, _vp, _vp,
+                                      _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
 }
 
 _lib = None
@@ -327,6 +339,93 @@ def awq_export_fp16(qscales: torch.Tensor, zeros: torch.Tensor, out=None, stream
     _check(lib.awq_export_fp16(_dev(qscales, "qscales"), _dev(zeros, "zeros"), rows, g, steps.data_ptr(),
                                zu4.data_ptr(), counts.data_ptr(), _stream(stream)))
     return {"steps_f16": steps, "zeros_u4": zu4, "counts": counts}
+
+
+def _ratios(ratios):
+    r = [float(v) for v in ratios]
+    return (ctypes.c_double * max(len(r), 1))(*r), len(r)
+
+
+def _opt_dev(t, name: str) -> int:
+    return 0 if t is None else _dev(t, name)
+
+
+def awq_weight_mean(w_parts, w_mean=None, workspace=None, stream=None):
+    """float64 [d_in] mean of |W| over the stacked output rows of the parts."""
+    lib = load_library()
+    parts, ptrs, rows, d_out = _parts(w_parts)
+    d_in = parts[0].shape[1]
+    dt = _dtype_code(parts[0])
+    dev = parts[0].device
+    if w_mean is None:
+        w_mean = torch.empty(d_in, dtype=torch.float64, device=dev)
+    need = max(lib.awq_act_stats_workspace_bytes(dt, r, d_in) for r in rows)
+    ws = _workspace(need, dev, workspace)
+    _check(lib.awq_weight_mean(ptrs, rows, len(parts), dt, d_in, _dev(w_mean, "w_mean"), ws.data_ptr(),
+                               ws.numel() * ws.element_size(), _stream(stream)))
+    return w_mean
+
+
+def awq_candidate_scales_ex(act_mean: torch.Tensor, ratios, formula: int = AWQ_FORMULA_MSMODELSLIM,
+                            w_mean=None, cand_scales=None, stream=None):
+    """float64 [len(ratios), d_in] candidate scales of a formula over an explicit ratio list."""
+    lib = load_library()
+    d = act_mean.shape[0]
+    rv, n = _ratios(ratios)
+    if cand_scales is None:
+        cand_scales = torch.empty((max(n, 1), d), dtype=torch.float64, device=act_mean.device)
+    _check(lib.awq_candidate_scales_ex(_dev(act_mean, "act_mean"), _opt_dev(w_mean, "w_mean"), d, rv, n, formula,
+                                       _dev(cand_scales, "cand_scales"), _stream(stream)))
+    return cand_scales
+
+
+def awq_quant_delta_ex(w_parts, cand_scales: torch.Tensor, quantizer: int = AWQ_QUANT_INT4_GROUP, delta=None,
+                       stream=None):
+    """[n_cand, d_out, d_in] delta = What - W under the chosen quantizer, in the weights' dtype."""
+    lib = load_library()
+    parts, ptrs, rows, d_out = _parts(w_parts)
+    d_in = parts[0].shape[1]
+    n_cand = cand_scales.shape[0]
+    if delta is None:
+        delta = torch.empty((n_cand, d_out, d_in), dtype=parts[0].dtype, device=parts[0].device)
+    _check(lib.awq_quant_delta_ex(ptrs, rows, len(parts), _dtype_code(parts[0]), d_in, quantizer,
+                                  _dev(cand_scales, "cand_scales"), n_cand, _dev(delta, "delta"), _stream(stream)))
+    return delta
+
+
+def awq_search_scales_ex(x: torch.Tensor, w_parts, act_mean: torch.Tensor, ratios,
+                         formula: int = AWQ_FORMULA_MSMODELSLIM, quantizer: int = AWQ_QUANT_INT4_GROUP,
+                         w_mean=None, cand_per_pass: int | None = None, workspace=None, out=None,
+                         stream=None) -> dict:
+    """The search over an explicit ratio list with a scale formula and a quantizer."""
+    lib = load_library()
+    px, n, d, ld = _x_args(x)
+    parts, ptrs, rows, d_out = _parts(w_parts)
+    dt = _dtype_code(x)
+    rv, n_r = _ratios(ratios)
+    if cand_per_pass is None:
+        cand_per_pass = n_r
+    dev = x.device
+    out = out or {}
+    cand = out.get("cand_scales")
+    if cand is None:
+        cand = torch.empty((max(n_r, 1), d), dtype=torch.float64, device=dev)
+    losses = out.get("losses")
+    if losses is None:
+        losses = torch.empty(max(n_r, 1), dtype=torch.float64, device=dev)
+    best = out.get("best_scales")
+    if best is None:
+        best = torch.empty(d, dtype=torch.float64, device=dev)
+    info = out.get("best_info")
+    if info is None:
+        info = torch.empty(2, dtype=torch.int32, device=dev)
+    need = lib.awq_search_workspace_bytes(dt, n, d, d_out, GROUP_SIZE, n_r, cand_per_pass)
+    ws = _workspace(need, dev, workspace)
+    _check(lib.awq_search_scales_ex(px, ld, ptrs, rows, len(parts), dt, n, d, _dev(act_mean, "act_mean"),
+                                    _opt_dev(w_mean, "w_mean"), rv, n_r, formula, quantizer, cand_per_pass,
+                                    cand.data_ptr(), losses.data_ptr(), best.data_ptr(), info.data_ptr(),
+                                    ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream)))
+    return {"cand_scales": cand, "losses": losses, "best_scales": best, "best_info": info}
 
 
 def awq_layer(x: torch.Tensor, w_parts, n_grid: int = 20, group_size: int = GROUP_SIZE,

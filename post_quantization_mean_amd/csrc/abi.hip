@@ -111,6 +111,86 @@ int check_d_in_bytes(int dtype, int64_t d_in) {
     if (_s != AWQ_OK) return _s; \
   } while (0)
 
+int check_ratios(const double* ratios, int n_ratios, int formula, const double* w_mean, awq::RatioList* out) {
+  if (formula != AWQ_FORMULA_MSMODELSLIM && formula != AWQ_FORMULA_RMS && formula != AWQ_FORMULA_DUO)
+    return fail(AWQ_ERR_ARG, "formula %d is not an awq_formula", formula);
+  if (formula == AWQ_FORMULA_DUO && !w_mean) return fail(AWQ_ERR_NULL, "AWQ_FORMULA_DUO needs w_mean");
+  if (!ratios) return fail(AWQ_ERR_NULL, "ratios is NULL");
+  if (n_ratios < 1 || n_ratios > AWQ_MAX_RATIOS)
+    return fail(AWQ_ERR_ARG, "n_ratios %d outside [1, %d]", n_ratios, AWQ_MAX_RATIOS);
+  memset(out, 0, sizeof *out);
+  for (int k = 0; k < n_ratios; ++k) {
+    if (!(ratios[k] >= 0.0 && ratios[k] <= 1.0))
+      return fail(AWQ_ERR_ARG, "ratios[%d] = %g is outside [0, 1]", k, ratios[k]);
+    out->r[k] = ratios[k];
+  }
+  return AWQ_OK;
+}
+
+int check_quantizer(int quantizer) {
+  if (quantizer != AWQ_QUANT_INT4_GROUP && quantizer != AWQ_QUANT_INT4_ROW && quantizer != AWQ_QUANT_INT8_ROW_SYM)
+    return fail(AWQ_ERR_ARG, "quantizer %d is not an awq_quantizer", quantizer);
+  return AWQ_OK;
+}
+
+// The search composed from its steps. `ratios` == nullptr selects the msModelSlim grid
+// k / n_grid with the main quantizer; otherwise the variant formula and quantizer.
+int run_search(const void* x, int64_t ld_x, const void* const* w_parts, const int64_t* part_rows, int n_parts,
+               int dtype, int64_t n_tokens, int64_t d_in, const double* act_mean, const double* w_mean,
+               const double* ratios, int formula, int quantizer, int n_grid, int cand_per_pass,
+               double* cand_scales, double* losses, double* best_scales, int32_t* best_info, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  TRY(check_dtype(dtype));
+  TRY(check_group(AWQ_GROUP_SIZE, d_in));
+  TRY(check_d_in_bytes(dtype, d_in));
+  TRY(check_x(x, dtype, n_tokens, d_in, ld_x));
+  awq::WParts w;
+  TRY(make_parts(w_parts, part_rows, n_parts, dtype, d_in, &w));
+  const int64_t d_out = w.row_begin[w.n];
+  if (!act_mean || !cand_scales || !losses || !best_scales || !best_info)
+    return fail(AWQ_ERR_NULL, "a required pointer is NULL");
+  awq::RatioList rl;
+  if (ratios) {
+    TRY(check_ratios(ratios, n_grid, formula, w_mean, &rl));
+    TRY(check_quantizer(quantizer));
+  } else if (n_grid < 1 || n_grid > 65535) {
+    return fail(AWQ_ERR_ARG, "n_grid %d outside [1, 65535]", n_grid);
+  }
+  if (cand_per_pass < 1 || cand_per_pass > n_grid)
+    return fail(AWQ_ERR_ARG, "cand_per_pass %d outside [1, n_grid]", cand_per_pass);
+  const int64_t tiles = awq_error_tiles(n_tokens, d_out);
+  if (tiles * cand_per_pass > 0x7FFFFFFF)
+    return fail(AWQ_ERR_UNSUPPORTED, "too many tiles for one launch; lower cand_per_pass");
+  const size_t need =
+      awq_search_workspace_bytes(dtype, n_tokens, d_in, d_out, AWQ_GROUP_SIZE, n_grid, cand_per_pass);
+  if (!workspace || workspace_bytes < need)
+    return fail(AWQ_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace ? workspace_bytes : 0, need);
+  if (!aligned(workspace, 256)) return fail(AWQ_ERR_UNSUPPORTED, "workspace is not 256-byte aligned");
+
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = static_cast<char*>(workspace);
+  void* delta = ws;
+  double* tile_sse = reinterpret_cast<double*>(
+      ws + round_up((size_t)cand_per_pass * (size_t)d_out * (size_t)d_in * esize(dtype), 256));
+
+  hipError_t e = ratios ? awq::launch_candidate_scales_ex(act_mean, w_mean, d_in, rl, n_grid, formula, cand_scales, st)
+                        : awq::launch_candidate_scales(act_mean, d_in, n_grid, cand_scales, st);
+  if (e != hipSuccess) return hip_fail(e, "candidate_scales launch");
+  for (int k0 = 0; k0 < n_grid; k0 += cand_per_pass) {
+    const int nk = n_grid - k0 < cand_per_pass ? n_grid - k0 : cand_per_pass;
+    const double* cs = cand_scales + (int64_t)k0 * d_in;
+    e = quantizer == AWQ_QUANT_INT4_GROUP ? awq::launch_quant_delta(w, dtype, d_in, cs, nk, delta, st)
+                                          : awq::launch_quant_delta_row(w, dtype, d_in, quantizer, cs, nk, delta, st);
+    if (e != hipSuccess) return hip_fail(e, "quant_delta launch");
+    e = awq::launch_error_sse(x, ld_x, delta, dtype, n_tokens, d_in, d_out, nk, tile_sse + (int64_t)k0 * tiles, st);
+    if (e != hipSuccess) return hip_fail(e, "error_sse launch");
+  }
+  e = awq::launch_loss_argmin(tile_sse, tiles, n_grid, n_tokens, d_out, cand_scales, d_in, losses,
+                              best_scales, best_info, st);
+  if (e != hipSuccess) return hip_fail(e, "loss_argmin launch");
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -240,43 +320,9 @@ int awq_search_scales(const void* x, int64_t ld_x, const void* const* w_parts,
                       size_t workspace_bytes, void* stream) {
   TRY(check_dtype(dtype));
   TRY(check_group(group_size, d_in));
-  TRY(check_d_in_bytes(dtype, d_in));
-  TRY(check_x(x, dtype, n_tokens, d_in, ld_x));
-  awq::WParts w;
-  TRY(make_parts(w_parts, part_rows, n_parts, dtype, d_in, &w));
-  const int64_t d_out = w.row_begin[w.n];
-  if (!act_mean || !cand_scales || !losses || !best_scales || !best_info)
-    return fail(AWQ_ERR_NULL, "a required pointer is NULL");
-  if (n_grid < 1 || n_grid > 65535) return fail(AWQ_ERR_ARG, "n_grid %d outside [1, 65535]", n_grid);
-  if (cand_per_pass < 1 || cand_per_pass > n_grid)
-    return fail(AWQ_ERR_ARG, "cand_per_pass %d outside [1, n_grid]", cand_per_pass);
-  const int64_t tiles = awq_error_tiles(n_tokens, d_out);
-  if (tiles * cand_per_pass > 0x7FFFFFFF)
-    return fail(AWQ_ERR_UNSUPPORTED, "too many tiles for one launch; lower cand_per_pass");
-  const size_t need = awq_search_workspace_bytes(dtype, n_tokens, d_in, d_out, group_size, n_grid, cand_per_pass);
-  if (!workspace || workspace_bytes < need)
-    return fail(AWQ_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace ? workspace_bytes : 0, need);
-  if (!aligned(workspace, 256)) return fail(AWQ_ERR_UNSUPPORTED, "workspace is not 256-byte aligned");
-
-  hipStream_t st = (hipStream_t)stream;
-  char* ws = static_cast<char*>(workspace);
-  void* delta = ws;
-  double* tile_sse = reinterpret_cast<double*>(
-      ws + round_up((size_t)cand_per_pass * (size_t)d_out * (size_t)d_in * esize(dtype), 256));
-
-  hipError_t e = awq::launch_candidate_scales(act_mean, d_in, n_grid, cand_scales, st);
-  if (e != hipSuccess) return hip_fail(e, "candidate_scales launch");
-  for (int k0 = 0; k0 < n_grid; k0 += cand_per_pass) {
-    const int nk = n_grid - k0 < cand_per_pass ? n_grid - k0 : cand_per_pass;
-    e = awq::launch_quant_delta(w, dtype, d_in, cand_scales + (int64_t)k0 * d_in, nk, delta, st);
-    if (e != hipSuccess) return hip_fail(e, "quant_delta launch");
-    e = awq::launch_error_sse(x, ld_x, delta, dtype, n_tokens, d_in, d_out, nk, tile_sse + (int64_t)k0 * tiles, st);
-    if (e != hipSuccess) return hip_fail(e, "error_sse launch");
-  }
-  e = awq::launch_loss_argmin(tile_sse, tiles, n_grid, n_tokens, d_out, cand_scales, d_in, losses,
-                              best_scales, best_info, st);
-  if (e != hipSuccess) return hip_fail(e, "loss_argmin launch");
-  return ok();
+  return run_search(x, ld_x, w_parts, part_rows, n_parts, dtype, n_tokens, d_in, act_mean, nullptr, nullptr,
+                    AWQ_FORMULA_MSMODELSLIM, AWQ_QUANT_INT4_GROUP, n_grid, cand_per_pass, cand_scales, losses,
+                    best_scales, best_info, workspace, workspace_bytes, stream);
 }
 
 int awq_quantize_pack(const void* const* w_parts, const int64_t* part_rows, int n_parts, int dtype,
@@ -356,6 +402,82 @@ int awq_export_fp16(const float* qscales, const int32_t* zeros, int64_t rows, in
                                          (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "export_fp16 launch");
   return ok();
+}
+
+int awq_weight_mean(const void* const* w_parts, const int64_t* part_rows, int n_parts, int dtype, int64_t d_in,
+                    double* w_mean, void* workspace, size_t workspace_bytes, void* stream) {
+  TRY(check_dtype(dtype));
+  TRY(check_group(AWQ_GROUP_SIZE, d_in));
+  TRY(check_d_in_bytes(dtype, d_in));
+  awq::WParts w;
+  TRY(make_parts(w_parts, part_rows, n_parts, dtype, d_in, &w));
+  if (!w_mean) return fail(AWQ_ERR_NULL, "w_mean is NULL");
+  size_t need = 0;
+  for (int p = 0; p < n_parts; ++p) {
+    const size_t b = awq_act_stats_workspace_bytes(dtype, part_rows[p], d_in);
+    need = b > need ? b : need;
+  }
+  if (!workspace || workspace_bytes < need)
+    return fail(AWQ_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace ? workspace_bytes : 0, need);
+  if (!aligned(workspace, 256)) return fail(AWQ_ERR_UNSUPPORTED, "workspace is not 256-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  // column sums of |W| part by part (the statistic's kernels, W's rows in place of tokens), then
+  // one division by the stacked row count
+  hipError_t e = awq::launch_fill(w_mean, d_in, 0.0, st);
+  if (e != hipSuccess) return hip_fail(e, "weight_mean fill");
+  for (int p = 0; p < n_parts; ++p) {
+    const awq::ActStatsPlan plan = awq::act_stats_plan(dtype, part_rows[p], d_in);
+    e = awq::launch_act_stats(w_parts[p], dtype, part_rows[p], d_in, d_in, w_mean, static_cast<double*>(workspace),
+                              plan, st, true);
+    if (e != hipSuccess) return hip_fail(e, "weight_mean column sums");
+  }
+  e = awq::launch_act_mean_from_sums(w_mean, d_in, w.row_begin[w.n], w_mean, st);
+  if (e != hipSuccess) return hip_fail(e, "weight_mean division");
+  return ok();
+}
+
+int awq_candidate_scales_ex(const double* act_mean, const double* w_mean, int64_t d_in, const double* ratios,
+                            int n_ratios, int formula, double* cand_scales, void* stream) {
+  if (!act_mean || !cand_scales) return fail(AWQ_ERR_NULL, "act_mean or cand_scales is NULL");
+  if (d_in <= 0) return fail(AWQ_ERR_SHAPE, "d_in %lld must be > 0", (long long)d_in);
+  awq::RatioList rl;
+  TRY(check_ratios(ratios, n_ratios, formula, w_mean, &rl));
+  hipError_t e = awq::launch_candidate_scales_ex(act_mean, w_mean, d_in, rl, n_ratios, formula, cand_scales,
+                                                 (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "candidate_scales_ex launch");
+  return ok();
+}
+
+int awq_quant_delta_ex(const void* const* w_parts, const int64_t* part_rows, int n_parts, int dtype, int64_t d_in,
+                       int quantizer, const double* cand_scales, int n_cand, void* delta, void* stream) {
+  TRY(check_quantizer(quantizer));
+  if (quantizer == AWQ_QUANT_INT4_GROUP)
+    return awq_quant_delta(w_parts, part_rows, n_parts, dtype, d_in, AWQ_GROUP_SIZE, cand_scales, n_cand, delta,
+                           stream);
+  TRY(check_dtype(dtype));
+  TRY(check_group(AWQ_GROUP_SIZE, d_in));
+  TRY(check_d_in_bytes(dtype, d_in));
+  awq::WParts w;
+  TRY(make_parts(w_parts, part_rows, n_parts, dtype, d_in, &w));
+  if (!cand_scales || !delta) return fail(AWQ_ERR_NULL, "cand_scales or delta is NULL");
+  if (n_cand < 1) return fail(AWQ_ERR_ARG, "n_cand %d < 1", n_cand);
+  if (!aligned(delta, 16) || !aligned(cand_scales, 16))
+    return fail(AWQ_ERR_UNSUPPORTED, "delta and cand_scales must be 16-byte aligned");
+  hipError_t e = awq::launch_quant_delta_row(w, dtype, d_in, quantizer, cand_scales, n_cand, delta,
+                                             (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "quant_delta_ex launch");
+  return ok();
+}
+
+int awq_search_scales_ex(const void* x, int64_t ld_x, const void* const* w_parts, const int64_t* part_rows,
+                         int n_parts, int dtype, int64_t n_tokens, int64_t d_in, const double* act_mean,
+                         const double* w_mean, const double* ratios, int n_ratios, int formula, int quantizer,
+                         int cand_per_pass, double* cand_scales, double* losses, double* best_scales,
+                         int32_t* best_info, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!ratios) return fail(AWQ_ERR_NULL, "ratios is NULL");
+  return run_search(x, ld_x, w_parts, part_rows, n_parts, dtype, n_tokens, d_in, act_mean, w_mean, ratios, formula,
+                    quantizer, n_ratios, cand_per_pass, cand_scales, losses, best_scales, best_info, workspace,
+                    workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -4,7 +4,7 @@
 //   scales = act_mean.pow(ratio).clamp(min=1e-4);  scales = scales / sqrt(scales.max() * scales.min())
 // with ratio = k / n_grid, k = 0 .. n_grid-1 (the grid covers [0, 1) in steps of 1/n_grid).
 // a5 follows gsyq.cn "AWQ 离群激活平滑实操", section 二: start from best_loss = +inf with unit
-// scales and keep a ratio only when its loss is strictly smaller.
+// scales and keep a ratio only when its loss is strictly smaller (unit scales remain when none is).
 #include <math.h>
 
 #include "internal.h"
@@ -78,7 +78,7 @@ __global__ __launch_bounds__(kThreads) void argmin_kernel(const double* __restri
                                                           const double* __restrict__ cand_scales,
                                                           int64_t d_in, double* __restrict__ best,
                                                           int32_t* __restrict__ info) {
-  __shared__ int kbest;
+  __shared__ int kbest, knone;
   if (threadIdx.x == 0) {
     double best_loss = INFINITY;
     int kb = 0;
@@ -91,11 +91,15 @@ __global__ __launch_bounds__(kThreads) void argmin_kernel(const double* __restri
     }
     kbest = kb;
     info[0] = kb;
-    info[1] = (best_loss < INFINITY) ? 0 : 1;
+    knone = (best_loss < INFINITY) ? 0 : 1;
+    info[1] = knone;
   }
   __syncthreads();
+  // with no loss below +inf the scales stay at their starting value, ones (the k = 0 row of the
+  // msModelSlim grid is exactly that; other grids and formulas need not start there)
+  const bool none = knone != 0;
   const double* src = cand_scales + (int64_t)kbest * d_in;
-  for (int64_t c = threadIdx.x; c < d_in; c += kThreads) best[c] = src[c];
+  for (int64_t c = threadIdx.x; c < d_in; c += kThreads) best[c] = none ? 1.0 : src[c];
 }
 
 }  // namespace

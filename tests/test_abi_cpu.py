@@ -30,11 +30,11 @@ def _declared():
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
     names = _declared()
-    assert len(names) == 17
+    assert len(names) == 21
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(b.exported_symbols()) == names
-    assert lib.awq_abi_version() == 2
+    assert lib.awq_abi_version() == 3
 
 
 def test_status_strings(lib):
@@ -162,3 +162,63 @@ def test_fold_and_export_validation(lib):
     assert lib.awq_export_fp16(FAKE, FAKE, 0, 2, FAKE, FAKE, FAKE, None) == 2
     assert lib.awq_export_fp16(FAKE, FAKE, 4, -1, FAKE, FAKE, FAKE, None) == 2
     assert lib.awq_export_fp16(FAKE + 2, FAKE, 4, 2, FAKE, FAKE, FAKE, None) == 5
+
+
+def _vparts():
+    p = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    r = (ctypes.c_int64 * 2)(64, 64)
+    return p, r
+
+
+def test_variant_validation(lib):
+    rv = (ctypes.c_double * 3)(0.0, 0.5, 1.0)
+    bad = (ctypes.c_double * 2)(0.0, 1.5)
+    nan = (ctypes.c_double * 1)(float("nan"))
+    # candidate scales over an explicit ratio list
+    assert lib.awq_candidate_scales_ex(None, None, 256, rv, 3, 0, FAKE, None) == 1
+    assert lib.awq_candidate_scales_ex(FAKE, None, 0, rv, 3, 0, FAKE, None) == 2
+    assert lib.awq_candidate_scales_ex(FAKE, None, 256, rv, 3, 3, FAKE, None) == 4
+    assert "formula" in _err(lib)
+    assert lib.awq_candidate_scales_ex(FAKE, None, 256, rv, 3, 2, FAKE, None) == 1  # duo needs w_mean
+    assert "w_mean" in _err(lib)
+    assert lib.awq_candidate_scales_ex(FAKE, None, 256, None, 3, 0, FAKE, None) == 1
+    assert lib.awq_candidate_scales_ex(FAKE, None, 256, rv, 0, 0, FAKE, None) == 4
+    assert lib.awq_candidate_scales_ex(FAKE, None, 256, rv, 65, 0, FAKE, None) == 4
+    assert lib.awq_candidate_scales_ex(FAKE, None, 256, bad, 2, 0, FAKE, None) == 4
+    assert "outside [0, 1]" in _err(lib)
+    assert lib.awq_candidate_scales_ex(FAKE, None, 256, nan, 1, 1, FAKE, None) == 4
+    # quantizer choice
+    p, r = _vparts()
+    assert lib.awq_quant_delta_ex(p, r, 2, 1, 256, 7, FAKE, 3, FAKE, None) == 4
+    assert "quantizer" in _err(lib)
+    assert lib.awq_quant_delta_ex(p, r, 2, 1, 200, 1, FAKE, 3, FAKE, None) == 2
+    assert lib.awq_quant_delta_ex(p, r, 2, 1, 200, 0, FAKE, 3, FAKE, None) == 2  # group path checks too
+    assert lib.awq_quant_delta_ex(p, r, 2, 5, 256, 2, FAKE, 3, FAKE, None) == 5
+    assert lib.awq_quant_delta_ex(p, r, 2, 1, 256, 2, None, 3, FAKE, None) == 1
+    assert lib.awq_quant_delta_ex(p, r, 2, 1, 256, 2, FAKE, 0, FAKE, None) == 4
+    assert lib.awq_quant_delta_ex(p, r, 2, 1, 256, 1, FAKE_ODD, 3, FAKE, None) == 5
+    assert lib.awq_quant_delta_ex(p, r, 9, 1, 256, 1, FAKE, 3, FAKE, None) == 4
+    # weight mean
+    assert lib.awq_weight_mean(p, r, 2, 1, 256, None, FAKE, 1 << 20, None) == 1
+    assert lib.awq_weight_mean(p, r, 2, 1, 200, FAKE, FAKE, 1 << 20, None) == 2
+    assert lib.awq_weight_mean(p, r, 2, 1, 256, FAKE, FAKE, 8, None) == 6
+    assert lib.awq_weight_mean(p, r, 2, 1, 256, FAKE, None, 1 << 20, None) == 6
+    assert lib.awq_weight_mean(p, r, 2, 1, 256, FAKE, FAKE + 16, 1 << 20, None) == 5
+    # the composed search
+    ws = lib.awq_search_workspace_bytes(1, 600, 256, 128, 128, 3, 3)
+    args = [FAKE, 256, p, r, 2, 1, 600, 256, FAKE, None, rv, 3, 0, 0, 3, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None]
+    def call(**kw):
+        a = list(args)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return lib.awq_search_scales_ex(*a)
+    assert call(a10=None) == 1
+    assert call(a12=2) == 1       # duo without w_mean
+    assert call(a12=5) == 4
+    assert call(a13=3) == 4       # quantizer
+    assert call(a11=0) == 4       # no ratios
+    assert call(a14=4) == 4       # cand_per_pass > n_ratios
+    assert call(a6=0) == 3        # no tokens
+    assert call(a20=ws - 8) == 6
+    assert call(a18=None) == 1
+    assert call(a19=None) == 6
