@@ -58,7 +58,7 @@ def _source_digest(*paths) -> str:
     return h.hexdigest()[:16]
 
 
-GEMM_SOURCES = ("post_quantization_mean_amd/csrc/err_gemm.hip", "post_quantization_mean_amd/csrc/internal.h")
+GEMM_SOURCES = ("post_quantization_mean_amd/csrc/err_gemm.hip", "post_quantization_mean_amd/csrc/gemm.h")
 
 
 def measured_traffic(workload_name: str):
@@ -266,7 +266,44 @@ def main() -> int:
     exp_out = {"counts": torch.zeros(2, dtype=torch.int32, device=dev)}
     exp_out.update(B.awq_export_fp16(pack_out["qscales"], pack_out["zeros"], out=exp_out))
     iso_ms["export_fp16"] = isolated(lambda: B.awq_export_fp16(pack_out["qscales"], pack_out["zeros"], out=exp_out))
+    # Grid and quantizer variants at this workload: the per-row quantizers' delta step (same
+    # algorithmic bytes as the group quantizer's), the |W| column mean of the duo formula, and the
+    # whole search with each page's pairing of formula, grid and quantizer
+    wm = B.awq_weight_mean(w_parts)
+    var_ms = {
+        "weight_mean": isolated(lambda: B.awq_weight_mean(w_parts, wm)),
+        "quant_delta_int4_row": isolated(lambda: B.awq_quant_delta_ex(w_parts, cand[:cpp], B.AWQ_QUANT_INT4_ROW,
+                                                                      delta[:cpp])),
+        "quant_delta_int8_row_sym": isolated(lambda: B.awq_quant_delta_ex(w_parts, cand[:cpp],
+                                                                          B.AWQ_QUANT_INT8_ROW_SYM, delta[:cpp])),
+    }
     del flush
+    var_gbps = {"weight_mean": (wl.d_out * wl.d_in * esz + wl.d_in * 8) / (var_ms["weight_mean"] * 1e-3) / 1e9,
+                "quant_delta_int4_row": q_bytes / (var_ms["quant_delta_int4_row"] * 1e-3) / 1e9,
+                "quant_delta_int8_row_sym": q_bytes / (var_ms["quant_delta_int8_row_sym"] * 1e-3) / 1e9}
+    ws_s = torch.empty(B.awq_search_workspace_bytes(dt, wl.n_tokens, wl.d_in, wl.d_out, 128, 20,
+                                                    min(cpp, 20)), dtype=torch.uint8, device=dev)
+    pairings = {"duo/linspace20/int4_row": (B.AWQ_FORMULA_DUO, [k / 19 for k in range(20)], B.AWQ_QUANT_INT4_ROW),
+                "rms/tenths/int4_group": (B.AWQ_FORMULA_RMS, [k / 10 for k in range(11)], B.AWQ_QUANT_INT4_GROUP),
+                "msmodelslim/ms20/int8_row_sym": (B.AWQ_FORMULA_MSMODELSLIM, [k / 20 for k in range(20)],
+                                                  B.AWQ_QUANT_INT8_ROW_SYM)}
+    search_ms = {}
+    for name, (formula, ratios, quantizer) in pairings.items():
+        c = min(cpp, len(ratios))
+        fn = lambda: B.awq_search_scales_ex(x, w_parts, act, ratios, formula, quantizer, w_mean=wm,
+                                            cand_per_pass=c, workspace=ws_s)
+        fn()
+        ts = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        search_ms[name] = {"ms": float(np.median(ts)), "candidates": len(ratios),
+                           "candidates_per_s": len(ratios) / (float(np.median(ts)) * 1e-3)}
+    del ws_s
     f_bytes = 2 * src_rows * src_cols * esz + src_rows * 8
     e_bytes = wl.d_out * G * (4 + 4 + 2) + wl.d_out * ((G + 1) // 2)
     iso_gbps = {"act_stats+finalize": a_bytes / (iso_ms["act_stats+finalize"] * 1e-3) / 1e9,
@@ -301,6 +338,11 @@ def main() -> int:
                                 "algorithmic bytes / time against 8000 GB/s",
                         "fold_source": src_kind, "ms": iso_ms, "gbps": iso_gbps,
                         "frac_of_peak": {k: v / PEAK_HBM_GBPS for k, v in iso_gbps.items()}},
+        "variants": {"note": "per-row quantizers and |W| mean alone (cache flushed, median of 5, algorithmic bytes "
+                             "/ time); searches with each page's formula/grid/quantizer (median of 3)",
+                     "ms": var_ms, "gbps": var_gbps,
+                     "frac_of_peak": {k: v / PEAK_HBM_GBPS for k, v in var_gbps.items()},
+                     "search": search_ms},
         "best_k": info_h[0],
     }
     if not args.no_cpu_baseline:

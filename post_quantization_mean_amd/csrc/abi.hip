@@ -7,6 +7,7 @@
 
 #include "awq.h"
 #include "internal.h"
+#include "variants.h"
 
 namespace {
 

@@ -29,7 +29,7 @@
 #include <algorithm>
 #include <type_traits>
 
-#include "internal.h"
+#include "gemm.h"
 
 namespace awq {
 namespace {

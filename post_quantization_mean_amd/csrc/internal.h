@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "gemm.h"
+
 namespace awq {
 
 constexpr int kMaxParts = 8;
@@ -48,31 +50,6 @@ hipError_t launch_quant_delta(const WParts& w, int dtype, int64_t d_in, const do
 hipError_t launch_quantize_pack(const WParts& w, int dtype, int64_t d_in, const double* s,
                                 uint8_t* codes, float* qscales, int32_t* zeros,
                                 hipStream_t stream);
-
-// ---- variants of a2 and a3 (scale formulas over explicit ratio lists, per-row quantizers)
-constexpr int kMaxRatios = 64;
-struct RatioList {
-  double r[kMaxRatios];
-};
-constexpr int kFormulaMs = 0;    // max(a^r, 1e-4) / sqrt(max * min)
-constexpr int kFormulaRms = 1;   // max(max(a, 1e-5)^r / sqrt(mean(.^2)), 1e-4)
-constexpr int kFormulaDuo = 2;   // max(a^r / (wm^(1-r) + 1e-6), 1e-4) / sqrt(max * min)
-constexpr int kQuantInt4Group = 0;
-constexpr int kQuantInt4Row = 1;
-constexpr int kQuantInt8RowSym = 2;
-hipError_t launch_candidate_scales_ex(const double* act_mean, const double* w_mean, int64_t d_in,
-                                      const RatioList& ratios, int n_ratios, int formula, double* cand_scales,
-                                      hipStream_t stream);
-hipError_t launch_quant_delta_row(const WParts& w, int dtype, int64_t d_in, int quantizer, const double* cand_scales,
-                                  int n_cand, void* delta, hipStream_t stream);
-hipError_t launch_fill(double* p, int64_t n, double v, hipStream_t stream);
-
-// ---- a4
-constexpr int kTileM = 256;  // tokens per error-GEMM tile
-constexpr int kTileN = 256;  // weight rows per error-GEMM tile
-hipError_t launch_error_sse(const void* x, int64_t ld_x, const void* delta, int dtype,
-                            int64_t n_tokens, int64_t d_in, int64_t d_out, int n_cand,
-                            double* tile_sse, hipStream_t stream);
 
 // ---- around the search: source fold and deployment form
 hipError_t launch_fold_scales(const void* src, int64_t ld_src, int dtype, int64_t rows, int64_t cols,

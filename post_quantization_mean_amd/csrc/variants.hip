@@ -21,6 +21,7 @@
 #include <math.h>
 
 #include "internal.h"
+#include "variants.h"
 #include "device_common.h"
 
 #pragma clang fp contract(off)

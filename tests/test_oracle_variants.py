@@ -104,3 +104,35 @@ def test_search_variants_run_and_fall_back_to_ones():
     Xn[0, 3] = np.nan
     scales, losses, k, best = V.search(Xn, W, V.grid_linspace(3), V.FORMULA_DUO, V.QUANT_INT4_ROW)
     assert k == 0 and np.all(np.isnan(losses)) and np.array_equal(best, np.ones(256))
+
+
+def test_int4_row_codes_are_nearest_multiples_brute_force():
+    # q = round(y / (step + 1e-6)) is the integer j nearest to y / (step + 1e-6): brute force over j
+    rng = np.random.default_rng(6)
+    y = rng.standard_normal((4, 64)) * np.array([[0.1], [1.0], [3.0], [0.01]])
+    step = (y.max(axis=1, keepdims=True) - y.min(axis=1, keepdims=True)) / 15.0
+    d = step + 1e-6
+    js = np.arange(-40, 41)[None, None, :]
+    best_j = np.take_along_axis(np.broadcast_to(js, y.shape + (81,)),
+                                np.abs(js * d[:, :, None] - y[:, :, None]).argmin(-1)[..., None], -1)[..., 0]
+    assert np.array_equal(V.quantize_restore_row(y, V.QUANT_INT4_ROW), best_j * step)
+    # every row spans 16 consecutive integers at most (max - min = 15 steps)
+    q = best_j
+    assert np.all(q.max(axis=1) - q.min(axis=1) <= 15)
+
+
+def test_rms_formula_unit_mean_square_and_ratio_law():
+    rng = np.random.default_rng(8)
+    a = np.exp(rng.normal(0, 1, 300))
+    for r in (0.2, 0.5, 0.9):
+        s = V.candidate_scales(V.FORMULA_RMS, a, r)
+        assert s.min() > 1e-4  # no floor active on these values
+        assert math.isclose(float(np.mean(s ** 2)), 1.0, rel_tol=1e-13)
+        assert np.allclose(s[1:] / s[0], (a[1:] / a[0]) ** r, rtol=1e-12)
+
+
+def test_weight_mean_brute_force_over_stacked_rows():
+    rng = np.random.default_rng(9)
+    W = rng.standard_normal((7, 5))
+    want = [sum(abs(W[o, c]) for o in range(7)) / 7 for c in range(5)]
+    assert np.allclose(V.weight_mean(W), want, rtol=1e-15)
