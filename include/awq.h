@@ -77,7 +77,11 @@ typedef enum {
   AWQ_ERR_HIP = 7          /* a HIP runtime call or kernel launch failed */
 } awq_status;
 
-typedef enum { AWQ_DTYPE_F32 = 0, AWQ_DTYPE_BF16 = 1 } awq_dtype;
+typedef enum {
+  AWQ_DTYPE_F32 = 0,
+  AWQ_DTYPE_BF16 = 1,
+  AWQ_DTYPE_F16 = 2 /* float16 (uint16 bit patterns): activations of awq_w4a16_gemm only */
+} awq_dtype;
 
 /* Candidate-scale formulas (awq_candidate_scales_ex), a = act_mean, r = a ratio of the list. */
 typedef enum {
@@ -309,6 +313,31 @@ AWQ_API int awq_search_scales_ex(const void* x, int64_t ld_x, const void* const*
                          const double* ratios, int n_ratios, int formula, int quantizer,
                          int cand_per_pass, double* cand_scales, double* losses, double* best_scales,
                          int32_t* best_info, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------ the export's consumer */
+
+/* Y = X * W_hat^T with W_hat dequantized on the fly from the deployment form written by
+ * awq_quantize_pack + awq_export_fp16 (bjdmk "GPU 硬件级反量化算子内联融合": packed 4-bit weights
+ * unpacked and scaled per group in registers and fed to the matrix units with 16-bit activations;
+ * the 16-bit weights are never written to memory). For input c of output row o, in group
+ * g = c / 128:
+ *   W_hat[o, c] = (q[o, c] - zero[o, g]) * step[o, g]   (qqiyuan dequantize),
+ * exact in float32 and rounded once, to nearest even, to the activations' type; products are
+ * accumulated in float32. X is usually the layer input divided by the searched scales (the fold of
+ * gsyq section 四), so that Y approximates X_orig * W^T.
+ *   x         device, [n_tokens, ld_x] of x_dtype (AWQ_DTYPE_BF16 or AWQ_DTYPE_F16); ld_x >= d_in,
+ *             ld_x a multiple of 8.
+ *   codes     device, uint8 [d_out, d_in / 2] (element 2j in the low 4 bits of byte j), 16-byte
+ *             aligned.
+ *   steps_f16 device, uint16 [d_out, d_in / 128], float16 bit patterns.
+ *   zeros_u4  device, uint8 [d_out, ceil(d_in / 256)], groups 2i / 2i+1 in the low / high 4 bits.
+ *   y         device, [n_tokens, ld_y] of y_dtype (AWQ_DTYPE_F32, or x_dtype: rounded to nearest
+ *             even), ld_y >= d_out; written.
+ * d_in must be a multiple of 128. n_tokens == 0 returns AWQ_ERR_NO_TOKENS. Up to 32 tokens use a
+ * kernel that streams the weights once per 16 tokens; more use one that stages activations in LDS. */
+AWQ_API int awq_w4a16_gemm(const void* x, int64_t ld_x, int x_dtype, const uint8_t* codes,
+                   const uint16_t* steps_f16, const uint8_t* zeros_u4, int64_t n_tokens, int64_t d_in,
+                   int64_t d_out, void* y, int64_t ld_y, int y_dtype, void* stream);
 
 #ifdef __cplusplus
 }

@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libawq_mi35
 AWQ_OK = 0
 AWQ_DTYPE_F32 = 0
 AWQ_DTYPE_BF16 = 1
+AWQ_DTYPE_F16 = 2
 AWQ_INFO_ALL_NONFINITE = 1
 AWQ_MAX_PARTS = 8
 AWQ_MAX_RATIOS = 64
@@ -55,6 +56,8 @@ _SIGNATURES = {
     "awq_quant_delta_ex": (_c_int, [_vp, _vp, _c_int, _c_int, _c_i64, _c_int, _vp, _c_int, _vp, _vp]),
     "awq_search_scales_ex": (_c_int, [_vp, _c_i64, _vp, _vp, _c_int, _c_int, _c_i64, _c_i64, _vp, _vp, _vp,
                                       _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
+    "awq_w4a16_gemm": (_c_int, [_vp, _c_i64, _c_int, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64, _vp, _c_i64, _c_int,
+                                _vp]),
 }
 
 _lib = None
@@ -426,6 +429,39 @@ def awq_search_scales_ex(x: torch.Tensor, w_parts, act_mean: torch.Tensor, ratio
                                     cand.data_ptr(), losses.data_ptr(), best.data_ptr(), info.data_ptr(),
                                     ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream)))
     return {"cand_scales": cand, "losses": losses, "best_scales": best, "best_info": info}
+
+
+def awq_w4a16_gemm(x: torch.Tensor, codes: torch.Tensor, steps_f16: torch.Tensor, zeros_u4: torch.Tensor,
+                   out_dtype=torch.float32, y=None, stream=None):
+    """Y [n_tokens, d_out] = x @ W_hat^T, W_hat dequantized on the fly from the deployment form
+    (codes [d_out, d_in/2] u8, float16 steps as int16/uint16 bits [d_out, d_in/128], zero points
+    packed two per byte [d_out, ceil(d_in/256)]). x is bfloat16 or float16; Y float32 or x's dtype."""
+    lib = load_library()
+    if x.dtype == torch.bfloat16:
+        xd = AWQ_DTYPE_BF16
+    elif x.dtype == torch.float16:
+        xd = AWQ_DTYPE_F16
+    else:
+        raise TypeError("x must be torch.bfloat16 or torch.float16")
+    px, n, d_in, ld = _x_args(x)
+    d_out = codes.shape[0]
+    if out_dtype == torch.float32:
+        yd = AWQ_DTYPE_F32
+    elif out_dtype == x.dtype:
+        yd = xd
+    else:
+        raise TypeError("out_dtype must be torch.float32 or x's dtype")
+    if y is None:
+        y = torch.empty((n, d_out), dtype=out_dtype, device=x.device)
+    if y.dim() != 2 or y.stride(1) != 1 or y.dtype != out_dtype:
+        raise ValueError("y must be a [n_tokens, d_out] matrix of out_dtype with unit stride along d_out")
+    for t, name in ((codes, "codes"), (steps_f16, "steps_f16"), (zeros_u4, "zeros_u4")):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    _check(lib.awq_w4a16_gemm(px, ld, xd, _dev(codes, "codes"), _dev(steps_f16, "steps_f16"),
+                              _dev(zeros_u4, "zeros_u4"), n, d_in, d_out, _dev(y, "y"), y.stride(0), yd,
+                              _stream(stream)))
+    return y
 
 
 def awq_layer(x: torch.Tensor, w_parts, n_grid: int = 20, group_size: int = GROUP_SIZE,

@@ -8,6 +8,7 @@
 #include "awq.h"
 #include "internal.h"
 #include "variants.h"
+#include "w4a16.h"
 
 namespace {
 
@@ -479,6 +480,34 @@ int awq_search_scales_ex(const void* x, int64_t ld_x, const void* const* w_parts
   return run_search(x, ld_x, w_parts, part_rows, n_parts, dtype, n_tokens, d_in, act_mean, w_mean, ratios, formula,
                     quantizer, n_ratios, cand_per_pass, cand_scales, losses, best_scales, best_info, workspace,
                     workspace_bytes, stream);
+}
+
+int awq_w4a16_gemm(const void* x, int64_t ld_x, int x_dtype, const uint8_t* codes, const uint16_t* steps_f16,
+                   const uint8_t* zeros_u4, int64_t n_tokens, int64_t d_in, int64_t d_out, void* y, int64_t ld_y,
+                   int y_dtype, void* stream) {
+  if (x_dtype != AWQ_DTYPE_BF16 && x_dtype != AWQ_DTYPE_F16)
+    return fail(AWQ_ERR_UNSUPPORTED, "x_dtype %d: the activations are AWQ_DTYPE_BF16 or AWQ_DTYPE_F16", x_dtype);
+  if (y_dtype != AWQ_DTYPE_F32 && y_dtype != x_dtype)
+    return fail(AWQ_ERR_UNSUPPORTED, "y_dtype %d: AWQ_DTYPE_F32 or x_dtype", y_dtype);
+  if (n_tokens < 0 || d_out <= 0)
+    return fail(AWQ_ERR_SHAPE, "n_tokens %lld must be >= 0 and d_out %lld > 0", (long long)n_tokens,
+                (long long)d_out);
+  if (n_tokens == 0) return fail(AWQ_ERR_NO_TOKENS, "n_tokens == 0");
+  TRY(check_group(AWQ_GROUP_SIZE, d_in));
+  if (!x || !codes || !steps_f16 || !zeros_u4 || !y) return fail(AWQ_ERR_NULL, "a required pointer is NULL");
+  if (ld_x < d_in) return fail(AWQ_ERR_ARG, "ld_x %lld < d_in %lld", (long long)ld_x, (long long)d_in);
+  if (ld_y < d_out) return fail(AWQ_ERR_ARG, "ld_y %lld < d_out %lld", (long long)ld_y, (long long)d_out);
+  if (ld_x % 8 || !aligned(x, 16)) return fail(AWQ_ERR_UNSUPPORTED, "x must be 16-byte aligned with ld_x % 8 == 0");
+  if (!aligned(codes, 16) || !aligned(steps_f16, 2))
+    return fail(AWQ_ERR_UNSUPPORTED, "codes must be 16-byte and steps_f16 2-byte aligned");
+  if (!aligned(y, y_dtype == AWQ_DTYPE_F32 ? 4 : 2)) return fail(AWQ_ERR_UNSUPPORTED, "y is not element-aligned");
+  if (n_tokens > 0x7FFFFFFF - 256 || d_out > 0x7FFFFFFF - 256 || d_in > 0x7FFFFFFF / 2)
+    return fail(AWQ_ERR_UNSUPPORTED, "sizes beyond the kernels' 32-bit indices");
+  hipError_t e = awq::launch_w4a16_gemm(x, ld_x, x_dtype == AWQ_DTYPE_F16 ? 1 : 0, codes, steps_f16, zeros_u4,
+                                        n_tokens, d_in, d_out, y, ld_y, y_dtype == AWQ_DTYPE_F32,
+                                        (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "w4a16_gemm launch");
+  return ok();
 }
 
 }  // extern "C"

@@ -30,7 +30,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
     names = _declared()
-    assert len(names) == 21
+    assert len(names) == 22
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(b.exported_symbols()) == names
@@ -222,3 +222,27 @@ def test_variant_validation(lib):
     assert call(a20=ws - 8) == 6
     assert call(a18=None) == 1
     assert call(a19=None) == 6
+
+
+def test_w4a16_validation(lib):
+    def call(**kw):
+        a = [FAKE, 256, 1, FAKE, FAKE, FAKE, 16, 256, 300, FAKE, 300, 0, None]
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return lib.awq_w4a16_gemm(*a)
+    assert call(a2=0) == 5          # f32 activations are not a W4A16 input
+    assert "x_dtype" in _err(lib)
+    assert call(a11=2) == 5         # bf16 activations, f16 output
+    assert call(a6=0) == 3
+    assert call(a6=-1) == 2
+    assert call(a8=0) == 2
+    assert call(a7=200) == 2        # d_in not a multiple of 128
+    assert call(a3=None) == 1
+    assert call(a9=None) == 1
+    assert call(a1=128) == 4        # ld_x < d_in
+    assert call(a10=299) == 4       # ld_y < d_out
+    assert call(a1=260) == 5        # ld_x not a multiple of 8
+    assert call(a0=FAKE + 2) == 5
+    assert call(a3=FAKE_ODD) == 5   # codes need 16-byte alignment
+    assert call(a4=FAKE + 1) == 5
+    assert call(a9=FAKE + 2) == 5   # f32 output needs 4-byte alignment
