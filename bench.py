@@ -277,6 +277,26 @@ def main() -> int:
         "quant_delta_int8_row_sym": isolated(lambda: B.awq_quant_delta_ex(w_parts, cand[:cpp],
                                                                           B.AWQ_QUANT_INT8_ROW_SYM, delta[:cpp])),
     }
+    # The export's consumer: the W4A16 product on this layer's deployment form, at decode token
+    # counts (weight-streaming, HBM-bound) and at the calibration token count (matrix-core-bound)
+    w4_ex = B.awq_export_fp16(pack_out["qscales"], pack_out["zeros"])
+    w4_ms, w4_rate = {}, {}
+    w4_bytes_w = wl.d_out * wl.d_in // 2 + wl.d_out * G * 2 + wl.d_out * ((G + 1) // 2)
+    if wl.dtype == "bf16":
+        for m in (1, 16, 32, wl.n_tokens):
+            ym = torch.empty((m, wl.d_out), dtype=x.dtype, device=dev)
+            t_ms = isolated(lambda: B.awq_w4a16_gemm(x[:m], pack_out["codes"], w4_ex["steps_f16"],
+                                                     w4_ex["zeros_u4"], out_dtype=x.dtype, y=ym))
+            w4_ms[f"tokens_{m}"] = t_ms
+            if m <= 32:
+                w4_rate[f"tokens_{m}"] = {"gbps": (w4_bytes_w + m * wl.d_in * 2 + m * wl.d_out * 2) / (t_ms * 1e-3) / 1e9}
+            else:
+                w4_rate[f"tokens_{m}"] = {"tflops": 2.0 * m * wl.d_in * wl.d_out / (t_ms * 1e-3) / 1e12}
+        # context: the library's dense bf16 GEMM on the same shape (weights already 16-bit)
+        wd = w.view(wl.d_out, wl.d_in)
+        yd = torch.empty((wl.n_tokens, wl.d_out), dtype=x.dtype, device=dev)
+        w4_ms["dense_bf16_torch_matmul"] = isolated(lambda: torch.matmul(x, wd.t(), out=yd))
+        del yd
     del flush
     var_gbps = {"weight_mean": (wl.d_out * wl.d_in * esz + wl.d_in * 8) / (var_ms["weight_mean"] * 1e-3) / 1e9,
                 "quant_delta_int4_row": q_bytes / (var_ms["quant_delta_int4_row"] * 1e-3) / 1e9,
@@ -343,6 +363,10 @@ def main() -> int:
                      "ms": var_ms, "gbps": var_gbps,
                      "frac_of_peak": {k: v / PEAK_HBM_GBPS for k, v in var_gbps.items()},
                      "search": search_ms},
+        "w4a16": {"note": "awq_w4a16_gemm on this layer's float16 export, cache flushed, median of 5; decode token "
+                           "counts in GB/s of codes + steps + zeros + X + Y against 8000, the calibration token count in "
+                           "TFLOP/s against 2500; dense_bf16_torch_matmul is the library bf16 GEMM of the same shape",
+                  "ms": w4_ms, "rate": w4_rate},
         "best_k": info_h[0],
     }
     if not args.no_cpu_baseline:

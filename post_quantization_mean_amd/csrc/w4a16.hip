@@ -22,7 +22,10 @@ namespace awq {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBatch = 8;          // small-M kernel: groups whose codes a wave loads at once
+constexpr int kBatch = 4;   // small-M kernel: groups whose codes a wave loads at once
+constexpr int kXSub = 4;    // small-M kernel: groups whose activations are loaded at once
+constexpr int kSmallNT = 1; // small-M kernel: 16-row tiles per wave (more cut the activations' L2
+                            // re-reads but leave too few blocks for layers of 4096 rows)
 constexpr int kBigTokens = 128;    // large-M kernel: tokens per block (8 tiles of 16)
 constexpr int kBigRowsPerWave = 64;  // 4 tiles of 16 output rows per wave
 constexpr int kBigRows = 4 * kBigRowsPerWave;
@@ -66,19 +69,21 @@ __device__ __forceinline__ uint16_t to_out<uint16_t>(float v, int kind) {
   return (uint16_t)(pack2(v, 0.f, kind) & 0xFFFFu);
 }
 
-// The step and the negated offset of group g of a row.
-__device__ __forceinline__ void group_params(const uint16_t* srow, const uint8_t* zrow, int g, float& st,
-                                             float& nzs) {
-  const float s = (float)__builtin_bit_cast(_Float16, srow[g]);
-  const int z = (zrow[g >> 1] >> ((g & 1) * 4)) & 15;
+// The step and the negated offset of a group from its raw float16 step and zero-point byte.
+__device__ __forceinline__ void group_params(uint32_t step_bits, uint32_t zbyte, int g, float& st, float& nzs) {
+  const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)step_bits);
+  const int z = (zbyte >> ((g & 1) * 4)) & 15;
   st = s;
   nzs = -(float)z * s;  // exact: 4-bit integer times an 11-bit mantissa
 }
 
-// Few tokens (decode): a block computes 16 tokens x 16 output rows; its four waves take four
-// contiguous ranges of the groups and their partial products are added in wave order. The
-// weights, read once per 16 tokens, dominate the traffic: each wave has the codes of up to
-// kBatch groups in flight before it starts on them.
+// Few tokens (decode): a block computes 16 tokens x (16 kSmallNT) output rows; its four waves take
+// four contiguous ranges of the groups and their partial products are added in wave order. The
+// weights, read once per 16 tokens, dominate the HBM traffic; each activation fragment is used for
+// kSmallNT row tiles, which divides the activations' re-reads from L2. Loads are unconditional
+// (rows and tokens past the end read the last valid one, whose results are never stored) so that a
+// batch's loads all go out back to back; the codes of the next batch are in flight while the
+// current one is multiplied.
 template <int KIND, typename OutT>
 __global__ __launch_bounds__(kThreads) void w4a16_small_kernel(const uint16_t* __restrict__ x, int64_t ld_x,
                                                               const uint8_t* __restrict__ codes,
@@ -86,53 +91,88 @@ __global__ __launch_bounds__(kThreads) void w4a16_small_kernel(const uint16_t* _
                                                               const uint8_t* __restrict__ zeros, int n_tokens,
                                                               int d_in, int d_out, OutT* __restrict__ y,
                                                               int64_t ld_y) {
+  constexpr int NT = kSmallNT;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, kq = lane >> 4;
-  const int row = blockIdx.x * 16 + n;
-  const int tok = blockIdx.y * 16 + n;
+  const int tok = min(blockIdx.y * 16 + n, n_tokens - 1);
   const int G = d_in / kGroup, GZ = (G + 1) / 2;
-  const bool row_ok = row < d_out, tok_ok = tok < n_tokens;
   const int g_begin = (G * wave) / 4, g_end = (G * (wave + 1)) / 4;
-  const uint8_t* crow = codes + (int64_t)row * (d_in / 2) + kq * 16;
-  const uint16_t* srow = steps + (int64_t)row * G;
-  const uint8_t* zrow = zeros + (int64_t)row * GZ;
+  const uint8_t* crow[NT];
+  const uint16_t* srow[NT];
+  const uint8_t* zrow[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    const int row = min(blockIdx.x * (16 * NT) + 16 * j + n, d_out - 1);
+    crow[j] = codes + (int64_t)row * (d_in / 2) + kq * 16;
+    srow[j] = steps + (int64_t)row * G;
+    zrow[j] = zeros + (int64_t)row * GZ;
+  }
   const uint16_t* xrow = x + (int64_t)tok * ld_x + kq * 32;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int gb = g_begin; gb < g_end; gb += kBatch) {
-    const int nb = min(kBatch, g_end - gb);
-    uint4 cw[kBatch];
-    float st[kBatch], nzs[kBatch];
+  f32x4 acc[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  uint4 cw[kBatch][NT];
+  uint32_t sr[kBatch][NT], zr[kBatch][NT];
+  auto load_w = [&](int gb) {
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
-      cw[i] = make_uint4(0, 0, 0, 0);
-      st[i] = 0.f;
-      nzs[i] = 0.f;
-      if (i < nb && row_ok) {
-        cw[i] = *reinterpret_cast<const uint4*>(crow + (int64_t)(gb + i) * (kGroup / 2));
-        group_params(srow, zrow, gb + i, st[i], nzs[i]);
+      const int g = min(gb + i, g_end - 1);  // a short last batch re-reads its last group (unused)
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        cw[i][j] = *reinterpret_cast<const uint4*>(crow[j] + (int64_t)g * (kGroup / 2));
+        sr[i][j] = srow[j][g];
+        zr[i][j] = zrow[j][g >> 1];
       }
     }
+  };
+  if (g_begin < g_end) load_w(g_begin);
+  for (int gb = g_begin; gb < g_end; gb += kBatch) {
+    uint4 cur[kBatch][NT];
+    float st[kBatch][NT], nzs[kBatch][NT];
 #pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      if (i < nb) {
-        uint4 a[4];
+    for (int i = 0; i < kBatch; ++i)
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-          a[t] = tok_ok ? *reinterpret_cast<const uint4*>(xrow + (gb + i) * kGroup + t * 8) : make_uint4(0, 0, 0, 0);
-        const uint32_t wt[4] = {cw[i].x, cw[i].y, cw[i].z, cw[i].w};
+      for (int j = 0; j < NT; ++j) {
+        cur[i][j] = cw[i][j];
+        group_params(sr[i][j], zr[i][j], gb + i, st[i][j], nzs[i][j]);
+      }
+    if (gb + kBatch < g_end) load_w(gb + kBatch);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) acc = mma<KIND>(a[t], dequant8<KIND>(wt[t], st[i], nzs[i]), acc);
+    for (int h = 0; h < kBatch; h += kXSub) {
+      if (gb + h < g_end) {  // wave-uniform
+        uint4 a[kXSub][4];
+#pragma unroll
+        for (int i = 0; i < kXSub; ++i) {
+          const int g = min(gb + h + i, g_end - 1);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) a[i][t] = *reinterpret_cast<const uint4*>(xrow + g * kGroup + t * 8);
+        }
+#pragma unroll
+        for (int i = 0; i < kXSub; ++i) {
+          if (gb + h + i < g_end) {  // wave-uniform
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+              const uint32_t wt[4] = {cur[h + i][j].x, cur[h + i][j].y, cur[h + i][j].z, cur[h + i][j].w};
+#pragma unroll
+              for (int t = 0; t < 4; ++t)
+                acc[j] = mma<KIND>(a[i][t], dequant8<KIND>(wt[t], st[h + i][j], nzs[h + i][j]), acc[j]);
+            }
+          }
+        }
       }
     }
   }
-  __shared__ f32x4 red[4][64];
-  red[wave][lane] = acc;
+  __shared__ f32x4 red[4][NT][64];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) red[wave][j][lane] = acc[j];
   __syncthreads();
-  if (wave == 0) {
-    const f32x4 s = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+  if (wave < NT) {
+    const int j = wave;
+    const f32x4 s = ((red[0][j][lane] + red[1][j][lane]) + red[2][j][lane]) + red[3][j][lane];
     // C layout of the 16x16 result: lane l holds rows 4 (l / 16) .. +3 of column l mod 16
-    const int orow = blockIdx.x * 16 + (lane & 15);
+    const int orow = blockIdx.x * (16 * NT) + 16 * j + (lane & 15);
     const float sv[4] = {s.x, s.y, s.z, s.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -142,19 +182,55 @@ __global__ __launch_bounds__(kThreads) void w4a16_small_kernel(const uint16_t* _
   }
 }
 
+// s_waitcnt immediate for "no vector-memory operation outstanding" (gfx9 encoding; expcnt and
+// lgkmcnt left at their maxima).
+constexpr int kVmcnt0 = (0x7 << 4) | (0xF << 8);
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// One 16-byte-per-lane buffer load that writes LDS directly (M0 = the wave's LDS destination,
+// lane i's 16 bytes at M0 + 16 i). Issued from inline assembly so that the compiler does not make
+// later LDS reads wait for it; the kernel orders it with its own s_waitcnt vmcnt(0) + barrier. M0 is
+// set in the same statement and nothing else in this kernel uses M0.
+__device__ __forceinline__ void dma_load16(i32x4 rsrc, uint32_t lds_addr, int voff, int soff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "buffer_load_dwordx4 %1, %2, %3 offen lds"
+      :
+      : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff)
+      : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// Raw buffer descriptor: 48-bit base, stride 0, num_records bytes (reads at offsets >= num_records
+// return zero), 32-bit data format, no swizzle.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t num_records) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  i32x4 r;
+  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xFFFF);
+  r.z = __builtin_amdgcn_readfirstlane((int)num_records);
+  r.w = 0x00020000;
+  return r;
+}
+
 // Many tokens (prefill): a block computes 128 tokens x 256 output rows, each wave 128 tokens x 64
-// rows. Per group the block stages the 128 x 128 activations in LDS (16-byte chunks of a token row
-// XOR-swizzled by the token, so that the 16 lanes of a read phase hit distinct banks) and every
-// wave dequantizes its own rows' codes in registers. The next group's activations and codes are
-// loaded while the current one is multiplied.
+// rows. Per group the block's activations (128 tokens x 128 inputs, 32 KiB) go global -> LDS by
+// DMA, 16-byte chunks of a token row XOR-swizzled by the token so that the 16 lanes of a fragment
+// read hit distinct banks; tokens past the end lie outside the buffer range and read as zero. Every
+// wave dequantizes its own rows' codes in registers. The next group's activations and codes are in
+// flight while the current group is multiplied (two LDS stages, two register sets of codes).
 template <int KIND, typename OutT>
-__global__ __launch_bounds__(kThreads) void w4a16_big_kernel(const uint16_t* __restrict__ x, int64_t ld_x,
-                                                            const uint8_t* __restrict__ codes,
-                                                            const uint16_t* __restrict__ steps,
-                                                            const uint8_t* __restrict__ zeros, int n_tokens,
-                                                            int d_in, int d_out, OutT* __restrict__ y,
-                                                            int64_t ld_y) {
-  __shared__ __attribute__((aligned(16))) uint4 xs[2][kBigTokens * 16];  // 2 x 32 KiB
+__global__ __launch_bounds__(kThreads, 2) void w4a16_big_kernel(const uint16_t* __restrict__ x, int64_t ld_x,
+                                                               const uint8_t* __restrict__ codes,
+                                                               const uint16_t* __restrict__ steps,
+                                                               const uint8_t* __restrict__ zeros, int n_tokens,
+                                                               int d_in, int d_out, OutT* __restrict__ y,
+                                                               int64_t ld_y) {
+  __shared__ __attribute__((aligned(1024))) uint4 xs[2][kBigTokens * 16];  // 2 x 32 KiB
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, kq = lane >> 4;
@@ -162,39 +238,44 @@ __global__ __launch_bounds__(kThreads) void w4a16_big_kernel(const uint16_t* __r
   const int tok0 = blockIdx.y * kBigTokens;
   const int row0 = blockIdx.x * kBigRows + wave * kBigRowsPerWave;
 
-  // activations: thread t moves chunks t, t + 256, ... (token = chunk / 16, 16-byte piece = chunk % 16)
-  uint4 xa[8];
-  auto load_x = [&](int g) {
+  // activations: wave w fills LDS chunks p = 512 w + 64 j + lane (token p / 16, slot p % 16) with
+  // the global chunk (p % 16) ^ (token % 16) of that token's 256-byte group slice; the chunk pattern
+  // repeats every 4 instructions (16 tokens), so 4 offsets and a scalar token step cover all 8
+  const int valid_tok = min(kBigTokens, n_tokens - tok0);
+  const i32x4 xr = make_rsrc(x + (int64_t)tok0 * ld_x, (uint32_t)valid_tok * (uint32_t)ld_x * 2u);
+  int xoff[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int c = threadIdx.x + kThreads * j;
-      const int tk = tok0 + (c >> 4);
-      xa[j] = tk < n_tokens ? *reinterpret_cast<const uint4*>(x + (int64_t)tk * ld_x + g * kGroup + (c & 15) * 8)
-                            : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto store_x = [&](int buf) {
+  for (int j = 0; j < 4; ++j) {
+    const int tr = 32 * wave + 4 * j + (lane >> 4);
+    xoff[j] = tr * (int)ld_x * 2 + (((lane & 15) ^ (tr & 15)) * 16);
+  }
+  const int x16 = 16 * (int)ld_x * 2;  // 16 tokens further
+  auto load_x = [&](int g, int buf) {
+    const uint32_t base = lds_address(&xs[buf][512 * wave]);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int c = threadIdx.x + kThreads * j;
-      const int tr = c >> 4;
-      xs[buf][tr * 16 + ((c & 15) ^ (tr & 15))] = xa[j];
-    }
+    for (int j = 0; j < 8; ++j) dma_load16(xr, base + 1024 * j, xoff[j & 3], (j >> 2) * x16 + g * (kGroup * 2));
   };
-  // codes of the wave's 4 row tiles: lane (n, kq) holds 32 codes of row row0 + 16 j + n
-  uint4 cw[4];
-  float st[4], nzs[4];
-  auto load_w = [&](int g) {
+  // codes, steps and zero points of the wave's 64 rows through buffer descriptors whose range ends at
+  // the last valid row (rows past it read zero; their results are not stored). Lane (n, kq) holds the
+  // 32 codes k = 32 kq .. 32 kq + 31 of group g of row row0 + 16 j + n.
+  const int vrows = max(0, min(kBigRowsPerWave, d_out - row0));
+  const int64_t r0 = min(row0, d_out - 1);
+  const __amdgpu_buffer_rsrc_t cr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(codes + r0 * (d_in / 2)), (short)0, vrows * (d_in / 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t sres =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(steps + r0 * G), (short)0, vrows * G * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t zres =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(zeros + r0 * GZ), (short)0, vrows * GZ, 0x00020000);
+  const int c_off = n * (d_in / 2) + kq * 16, s_off = n * G * 2, z_off = n * GZ;
+  uint4 cw[2][4];
+  uint32_t sr[2][4], zr[2][4];
+  auto load_w = [&](int g, int set) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int r = row0 + 16 * j + n;
-      cw[j] = make_uint4(0, 0, 0, 0);
-      st[j] = 0.f;
-      nzs[j] = 0.f;
-      if (r < d_out) {
-        cw[j] = *reinterpret_cast<const uint4*>(codes + (int64_t)r * (d_in / 2) + g * (kGroup / 2) + kq * 16);
-        group_params(steps + (int64_t)r * G, zeros + (int64_t)r * GZ, g, st[j], nzs[j]);
-      }
+      cw[set][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 cr, c_off, 16 * j * (d_in / 2) + g * (kGroup / 2), 0));
+      sr[set][j] = __builtin_amdgcn_raw_buffer_load_b16(sres, s_off, 16 * j * G * 2 + g * 2, 0);
+      zr[set][j] = __builtin_amdgcn_raw_buffer_load_b8(zres, z_off, 16 * j * GZ + (g >> 1), 0);
     }
   };
 
@@ -204,38 +285,62 @@ __global__ __launch_bounds__(kThreads) void w4a16_big_kernel(const uint16_t* __r
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  load_x(0);
-  load_w(0);
-  store_x(0);
-  __syncthreads();
-  for (int g = 0; g < G; ++g) {
-    const int buf = g & 1;
-    const uint4 cur[4] = {cw[0], cw[1], cw[2], cw[3]};
-    const float cst[4] = {st[0], st[1], st[2], st[3]};
-    const float cnz[4] = {nzs[0], nzs[1], nzs[2], nzs[3]};
+  auto step = [&](int g, int buf) {
+    // buf is also the codes register set of group g
     if (g + 1 < G) {
-      load_x(g + 1);
-      load_w(g + 1);
+      load_x(g + 1, buf ^ 1);
+      load_w(g + 1, buf ^ 1);
     }
+    float st[4], nz[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      uint4 b[4];
+    for (int j = 0; j < 4; ++j) group_params(sr[buf][j], zr[buf][j], g, st[j], nz[j]);
+    auto dq = [&](int t, uint4(&b)[4]) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint32_t wj[4] = {cur[j].x, cur[j].y, cur[j].z, cur[j].w};
-        b[j] = dequant8<KIND>(wj[t], cst[j], cnz[j]);
+        const uint32_t wj[4] = {cw[buf][j].x, cw[buf][j].y, cw[buf][j].z, cw[buf][j].w};
+        b[j] = dequant8<KIND>(wj[t], st[j], nz[j]);
       }
+    };
+    // software pipeline: sub-step t's MFMAs run while sub-step t+1's operands are dequantized and
+    // the next token tile's fragment is read from LDS
+    uint4 bcur[4], bnext[4];
+    dq(0, bcur);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      uint4 a = xs[buf][n * 16 + ((4 * kq + t) ^ n)];
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
-        const int tr = 16 * m + n;
-        const uint4 a = xs[buf][tr * 16 + ((4 * kq + t) ^ (tr & 15))];
+        uint4 an;
+        if (m + 1 < 8) {
+          const int tr = 16 * (m + 1) + n;
+          an = xs[buf][tr * 16 + ((4 * kq + t) ^ (tr & 15))];
+        }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[m][j] = mma<KIND>(a, b[j], acc[m][j]);
+        for (int j = 0; j < 4; ++j) acc[m][j] = mma<KIND>(a, bcur[j], acc[m][j]);
+        if (t + 1 < 4 && m < 4) {
+          // a quarter of the next sub-step's dequantization per token tile (j = m)
+          const uint32_t wj[4] = {cw[buf][m].x, cw[buf][m].y, cw[buf][m].z, cw[buf][m].w};
+          bnext[m] = dequant8<KIND>(wj[t + 1], st[m], nz[m]);
+        }
+        a = an;
       }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bcur[j] = bnext[j];
     }
-    if (g + 1 < G) store_x(buf ^ 1);
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
     __syncthreads();
+  };
+
+  load_x(0, 0);
+  load_w(0, 0);
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);
+  __syncthreads();
+  int g = 0;
+  for (; g + 1 < G; g += 2) {
+    step(g, 0);
+    step(g + 1, 1);
   }
+  if (g < G) step(g, 0);
 
 #pragma unroll
   for (int m = 0; m < 8; ++m) {
@@ -263,7 +368,7 @@ hipError_t launch_kind(const void* x, int64_t ld_x, const uint8_t* codes, const 
     hipLaunchKernelGGL((w4a16_big_kernel<KIND, OutT>), grid, dim3(kThreads), 0, st, xp, ld_x, codes, steps, zeros,
                        n_tokens, d_in, d_out, yp, ld_y);
   } else {
-    const dim3 grid((unsigned)((d_out + 15) / 16), (unsigned)((n_tokens + 15) / 16));
+    const dim3 grid((unsigned)((d_out + 16 * kSmallNT - 1) / (16 * kSmallNT)), (unsigned)((n_tokens + 15) / 16));
     hipLaunchKernelGGL((w4a16_small_kernel<KIND, OutT>), grid, dim3(kThreads), 0, st, xp, ld_x, codes, steps, zeros,
                        n_tokens, d_in, d_out, yp, ld_y);
   }
