@@ -297,6 +297,47 @@ def main() -> int:
         yd = torch.empty((wl.n_tokens, wl.d_out), dtype=x.dtype, device=dev)
         w4_ms["dense_bf16_torch_matmul"] = isolated(lambda: torch.matmul(x, wd.t(), out=yd))
         del yd
+    # The block-level objective: the gate/up search scored at the gated MLP's output, at the LLaMA-7B
+    # MLP widths (4096 -> 11008 -> 4096) on this layer's 4096-wide activations, random-init weights
+    blk = {}
+    if wl.dtype == "bf16" and wl.d_in == 4096:
+        d_ff, d_model = 11008, 4096
+        gen_b = torch.Generator(device=dev).manual_seed(7)
+        wg_b = (torch.randn((d_ff, 4096), generator=gen_b, device=dev) * 0.02).to(torch.bfloat16)
+        wu_b = (torch.randn((d_ff, 4096), generator=gen_b, device=dev) * 0.02).to(torch.bfloat16)
+        wd_b = (torch.randn((d_model, d_ff), generator=gen_b, device=dev) * 0.015).to(torch.bfloat16)
+        cpp_b = min(cpp, wl.n_grid)
+        ws_b = torch.empty(B.awq_search_workspace_bytes_mlp(wl.n_tokens, 4096, d_ff, d_model, wl.n_grid, cpp_b),
+                           dtype=torch.uint8, device=dev)
+        out_b = {}
+        run_b = lambda: B.awq_search_scales_mlp(x, wg_b, wu_b, wd_b, act, B.AWQ_ACT_SILU, wl.n_grid, cpp_b,
+                                                workspace=ws_b, out=out_b)
+        out_b.update(run_b())
+        ts = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            run_b()
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        g_ref, u_ref = B.awq_mlp_hidden_ref(x, wg_b, wu_b)
+        dwg = torch.zeros_like(wg_b)
+        dh_b = torch.empty((wl.n_tokens, d_ff), dtype=torch.bfloat16, device=dev)
+        t_ref = isolated(lambda: B.awq_mlp_hidden_ref(x, wg_b, wu_b, g_ref, u_ref))
+        t_dh = isolated(lambda: B.awq_mlp_hidden_delta(x, dwg, dwg, g_ref, u_ref, B.AWQ_ACT_SILU, dh_b))
+        sse_b = torch.empty((1, B.awq_error_tiles(wl.n_tokens, d_model)), dtype=torch.float64, device=dev)
+        t_dn = isolated(lambda: B.awq_error_sse(dh_b, wd_b.view(1, d_model, d_ff), sse_b))
+        f_gu = 2.0 * 2 * wl.n_tokens * 4096 * d_ff
+        f_dn = 2.0 * wl.n_tokens * d_ff * d_model
+        blk = {"shape": {"d_in": 4096, "d_ff": d_ff, "d_model": d_model, "n_tokens": wl.n_tokens,
+                         "n_grid": wl.n_grid},
+               "search_ms": float(np.median(ts)), "candidates_per_s": wl.n_grid / (float(np.median(ts)) * 1e-3),
+               "k_star": int(out_b["best_info"][0].item()),
+               "ms": {"mlp_hidden_ref": t_ref, "mlp_hidden_delta": t_dh, "error_sse_down": t_dn},
+               "tflops": {"mlp_hidden_ref": f_gu / (t_ref * 1e-3) / 1e12, "mlp_hidden_delta": f_gu / (t_dh * 1e-3) / 1e12,
+                          "error_sse_down": f_dn / (t_dn * 1e-3) / 1e12}}
+        del ws_b, g_ref, u_ref, dh_b, wg_b, wu_b, wd_b, dwg
     del flush
     var_gbps = {"weight_mean": (wl.d_out * wl.d_in * esz + wl.d_in * 8) / (var_ms["weight_mean"] * 1e-3) / 1e9,
                 "quant_delta_int4_row": q_bytes / (var_ms["quant_delta_int4_row"] * 1e-3) / 1e9,
@@ -367,6 +408,9 @@ def main() -> int:
                            "counts in GB/s of codes + steps + zeros + X + Y against 8000, the calibration token count in "
                            "TFLOP/s against 2500; dense_bf16_torch_matmul is the library bf16 GEMM of the same shape",
                   "ms": w4_ms, "rate": w4_rate},
+        "block_mlp": dict(blk, note="gate/up search scored at the gated MLP's output (LLaMA-7B MLP widths, "
+                                    "random-init weights): whole search median of 3; per-launch kernels cache "
+                                    "flushed, median of 5, TFLOP/s against 2500"),
         "best_k": info_h[0],
     }
     if not args.no_cpu_baseline:

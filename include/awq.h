@@ -339,6 +339,54 @@ AWQ_API int awq_w4a16_gemm(const void* x, int64_t ld_x, int x_dtype, const uint8
                    const uint16_t* steps_f16, const uint8_t* zeros_u4, int64_t n_tokens, int64_t d_in,
                    int64_t d_out, void* y, int64_t ld_y, int y_dtype, void* stream);
 
+/* ------------------------------------------------------------------ block-level objective */
+
+/* Activations of the gated MLP block (awq_search_scales_mlp). */
+typedef enum { AWQ_ACT_SILU = 0, AWQ_ACT_RELU = 1 } awq_act;
+
+/* The gated MLP's gate and up outputs with the original weights (the float reference of the
+ * block, msModelSlim 缩放因子搜索流程):
+ *   g_ref = X * w_gate^T, u_ref = X * w_up^T   (float32 [n_tokens, d_ff], row pitch d_ff; written)
+ *   x       device, bfloat16 [n_tokens, ld_x] (ld_x >= d_in, a multiple of 8).
+ *   w_gate, w_up  device, bfloat16 [d_ff, d_in].
+ * d_in and d_ff multiples of 128. */
+AWQ_API int awq_mlp_hidden_ref(const void* x, int64_t ld_x, const void* w_gate, const void* w_up, int64_t n_tokens,
+                       int64_t d_in, int64_t d_ff, float* g_ref, float* u_ref, void* stream);
+
+/* The change of the MLP's hidden activations when gate and up are replaced by their quantized
+ * versions W + dW (dW as awq_quant_delta writes it):
+ *   dh = act(g_ref) * u_ref - act(g_ref + X dw_gate^T) * (u_ref + X dw_up^T)
+ * float32 arithmetic, rounded to bfloat16 [n_tokens, d_ff] (row pitch d_ff; written). Since the down
+ * projection is linear, the block's output error is dh * w_down^T, whose sum of squares
+ * awq_error_sse gives (x = dh, delta = w_down).
+ *   act  AWQ_ACT_SILU (v / (1 + e^-v)) or AWQ_ACT_RELU. */
+AWQ_API int awq_mlp_hidden_delta(const void* x, int64_t ld_x, const void* dw_gate, const void* dw_up,
+                         const float* g_ref, const float* u_ref, int act, int64_t n_tokens, int64_t d_in,
+                         int64_t d_ff, void* dh, void* stream);
+
+/* Workspace bytes of awq_search_scales_mlp (0 on invalid sizes). */
+AWQ_API size_t awq_search_workspace_bytes_mlp(int64_t n_tokens, int64_t d_in, int64_t d_ff, int64_t d_model,
+                                      int n_grid, int cand_per_pass);
+
+/* The search for the gate/up pair of a gated MLP y = down(act(x gate^T) * (x up^T)), scored at the
+ * block's output — the lowest common ancestor of the two searched linears (msModelSlim 关键特性,
+ * block-level error; 缩放因子搜索流程). For k = 0 .. n_grid-1 the msModelSlim scales s_k are applied
+ * to gate and up together (one fused set), both are quantized (INT4, groups of 128) and unscaled,
+ * and losses[k] = mean over tokens and d_model outputs of (y_ref - y_k)^2, accumulated as the fixed
+ * order sum of per-tile float64 sums of squares of dh_k * w_down^T; k* as awq_loss_argmin.
+ *   x          device, bfloat16 [n_tokens, ld_x] (the block's input after the norm).
+ *   w_gate, w_up  device, bfloat16 [d_ff, d_in];  w_down  device, bfloat16 [d_model, d_ff].
+ *   act_mean   device, float64 [d_in] (awq_act_stats of x).
+ *   act        AWQ_ACT_SILU or AWQ_ACT_RELU.
+ *   cand_scales, losses, best_scales, best_info: as awq_search_scales.
+ *   workspace  device, >= awq_search_workspace_bytes_mlp(...) bytes, 256-byte aligned.
+ * d_in and d_ff multiples of 128. */
+AWQ_API int awq_search_scales_mlp(const void* x, int64_t ld_x, const void* w_gate, const void* w_up,
+                          const void* w_down, int64_t n_tokens, int64_t d_in, int64_t d_ff, int64_t d_model,
+                          const double* act_mean, int act, int n_grid, int cand_per_pass, double* cand_scales,
+                          double* losses, double* best_scales, int32_t* best_info, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

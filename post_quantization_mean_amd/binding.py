@@ -28,6 +28,8 @@ AWQ_FORMULA_DUO = 2
 AWQ_QUANT_INT4_GROUP = 0
 AWQ_QUANT_INT4_ROW = 1
 AWQ_QUANT_INT8_ROW_SYM = 2
+AWQ_ACT_SILU = 0
+AWQ_ACT_RELU = 1
 
 _c_int, _c_i64, _c_size, _vp = ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
 
@@ -58,6 +60,11 @@ _SIGNATURES = {
                                       _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
     "awq_w4a16_gemm": (_c_int, [_vp, _c_i64, _c_int, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64, _vp, _c_i64, _c_int,
                                 _vp]),
+    "awq_mlp_hidden_ref": (_c_int, [_vp, _c_i64, _vp, _vp, _c_i64, _c_i64, _c_i64, _vp, _vp, _vp]),
+    "awq_mlp_hidden_delta": (_c_int, [_vp, _c_i64, _vp, _vp, _vp, _vp, _c_int, _c_i64, _c_i64, _c_i64, _vp, _vp]),
+    "awq_search_workspace_bytes_mlp": (_c_size, [_c_i64, _c_i64, _c_i64, _c_i64, _c_int, _c_int]),
+    "awq_search_scales_mlp": (_c_int, [_vp, _c_i64, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64, _c_i64, _vp, _c_int,
+                                       _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
 }
 
 _lib = None
@@ -462,6 +469,72 @@ def awq_w4a16_gemm(x: torch.Tensor, codes: torch.Tensor, steps_f16: torch.Tensor
                               _dev(zeros_u4, "zeros_u4"), n, d_in, d_out, _dev(y, "y"), y.stride(0), yd,
                               _stream(stream)))
     return y
+
+
+def _bf16_matrix(t: torch.Tensor, name: str):
+    if t.dtype != torch.bfloat16 or t.dim() != 2 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous bfloat16 matrix")
+    return _dev(t, name)
+
+
+def awq_mlp_hidden_ref(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor, g_ref=None, u_ref=None,
+                       stream=None):
+    """(g_ref, u_ref) = (x @ w_gate^T, x @ w_up^T) in float32, [n_tokens, d_ff] each."""
+    lib = load_library()
+    px, n, d_in, ld = _x_args(x)
+    d_ff = w_gate.shape[0]
+    g_ref = torch.empty((n, d_ff), dtype=torch.float32, device=x.device) if g_ref is None else g_ref
+    u_ref = torch.empty((n, d_ff), dtype=torch.float32, device=x.device) if u_ref is None else u_ref
+    _check(lib.awq_mlp_hidden_ref(px, ld, _bf16_matrix(w_gate, "w_gate"), _bf16_matrix(w_up, "w_up"), n, d_in, d_ff,
+                                  _dev(g_ref, "g_ref"), _dev(u_ref, "u_ref"), _stream(stream)))
+    return g_ref, u_ref
+
+
+def awq_mlp_hidden_delta(x: torch.Tensor, dw_gate: torch.Tensor, dw_up: torch.Tensor, g_ref: torch.Tensor,
+                         u_ref: torch.Tensor, act: int = AWQ_ACT_SILU, dh=None, stream=None):
+    """dh = act(g) u - act(g + x dw_gate^T)(u + x dw_up^T), bfloat16 [n_tokens, d_ff]."""
+    lib = load_library()
+    px, n, d_in, ld = _x_args(x)
+    d_ff = dw_gate.shape[0]
+    dh = torch.empty((n, d_ff), dtype=torch.bfloat16, device=x.device) if dh is None else dh
+    _check(lib.awq_mlp_hidden_delta(px, ld, _bf16_matrix(dw_gate, "dw_gate"), _bf16_matrix(dw_up, "dw_up"),
+                                    _dev(g_ref, "g_ref"), _dev(u_ref, "u_ref"), act, n, d_in, d_ff, _dev(dh, "dh"),
+                                    _stream(stream)))
+    return dh
+
+
+def awq_search_workspace_bytes_mlp(n_tokens: int, d_in: int, d_ff: int, d_model: int, n_grid: int,
+                                   cand_per_pass: int) -> int:
+    return load_library().awq_search_workspace_bytes_mlp(n_tokens, d_in, d_ff, d_model, n_grid, cand_per_pass)
+
+
+def awq_search_scales_mlp(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor,
+                          act_mean: torch.Tensor, act: int = AWQ_ACT_SILU, n_grid: int = 20,
+                          cand_per_pass: int | None = None, workspace=None, out=None, stream=None) -> dict:
+    """The gate/up search scored at the gated MLP block's output. Device tensors: cand_scales, losses,
+    best_scales, best_info."""
+    lib = load_library()
+    px, n, d_in, ld = _x_args(x)
+    d_ff, d_model = w_gate.shape[0], w_down.shape[0]
+    cand_per_pass = cand_per_pass or n_grid
+    dev = x.device
+    out = out or {}
+    cand = out.get("cand_scales")
+    cand = torch.empty((n_grid, d_in), dtype=torch.float64, device=dev) if cand is None else cand
+    losses = out.get("losses")
+    losses = torch.empty(n_grid, dtype=torch.float64, device=dev) if losses is None else losses
+    best = out.get("best_scales")
+    best = torch.empty(d_in, dtype=torch.float64, device=dev) if best is None else best
+    info = out.get("best_info")
+    info = torch.empty(2, dtype=torch.int32, device=dev) if info is None else info
+    ws = _workspace(lib.awq_search_workspace_bytes_mlp(n, d_in, d_ff, d_model, n_grid, cand_per_pass), dev,
+                    workspace)
+    _check(lib.awq_search_scales_mlp(px, ld, _bf16_matrix(w_gate, "w_gate"), _bf16_matrix(w_up, "w_up"),
+                                     _bf16_matrix(w_down, "w_down"), n, d_in, d_ff, d_model,
+                                     _dev(act_mean, "act_mean"), act, n_grid, cand_per_pass, cand.data_ptr(),
+                                     losses.data_ptr(), best.data_ptr(), info.data_ptr(), ws.data_ptr(),
+                                     ws.numel() * ws.element_size(), _stream(stream)))
+    return {"cand_scales": cand, "losses": losses, "best_scales": best, "best_info": info}
 
 
 def awq_layer(x: torch.Tensor, w_parts, n_grid: int = 20, group_size: int = GROUP_SIZE,

@@ -19,7 +19,7 @@ LIB_NAME = "libawq_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["act_stats.hip", "scales.hip", "quant.hip", "err_gemm.hip", "export.hip", "variants.hip", "w4a16.hip", "abi.hip"]
+SOURCES = ["act_stats.hip", "scales.hip", "quant.hip", "err_gemm.hip", "export.hip", "variants.hip", "w4a16.hip", "block_gemm.hip", "abi.hip"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",

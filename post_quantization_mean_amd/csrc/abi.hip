@@ -9,6 +9,7 @@
 #include "internal.h"
 #include "variants.h"
 #include "w4a16.h"
+#include "block.h"
 
 namespace {
 
@@ -191,6 +192,18 @@ int run_search(const void* x, int64_t ld_x, const void* const* w_parts, const in
                               best_scales, best_info, st);
   if (e != hipSuccess) return hip_fail(e, "loss_argmin launch");
   return ok();
+}
+
+int check_mlp_dims(int64_t n_tokens, int64_t d_in, int64_t d_ff) {
+  if (n_tokens < 0) return fail(AWQ_ERR_SHAPE, "n_tokens %lld < 0", (long long)n_tokens);
+  if (n_tokens == 0) return fail(AWQ_ERR_NO_TOKENS, "n_tokens == 0");
+  TRY(check_group(AWQ_GROUP_SIZE, d_in));
+  if (d_ff <= 0 || d_ff % AWQ_GROUP_SIZE)
+    return fail(AWQ_ERR_SHAPE, "d_ff %lld is not a positive multiple of 128", (long long)d_ff);
+  TRY(check_d_in_bytes(AWQ_DTYPE_BF16, d_in));
+  TRY(check_d_in_bytes(AWQ_DTYPE_BF16, d_ff));
+  if (n_tokens * d_ff > ((int64_t)1 << 40)) return fail(AWQ_ERR_UNSUPPORTED, "n_tokens * d_ff too large");
+  return AWQ_OK;
 }
 
 }  // namespace
@@ -507,6 +520,112 @@ int awq_w4a16_gemm(const void* x, int64_t ld_x, int x_dtype, const uint8_t* code
                                         n_tokens, d_in, d_out, y, ld_y, y_dtype == AWQ_DTYPE_F32,
                                         (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "w4a16_gemm launch");
+  return ok();
+}
+
+int awq_mlp_hidden_ref(const void* x, int64_t ld_x, const void* w_gate, const void* w_up, int64_t n_tokens,
+                       int64_t d_in, int64_t d_ff, float* g_ref, float* u_ref, void* stream) {
+  TRY(check_mlp_dims(n_tokens, d_in, d_ff));
+  TRY(check_x(x, AWQ_DTYPE_BF16, n_tokens, d_in, ld_x));
+  if (!w_gate || !w_up || !g_ref || !u_ref) return fail(AWQ_ERR_NULL, "a required pointer is NULL");
+  if (!aligned(w_gate, 16) || !aligned(w_up, 16) || !aligned(g_ref, 4) || !aligned(u_ref, 4))
+    return fail(AWQ_ERR_UNSUPPORTED, "w_gate / w_up must be 16-byte and g_ref / u_ref 4-byte aligned");
+  hipError_t e = awq::launch_mlp_hidden(awq::kModeRef, awq::kActSilu, x, ld_x, w_gate, w_up, n_tokens, d_in, d_ff,
+                                        g_ref, u_ref, nullptr, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "mlp_hidden_ref launch");
+  return ok();
+}
+
+int awq_mlp_hidden_delta(const void* x, int64_t ld_x, const void* dw_gate, const void* dw_up, const float* g_ref,
+                         const float* u_ref, int act, int64_t n_tokens, int64_t d_in, int64_t d_ff, void* dh,
+                         void* stream) {
+  if (act != AWQ_ACT_SILU && act != AWQ_ACT_RELU) return fail(AWQ_ERR_ARG, "act %d is not an awq_act", act);
+  TRY(check_mlp_dims(n_tokens, d_in, d_ff));
+  TRY(check_x(x, AWQ_DTYPE_BF16, n_tokens, d_in, ld_x));
+  if (!dw_gate || !dw_up || !g_ref || !u_ref || !dh) return fail(AWQ_ERR_NULL, "a required pointer is NULL");
+  if (!aligned(dw_gate, 16) || !aligned(dw_up, 16) || !aligned(g_ref, 4) || !aligned(u_ref, 4) || !aligned(dh, 2))
+    return fail(AWQ_ERR_UNSUPPORTED, "dw_gate / dw_up must be 16-byte, g_ref / u_ref 4-byte, dh 2-byte aligned");
+  hipError_t e = awq::launch_mlp_hidden(awq::kModeDelta, act, x, ld_x, dw_gate, dw_up, n_tokens, d_in, d_ff,
+                                        const_cast<float*>(g_ref), const_cast<float*>(u_ref), dh,
+                                        (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "mlp_hidden_delta launch");
+  return ok();
+}
+
+size_t awq_search_workspace_bytes_mlp(int64_t n_tokens, int64_t d_in, int64_t d_ff, int64_t d_model, int n_grid,
+                                      int cand_per_pass) {
+  if (n_tokens <= 0 || d_in <= 0 || d_in % AWQ_GROUP_SIZE || d_ff <= 0 || d_ff % AWQ_GROUP_SIZE || d_model <= 0 ||
+      n_grid < 1 || cand_per_pass < 1 || cand_per_pass > n_grid)
+    return 0;
+  const size_t delta = round_up((size_t)cand_per_pass * 2 * (size_t)d_ff * (size_t)d_in * 2, 256);
+  const size_t gu = 2 * round_up((size_t)n_tokens * (size_t)d_ff * 4, 256);
+  const size_t dh = round_up((size_t)n_tokens * (size_t)d_ff * 2, 256);
+  const size_t sse = round_up((size_t)n_grid * (size_t)awq_error_tiles(n_tokens, d_model) * sizeof(double), 256);
+  return delta + gu + dh + sse;
+}
+
+int awq_search_scales_mlp(const void* x, int64_t ld_x, const void* w_gate, const void* w_up, const void* w_down,
+                          int64_t n_tokens, int64_t d_in, int64_t d_ff, int64_t d_model, const double* act_mean,
+                          int act, int n_grid, int cand_per_pass, double* cand_scales, double* losses,
+                          double* best_scales, int32_t* best_info, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  if (act != AWQ_ACT_SILU && act != AWQ_ACT_RELU) return fail(AWQ_ERR_ARG, "act %d is not an awq_act", act);
+  TRY(check_mlp_dims(n_tokens, d_in, d_ff));
+  TRY(check_x(x, AWQ_DTYPE_BF16, n_tokens, d_in, ld_x));
+  if (d_model <= 0) return fail(AWQ_ERR_SHAPE, "d_model %lld must be > 0", (long long)d_model);
+  if (!w_gate || !w_up || !w_down || !act_mean || !cand_scales || !losses || !best_scales || !best_info)
+    return fail(AWQ_ERR_NULL, "a required pointer is NULL");
+  if (!aligned(w_gate, 16) || !aligned(w_up, 16) || !aligned(w_down, 16))
+    return fail(AWQ_ERR_UNSUPPORTED, "weights must be 16-byte aligned");
+  if (d_ff > ((int64_t)65535 * 128) / 2) return fail(AWQ_ERR_UNSUPPORTED, "d_ff %lld too large", (long long)d_ff);
+  if (n_grid < 1 || n_grid > 65535) return fail(AWQ_ERR_ARG, "n_grid %d outside [1, 65535]", n_grid);
+  if (cand_per_pass < 1 || cand_per_pass > n_grid)
+    return fail(AWQ_ERR_ARG, "cand_per_pass %d outside [1, n_grid]", cand_per_pass);
+  const size_t need = awq_search_workspace_bytes_mlp(n_tokens, d_in, d_ff, d_model, n_grid, cand_per_pass);
+  if (!workspace || workspace_bytes < need)
+    return fail(AWQ_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace ? workspace_bytes : 0, need);
+  if (!aligned(workspace, 256)) return fail(AWQ_ERR_UNSUPPORTED, "workspace is not 256-byte aligned");
+
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = static_cast<char*>(workspace);
+  uint16_t* delta = reinterpret_cast<uint16_t*>(ws);
+  ws += round_up((size_t)cand_per_pass * 2 * (size_t)d_ff * (size_t)d_in * 2, 256);
+  float* g_ref = reinterpret_cast<float*>(ws);
+  ws += round_up((size_t)n_tokens * (size_t)d_ff * 4, 256);
+  float* u_ref = reinterpret_cast<float*>(ws);
+  ws += round_up((size_t)n_tokens * (size_t)d_ff * 4, 256);
+  uint16_t* dh = reinterpret_cast<uint16_t*>(ws);
+  ws += round_up((size_t)n_tokens * (size_t)d_ff * 2, 256);
+  double* tile_sse = reinterpret_cast<double*>(ws);
+  const int64_t tiles = awq_error_tiles(n_tokens, d_model);
+
+  const void* parts[2] = {w_gate, w_up};
+  const int64_t rows[2] = {d_ff, d_ff};
+  awq::WParts w;
+  TRY(make_parts(parts, rows, 2, AWQ_DTYPE_BF16, d_in, &w));
+
+  hipError_t e = awq::launch_candidate_scales(act_mean, d_in, n_grid, cand_scales, st);
+  if (e != hipSuccess) return hip_fail(e, "candidate_scales launch");
+  e = awq::launch_mlp_hidden(awq::kModeRef, act, x, ld_x, w_gate, w_up, n_tokens, d_in, d_ff, g_ref, u_ref, nullptr,
+                             st);
+  if (e != hipSuccess) return hip_fail(e, "mlp_hidden_ref launch");
+  for (int k0 = 0; k0 < n_grid; k0 += cand_per_pass) {
+    const int nk = n_grid - k0 < cand_per_pass ? n_grid - k0 : cand_per_pass;
+    e = awq::launch_quant_delta(w, AWQ_DTYPE_BF16, d_in, cand_scales + (int64_t)k0 * d_in, nk, delta, st);
+    if (e != hipSuccess) return hip_fail(e, "quant_delta launch");
+    for (int k = 0; k < nk; ++k) {
+      const uint16_t* dwg = delta + (int64_t)k * 2 * d_ff * d_in;
+      e = awq::launch_mlp_hidden(awq::kModeDelta, act, x, ld_x, dwg, dwg + d_ff * d_in, n_tokens, d_in, d_ff, g_ref,
+                                 u_ref, dh, st);
+      if (e != hipSuccess) return hip_fail(e, "mlp_hidden_delta launch");
+      e = awq::launch_error_sse(dh, d_ff, w_down, AWQ_DTYPE_BF16, n_tokens, d_ff, d_model, 1,
+                                tile_sse + (int64_t)(k0 + k) * tiles, st);
+      if (e != hipSuccess) return hip_fail(e, "error_sse launch");
+    }
+  }
+  e = awq::launch_loss_argmin(tile_sse, tiles, n_grid, n_tokens, d_model, cand_scales, d_in, losses, best_scales,
+                              best_info, st);
+  if (e != hipSuccess) return hip_fail(e, "loss_argmin launch");
   return ok();
 }
 

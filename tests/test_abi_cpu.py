@@ -30,7 +30,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
     names = _declared()
-    assert len(names) == 22
+    assert len(names) == 26
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(b.exported_symbols()) == names
@@ -246,3 +246,36 @@ def test_w4a16_validation(lib):
     assert call(a3=FAKE_ODD) == 5   # codes need 16-byte alignment
     assert call(a4=FAKE + 1) == 5
     assert call(a9=FAKE + 2) == 5   # f32 output needs 4-byte alignment
+
+
+def test_mlp_block_validation(lib):
+    assert lib.awq_search_workspace_bytes_mlp(4096, 4096, 11008, 4096, 20, 20) == (
+        20 * 2 * 11008 * 4096 * 2 + 2 * 4096 * 11008 * 4 + 4096 * 11008 * 2 + ((20 * 16 * 16 * 8 + 255) // 256) * 256)
+    assert lib.awq_search_workspace_bytes_mlp(4096, 4096, 11000, 4096, 20, 20) == 0   # d_ff % 128
+    assert lib.awq_search_workspace_bytes_mlp(4096, 4096, 11008, 4096, 20, 21) == 0
+    # hidden reference / delta
+    assert lib.awq_mlp_hidden_ref(FAKE, 256, FAKE, FAKE, 0, 256, 384, FAKE, FAKE, None) == 3
+    assert lib.awq_mlp_hidden_ref(FAKE, 256, FAKE, FAKE, 100, 200, 384, FAKE, FAKE, None) == 2
+    assert lib.awq_mlp_hidden_ref(FAKE, 256, FAKE, FAKE, 100, 256, 300, FAKE, FAKE, None) == 2
+    assert lib.awq_mlp_hidden_ref(FAKE, 256, None, FAKE, 100, 256, 384, FAKE, FAKE, None) == 1
+    assert lib.awq_mlp_hidden_ref(FAKE, 128, FAKE, FAKE, 100, 256, 384, FAKE, FAKE, None) == 4
+    assert lib.awq_mlp_hidden_ref(FAKE, 256, FAKE_ODD, FAKE, 100, 256, 384, FAKE, FAKE, None) == 5
+    assert lib.awq_mlp_hidden_delta(FAKE, 256, FAKE, FAKE, FAKE, FAKE, 2, 100, 256, 384, FAKE, None) == 4
+    assert "act" in _err(lib)
+    assert lib.awq_mlp_hidden_delta(FAKE, 256, FAKE, FAKE, FAKE, FAKE, 0, 100, 256, 384, None, None) == 1
+    # the composed search
+    ws = lib.awq_search_workspace_bytes_mlp(100, 256, 384, 200, 4, 2)
+    a = [FAKE, 256, FAKE, FAKE, FAKE, 100, 256, 384, 200, FAKE, 0, 4, 2, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None]
+    def call(**kw):
+        b = list(a)
+        for i, v in kw.items():
+            b[int(i[1:])] = v
+        return lib.awq_search_scales_mlp(*b)
+    assert call(a10=5) == 4
+    assert call(a8=0) == 2
+    assert call(a4=None) == 1
+    assert call(a12=5) == 4
+    assert call(a11=0) == 4
+    assert call(a18=ws - 8) == 6
+    assert call(a17=FAKE + 16) == 5
+    assert call(a5=0) == 3

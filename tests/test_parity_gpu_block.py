@@ -1,0 +1,131 @@
+"""GPU parity of the block-level objective (the gate/up search scored at the gated MLP's output)
+against the CPU oracle (oracle/awq_block.py), through the C ABI.
+
+* The float32 reference g = X Wg^T, u = X Wu^T bit-exact on exact-arithmetic inputs (small-integer
+  activations, weights on a 2^-6 grid: every product and partial sum is exact in float32), which
+  checks the tile indexing and the accumulator layout; ragged token counts.
+* The hidden difference dh against the float64 definition on the GPU's own quantized weights, within
+  a first-order bound: the float32 accumulation error of g, u and of the candidate's corrections
+  (K 2^-24 sum |x||w| each) through the partial derivatives of act(g) u - act(g + eg)(u + eu), a few
+  float32 roundings of its two terms and one bfloat16 rounding.
+* The composed search against the oracle's search: scales 1e-12, losses 1e-3 relative, k* equal up
+  to oracle near-ties, for SiLU and ReLU, ragged tokens and outputs, and at the LLaMA-7B MLP width.
+  (On the small case the bfloat16 roundings of dW and dh alone move the losses by up to 5.5e-4, as a
+  float64 emulation of those two roundings shows; at the 7B width by ~1e-5.)"""
+import numpy as np
+import pytest
+
+from oracle import awq_block as K
+from oracle import awq_oracle as O
+from oracle import parity as P
+from workloads import custom_workload, make_w, make_x, to_f32, to_torch
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def B():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from post_quantization_mean_amd import binding
+    binding.load_library()
+    return binding
+
+
+def _bf16(a):
+    return torch.from_numpy(np.asarray(a, np.float32)).to(torch.bfloat16).cuda()
+
+
+@pytest.mark.parametrize("n_tokens,d_in,d_ff", [(256, 256, 128), (300, 384, 384), (520, 128, 640)])
+def test_hidden_reference_bit_exact(B, n_tokens, d_in, d_ff):
+    rng = np.random.default_rng(n_tokens + d_in + d_ff)
+    x = rng.integers(-8, 9, (n_tokens, d_in)).astype(np.float64)
+    wg = rng.integers(-64, 65, (d_ff, d_in)) * 2.0 ** -6
+    wu = rng.integers(-64, 65, (d_ff, d_in)) * 2.0 ** -6
+    print(f"[gpu block] hidden reference tokens={n_tokens} d_in={d_in} d_ff={d_ff}", flush=True)
+    g, u = B.awq_mlp_hidden_ref(_bf16(x), _bf16(wg), _bf16(wu))
+    torch.cuda.synchronize()
+    assert np.array_equal(g.cpu().numpy().astype(np.float64), x @ wg.T)
+    assert np.array_equal(u.cpu().numpy().astype(np.float64), x @ wu.T)
+
+
+@pytest.mark.parametrize("act", [K.ACT_SILU, K.ACT_RELU])
+def test_hidden_difference(B, act):
+    wl = custom_workload(300, 256, 384, "bf16", outlier_channels=3, config_id=501)
+    x = make_x(wl)
+    wg = make_w(wl)
+    wu = make_w(custom_workload(16, 256, 384, "bf16", config_id=502))
+    xt, wgt, wut = to_torch(x, "cuda"), to_torch(wg, "cuda"), to_torch(wu, "cuda")
+    act_mean = B.awq_act_stats(xt)
+    cs = B.awq_candidate_scales(act_mean, 4)
+    delta = B.awq_quant_delta([wgt, wut], cs[2:3])   # [1, 2 d_ff, d_in]
+    g, u = B.awq_mlp_hidden_ref(xt, wgt, wut)
+    dh = B.awq_mlp_hidden_delta(xt, delta[0, :384], delta[0, 384:], g, u, act)
+    torch.cuda.synchronize()
+    X = to_f32(x).astype(np.float64)
+    dW = delta[0].float().cpu().numpy().astype(np.float64)
+    G, U = X @ to_f32(wg).astype(np.float64).T, X @ to_f32(wu).astype(np.float64).T
+    G1, U1 = G + X @ dW[:384].T, U + X @ dW[384:].T
+    a0, a1 = K.act(G, act) * U, K.act(G1, act) * U1
+    want = a0 - a1
+    got = dh.float().cpu().numpy().astype(np.float64)
+    # first-order bound: f(G, U, Eg, Eu) = act(G) U - act(G + Eg)(U + Eu) has |df/dG| <= 1.1 (|U| + |U1|),
+    # |df/dU| <= 1.1 |Eg|, |df/dEg| <= 1.1 |U1|, |df/dEu| <= |act(G1)| (|act'| <= 1.1 for SiLU, 1 for
+    # ReLU); each float32 sum of K = 256 exact products is within K 2^-24 sum |x||w| of the exact one;
+    # then a few float32 roundings (2^-20 of the two terms) and one bfloat16 rounding (2^-8)
+    Xa = np.abs(X)
+    gam = 256 * 2.0 ** -24
+    dG = gam * (Xa @ np.abs(to_f32(wg).astype(np.float64)).T)
+    dU = gam * (Xa @ np.abs(to_f32(wu).astype(np.float64)).T)
+    dEg, dEu = gam * (Xa @ np.abs(dW[:384]).T), gam * (Xa @ np.abs(dW[384:]).T)
+    tol = (2.0 ** -8 * np.abs(want) + 2.0 ** -20 * (np.abs(a0) + np.abs(a1))
+           + 1.1 * (np.abs(U) + np.abs(U1)) * dG + 1.1 * np.abs(G1 - G) * dU + 1.1 * np.abs(U1) * dEg
+           + np.abs(K.act(G1, act)) * dEu + 1e-30)
+    err = np.abs(got - want)
+    print(f"  act {act}: max err / bound {(err / tol).max():.3e}, median |dh| / |act(g) u| "
+          f"{np.median(np.abs(want) / (np.abs(a0) + 1e-30)):.3e}", flush=True)
+    assert np.all(err <= tol)
+
+
+def _search_case(B, wl_x, d_ff, d_model, n_grid, act, seed, cpp=None):
+    x = make_x(wl_x)
+    d_in = wl_x.d_in
+    wg = make_w(custom_workload(16, d_in, d_ff, "bf16", config_id=seed))
+    wu = make_w(custom_workload(16, d_in, d_ff, "bf16", config_id=seed + 1))
+    wd = make_w(custom_workload(16, d_ff, d_model, "bf16", config_id=seed + 2))
+    xt = to_torch(x, "cuda")
+    act_mean = B.awq_act_stats(xt)
+    res = B.awq_search_scales_mlp(xt, to_torch(wg, "cuda"), to_torch(wu, "cuda"), to_torch(wd, "cuda"), act_mean,
+                                  act, n_grid, cand_per_pass=cpp)
+    torch.cuda.synchronize()
+    g = {k: v.cpu().numpy() for k, v in res.items()}
+    f = lambda a: to_f32(a).astype(np.float64)
+    scales, losses, k_or, best = K.block_search(f(x), f(wg), f(wu), f(wd), n_grid, act)
+    return g, scales, losses, k_or
+
+
+@pytest.mark.parametrize("act", [K.ACT_SILU, K.ACT_RELU])
+def test_search_against_oracle(B, act):
+    wl = custom_workload(300, 256, 64, "bf16", outlier_channels=3, config_id=503)
+    print(f"[gpu block] search act={act} tokens=300 d_in=256 d_ff=384 d_model=200", flush=True)
+    g, scales, losses, k_or = _search_case(B, wl, 384, 200, 6, act, 510, cpp=4)
+    assert P.max_rel(g["cand_scales"], scales) < 1e-12
+    rel = P.max_rel(g["losses"], losses)
+    k = int(g["best_info"][0])
+    print(f"  losses max rel {rel:.2e}; k* gpu {k} oracle {k_or}; losses {np.round(losses / losses[0], 4)}",
+          flush=True)
+    assert rel < P.LOSS_RTOL
+    assert int(g["best_info"][1]) == 0 and P.kstar_ok(k, k_or, losses)
+    assert np.array_equal(g["best_scales"], g["cand_scales"][k])
+
+
+def test_search_llama7b_mlp_width(B):
+    # the LLaMA-7B MLP's widths (d_in 4096, d_ff 11008, d_model 4096) on 256 tokens, 3 ratios
+    wl = custom_workload(256, 4096, 64, "bf16", outlier_channels=41, config_id=504)
+    print("[gpu block] search at 4096 -> 11008 -> 4096, 256 tokens, n_grid 3", flush=True)
+    g, scales, losses, k_or = _search_case(B, wl, 11008, 4096, 3, K.ACT_SILU, 520)
+    rel = P.max_rel(g["losses"], losses)
+    k = int(g["best_info"][0])
+    print(f"  losses max rel {rel:.2e}; k* gpu {k} oracle {k_or}", flush=True)
+    assert rel < P.LOSS_RTOL and P.kstar_ok(k, k_or, losses)
