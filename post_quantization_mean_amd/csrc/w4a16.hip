@@ -27,8 +27,10 @@ constexpr int kXSub = 4;    // small-M kernel: groups whose activations are load
 constexpr int kSmallNT = 1; // small-M kernel: 16-row tiles per wave (more cut the activations' L2
                             // re-reads but leave too few blocks for layers of 4096 rows)
 constexpr int kBigTokens = 128;    // large-M kernel: tokens per block (8 tiles of 16)
-constexpr int kBigRowsPerWave = 64;  // 4 tiles of 16 output rows per wave
-constexpr int kBigRows = 4 * kBigRowsPerWave;
+// many-token kernel: NJ tiles of 16 output rows per wave (4 for prefill; 1 for a few hundred tokens,
+// where 4 would leave too few blocks to fill the chip)
+constexpr int kBigNJ = 4, kMidNJ = 1;
+constexpr int64_t kMidMaxTokens = 512;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -223,7 +225,7 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t num_record
 // read hit distinct banks; tokens past the end lie outside the buffer range and read as zero. Every
 // wave dequantizes its own rows' codes in registers. The next group's activations and codes are in
 // flight while the current group is multiplied (two LDS stages, two register sets of codes).
-template <int KIND, typename OutT>
+template <int KIND, typename OutT, int NJ>
 __global__ __launch_bounds__(kThreads, 2) void w4a16_big_kernel(const uint16_t* __restrict__ x, int64_t ld_x,
                                                                const uint8_t* __restrict__ codes,
                                                                const uint16_t* __restrict__ steps,
@@ -236,7 +238,8 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_big_kernel(const uint16_t* 
   const int n = lane & 15, kq = lane >> 4;
   const int G = d_in / kGroup, GZ = (G + 1) / 2;
   const int tok0 = blockIdx.y * kBigTokens;
-  const int row0 = blockIdx.x * kBigRows + wave * kBigRowsPerWave;
+  constexpr int kRowsPerWave = 16 * NJ;
+  const int row0 = blockIdx.x * (4 * kRowsPerWave) + wave * kRowsPerWave;
 
   // activations: wave w fills LDS chunks p = 512 w + 64 j + lane (token p / 16, slot p % 16) with
   // the global chunk (p % 16) ^ (token % 16) of that token's 256-byte group slice; the chunk pattern
@@ -258,7 +261,7 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_big_kernel(const uint16_t* 
   // codes, steps and zero points of the wave's 64 rows through buffer descriptors whose range ends at
   // the last valid row (rows past it read zero; their results are not stored). Lane (n, kq) holds the
   // 32 codes k = 32 kq .. 32 kq + 31 of group g of row row0 + 16 j + n.
-  const int vrows = max(0, min(kBigRowsPerWave, d_out - row0));
+  const int vrows = max(0, min(kRowsPerWave, d_out - row0));
   const int64_t r0 = min(row0, d_out - 1);
   const __amdgpu_buffer_rsrc_t cr =
       __builtin_amdgcn_make_buffer_rsrc((void*)(codes + r0 * (d_in / 2)), (short)0, vrows * (d_in / 2), 0x00020000);
@@ -267,11 +270,11 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_big_kernel(const uint16_t* 
   const __amdgpu_buffer_rsrc_t zres =
       __builtin_amdgcn_make_buffer_rsrc((void*)(zeros + r0 * GZ), (short)0, vrows * GZ, 0x00020000);
   const int c_off = n * (d_in / 2) + kq * 16, s_off = n * G * 2, z_off = n * GZ;
-  uint4 cw[2][4];
-  uint32_t sr[2][4], zr[2][4];
+  uint4 cw[2][NJ];
+  uint32_t sr[2][NJ], zr[2][NJ];
   auto load_w = [&](int g, int set) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NJ; ++j) {
       cw[set][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                                                  cr, c_off, 16 * j * (d_in / 2) + g * (kGroup / 2), 0));
       sr[set][j] = __builtin_amdgcn_raw_buffer_load_b16(sres, s_off, 16 * j * G * 2 + g * 2, 0);
@@ -279,11 +282,11 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_big_kernel(const uint16_t* 
     }
   };
 
-  f32x4 acc[8][4];
+  f32x4 acc[8][NJ];
 #pragma unroll
   for (int m = 0; m < 8; ++m)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NJ; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   auto step = [&](int g, int buf) {
     // buf is also the codes register set of group g
@@ -291,19 +294,19 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_big_kernel(const uint16_t* 
       load_x(g + 1, buf ^ 1);
       load_w(g + 1, buf ^ 1);
     }
-    float st[4], nz[4];
+    float st[NJ], nz[NJ];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) group_params(sr[buf][j], zr[buf][j], g, st[j], nz[j]);
-    auto dq = [&](int t, uint4(&b)[4]) {
+    for (int j = 0; j < NJ; ++j) group_params(sr[buf][j], zr[buf][j], g, st[j], nz[j]);
+    auto dq = [&](int t, uint4(&b)[NJ]) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < NJ; ++j) {
         const uint32_t wj[4] = {cw[buf][j].x, cw[buf][j].y, cw[buf][j].z, cw[buf][j].w};
         b[j] = dequant8<KIND>(wj[t], st[j], nz[j]);
       }
     };
     // software pipeline: sub-step t's MFMAs run while sub-step t+1's operands are dequantized and
     // the next token tile's fragment is read from LDS
-    uint4 bcur[4], bnext[4];
+    uint4 bcur[NJ], bnext[NJ];
     dq(0, bcur);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -316,16 +319,16 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_big_kernel(const uint16_t* 
           an = xs[buf][tr * 16 + ((4 * kq + t) ^ (tr & 15))];
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[m][j] = mma<KIND>(a, bcur[j], acc[m][j]);
-        if (t + 1 < 4 && m < 4) {
-          // a quarter of the next sub-step's dequantization per token tile (j = m)
+        for (int j = 0; j < NJ; ++j) acc[m][j] = mma<KIND>(a, bcur[j], acc[m][j]);
+        if (t + 1 < 4 && m < NJ) {
+          // one row tile of the next sub-step's dequantization per token tile (j = m)
           const uint32_t wj[4] = {cw[buf][m].x, cw[buf][m].y, cw[buf][m].z, cw[buf][m].w};
           bnext[m] = dequant8<KIND>(wj[t + 1], st[m], nz[m]);
         }
         a = an;
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bcur[j] = bnext[j];
+      for (int j = 0; j < NJ; ++j) bcur[j] = bnext[j];
     }
     __builtin_amdgcn_s_waitcnt(kVmcnt0);
     __syncthreads();
@@ -345,7 +348,7 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_big_kernel(const uint16_t* 
 #pragma unroll
   for (int m = 0; m < 8; ++m) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NJ; ++j) {
       const int orow = row0 + 16 * j + (lane & 15);
       const float sv[4] = {acc[m][j].x, acc[m][j].y, acc[m][j].z, acc[m][j].w};
 #pragma unroll
@@ -364,9 +367,13 @@ hipError_t launch_kind(const void* x, int64_t ld_x, const uint8_t* codes, const 
   const uint16_t* xp = static_cast<const uint16_t*>(x);
   OutT* yp = static_cast<OutT*>(y);
   if (big) {
-    const dim3 grid((unsigned)((d_out + kBigRows - 1) / kBigRows), (unsigned)((n_tokens + kBigTokens - 1) / kBigTokens));
-    hipLaunchKernelGGL((w4a16_big_kernel<KIND, OutT>), grid, dim3(kThreads), 0, st, xp, ld_x, codes, steps, zeros,
-                       n_tokens, d_in, d_out, yp, ld_y);
+    const unsigned gy = (unsigned)((n_tokens + kBigTokens - 1) / kBigTokens);
+    if (n_tokens > kMidMaxTokens)
+      hipLaunchKernelGGL((w4a16_big_kernel<KIND, OutT, kBigNJ>), dim3((unsigned)((d_out + 64 * kBigNJ - 1) / (64 * kBigNJ)), gy),
+                         dim3(kThreads), 0, st, xp, ld_x, codes, steps, zeros, n_tokens, d_in, d_out, yp, ld_y);
+    else
+      hipLaunchKernelGGL((w4a16_big_kernel<KIND, OutT, kMidNJ>), dim3((unsigned)((d_out + 64 * kMidNJ - 1) / (64 * kMidNJ)), gy),
+                         dim3(kThreads), 0, st, xp, ld_x, codes, steps, zeros, n_tokens, d_in, d_out, yp, ld_y);
   } else {
     const dim3 grid((unsigned)((d_out + 16 * kSmallNT - 1) / (16 * kSmallNT)), (unsigned)((n_tokens + 15) / 16));
     hipLaunchKernelGGL((w4a16_small_kernel<KIND, OutT>), grid, dim3(kThreads), 0, st, xp, ld_x, codes, steps, zeros,

@@ -8,8 +8,8 @@
   |Y - Y_oracle| <= K 2^-24 sum_c |x_c| |w_hat_c| (+ one rounding of the output when it is 16-bit):
   the products of two 16-bit operands are exact in float32 and each of the at most K additions into
   an output rounds once.
-Both the few-token kernel (<= 32 tokens) and the many-token kernel are covered, with ragged tokens,
-rows and group counts."""
+The few-token kernel (<= 32 tokens) and both shapes of the many-token kernel (16 rows per wave up to
+512 tokens, 64 beyond) are covered, with ragged tokens, rows and group counts."""
 import numpy as np
 import pytest
 
@@ -76,7 +76,8 @@ def _want_bits(yref, out, operand):
 @pytest.mark.parametrize("out", ["f32", "same"])
 @pytest.mark.parametrize("n_tokens,d_in,d_out", [
     (1, 128, 16), (5, 384, 300), (16, 1152, 272), (17, 256, 40), (32, 640, 33),   # few-token kernel
-    (33, 384, 300), (128, 256, 256), (300, 1152, 520), (129, 128, 17),            # many-token kernel
+    (33, 384, 300), (128, 256, 256), (300, 1152, 520), (129, 128, 17),            # many-token kernel,
+    (600, 384, 300), (513, 128, 520),                                              # 16 or 64 rows per wave
 ])
 def test_exact_arithmetic_bit_exact(B, operand, out, n_tokens, d_in, d_out):
     rng = np.random.default_rng(n_tokens * 1000 + d_in + d_out)
