@@ -24,6 +24,8 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kBatch = 4;   // small-M kernel: groups whose codes a wave loads at once
 constexpr int kXSub = 4;    // small-M kernel: groups whose activations are loaded at once
+constexpr int kSmallWaves = 8;  // small-M kernel: waves per block, each 1/8 of the groups (a 4096-input
+                                // layer's codes then fit one batch per wave)
 constexpr int kSmallNT = 1; // small-M kernel: 16-row tiles per wave (more cut the activations' L2
                             // re-reads but leave too few blocks for layers of 4096 rows)
 constexpr int kBigTokens = 128;    // large-M kernel: tokens per block (8 tiles of 16)
@@ -79,15 +81,15 @@ __device__ __forceinline__ void group_params(uint32_t step_bits, uint32_t zbyte,
   nzs = -(float)z * s;  // exact: 4-bit integer times an 11-bit mantissa
 }
 
-// Few tokens (decode): a block computes 16 tokens x (16 kSmallNT) output rows; its four waves take
-// four contiguous ranges of the groups and their partial products are added in wave order. The
+// Few tokens (decode): a block computes 16 tokens x (16 kSmallNT) output rows; its eight waves take
+// eight contiguous ranges of the groups and their partial products are added in wave order. The
 // weights, read once per 16 tokens, dominate the HBM traffic; each activation fragment is used for
 // kSmallNT row tiles, which divides the activations' re-reads from L2. Loads are unconditional
 // (rows and tokens past the end read the last valid one, whose results are never stored) so that a
 // batch's loads all go out back to back; the codes of the next batch are in flight while the
 // current one is multiplied.
 template <int KIND, typename OutT>
-__global__ __launch_bounds__(kThreads) void w4a16_small_kernel(const uint16_t* __restrict__ x, int64_t ld_x,
+__global__ __launch_bounds__(64 * kSmallWaves) void w4a16_small_kernel(const uint16_t* __restrict__ x, int64_t ld_x,
                                                               const uint8_t* __restrict__ codes,
                                                               const uint16_t* __restrict__ steps,
                                                               const uint8_t* __restrict__ zeros, int n_tokens,
@@ -99,7 +101,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_small_kernel(const uint16_t* _
   const int n = lane & 15, kq = lane >> 4;
   const int tok = min(blockIdx.y * 16 + n, n_tokens - 1);
   const int G = d_in / kGroup, GZ = (G + 1) / 2;
-  const int g_begin = (G * wave) / 4, g_end = (G * (wave + 1)) / 4;
+  const int g_begin = (G * wave) / kSmallWaves, g_end = (G * (wave + 1)) / kSmallWaves;
   const uint8_t* crow[NT];
   const uint16_t* srow[NT];
   const uint8_t* zrow[NT];
@@ -166,13 +168,15 @@ __global__ __launch_bounds__(kThreads) void w4a16_small_kernel(const uint16_t* _
       }
     }
   }
-  __shared__ f32x4 red[4][NT][64];
+  __shared__ f32x4 red[kSmallWaves][NT][64];
 #pragma unroll
   for (int j = 0; j < NT; ++j) red[wave][j][lane] = acc[j];
   __syncthreads();
   if (wave < NT) {
     const int j = wave;
-    const f32x4 s = ((red[0][j][lane] + red[1][j][lane]) + red[2][j][lane]) + red[3][j][lane];
+    f32x4 s = red[0][j][lane];
+#pragma unroll
+    for (int w = 1; w < kSmallWaves; ++w) s += red[w][j][lane];
     // C layout of the 16x16 result: lane l holds rows 4 (l / 16) .. +3 of column l mod 16
     const int orow = blockIdx.x * (16 * NT) + 16 * j + (lane & 15);
     const float sv[4] = {s.x, s.y, s.z, s.w};
@@ -376,7 +380,7 @@ hipError_t launch_kind(const void* x, int64_t ld_x, const uint8_t* codes, const 
                          dim3(kThreads), 0, st, xp, ld_x, codes, steps, zeros, n_tokens, d_in, d_out, yp, ld_y);
   } else {
     const dim3 grid((unsigned)((d_out + 16 * kSmallNT - 1) / (16 * kSmallNT)), (unsigned)((n_tokens + 15) / 16));
-    hipLaunchKernelGGL((w4a16_small_kernel<KIND, OutT>), grid, dim3(kThreads), 0, st, xp, ld_x, codes, steps, zeros,
+    hipLaunchKernelGGL((w4a16_small_kernel<KIND, OutT>), grid, dim3(64 * kSmallWaves), 0, st, xp, ld_x, codes, steps, zeros,
                        n_tokens, d_in, d_out, yp, ld_y);
   }
   return hipGetLastError();
