@@ -17,7 +17,8 @@
 //       step = max(max|y| / 127, 1e-8); restored = clip(round(y / step), -127, 127) * step.
 // delta = restored / s - W is written in the weights' dtype. Every operation that decides a
 // rounding is the float64 operation of the definition; a quotient y / d is first formed as
-// y * (1/d) and replaced by the exact division whenever the product could round differently.
+// y * (1/d) and replaced by the exact division whenever the product could round differently, and
+// restored / s is the correctly rounded quotient, so delta equals the definition's float64 value.
 #include <math.h>
 
 #include "internal.h"
@@ -163,62 +164,95 @@ __device__ __forceinline__ double round_quotient(double y, double d, double rd) 
   return rint(y / d);
 }
 
-// One wave per output row; the wave runs through every candidate for its row, so the row's
-// weights come from HBM once and from the caches after that. Lane l holds channels
-// 8l .. 8l+7 of each 512-channel slice.
+// (q step) / s with the correctly rounded reciprocal rs = 1/s: the product, its exact residual, and one
+// fused correction give the correctly rounded quotient (Markstein's theorem on division by
+// multiplication; the values here are far from under- and overflow).
+__device__ __forceinline__ double div_by(double a, double s, double rs) {
+  const double q = a * rs;
+  const double r = fma(-q, s, a);
+  return fma(r, rs, q);
+}
+
+// Each wave owns kRowsPerWave output rows and runs through every candidate for them, so the rows'
+// weights come from HBM once and from the caches after that. Per candidate a first pass over each row
+// finds its extremes; the second goes through the row in 512-channel slices (lane l: channels 8l ..
+// 8l+7 of the slice), forms each channel's reciprocal scale once for the wave's rows, and writes the
+// rows' deltas.
+constexpr int kRowsPerWave = 4;
+
 template <typename T, int Q>
 __global__ __launch_bounds__(kThreads) void quant_delta_row_kernel(WParts w, int64_t d_in, int d_out,
                                                                   const double* __restrict__ cand, int n_cand,
                                                                   T* __restrict__ delta) {
+  constexpr int R = kRowsPerWave;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int o = blockIdx.x * kRowWaves + wave;
-  if (o >= d_out) return;
-  const T* wr = part_row<T>(w, o, d_in);
+  const int o0 = (blockIdx.x * kRowWaves + wave) * R;
+  if (o0 >= d_out) return;
+  const T* wr[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) wr[r] = part_row<T>(w, min(o0 + r, d_out - 1), d_in);
   for (int k = 0; k < n_cand; ++k) {
     const double* s = cand + (int64_t)k * d_in;
-    T* out = delta + ((int64_t)k * d_out + o) * d_in;
-    double mx = -INFINITY, mn = INFINITY;
+    double mx[R], mn[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      mx[r] = -INFINITY;
+      mn[r] = INFINITY;
+    }
     for (int64_t c = lane * 8; c < d_in; c += 512) {
-      double wv[8], sv[8];
-      load8(wr + c, wv);
+      double sv[8];
       load8s(s + c, sv);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const double y = wv[j] * sv[j];
-        if constexpr (Q == kQuantInt8RowSym) {
-          mx = fmax(mx, fabs(y));
-        } else {
-          mx = fmax(mx, y);
-          mn = fmin(mn, y);
+      for (int r = 0; r < R; ++r) {
+        double wv[8];
+        load8(wr[r] + c, wv);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const double y = wv[j] * sv[j];
+          if constexpr (Q == kQuantInt8RowSym) {
+            mx[r] = fmax(mx[r], fabs(y));
+          } else {
+            mx[r] = fmax(mx[r], y);
+            mn[r] = fmin(mn[r], y);
+          }
         }
       }
     }
-    mx = wave_max(mx);
-    double step, div;
-    if constexpr (Q == kQuantInt8RowSym) {
-      step = mx / 127.0;
-      step = step < 1e-8 ? 1e-8 : step;
-      div = step;
-    } else {
-      mn = wave_min(mn);
-      step = (mx - mn) / 15.0;
-      div = step + 1e-6;
-    }
-    const double rd = 1.0 / div;
-    for (int64_t c = lane * 8; c < d_in; c += 512) {
-      double wv[8], sv[8];
-      load8(wr + c, wv);
-      load8s(s + c, sv);
-      float r[8];
+    double step[R], div[R], rdiv[R];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const double y = wv[j] * sv[j];
-        double q = round_quotient(y, div, rd);
-        if constexpr (Q == kQuantInt8RowSym) q = q < -127.0 ? -127.0 : (q > 127.0 ? 127.0 : q);
-        r[j] = (float)((q * step) / sv[j] - wv[j]);
+    for (int r = 0; r < R; ++r) {
+      const double hi = wave_max(mx[r]);
+      if constexpr (Q == kQuantInt8RowSym) {
+        step[r] = hi / 127.0;
+        step[r] = step[r] < 1e-8 ? 1e-8 : step[r];
+        div[r] = step[r];
+      } else {
+        step[r] = (hi - wave_min(mn[r])) / 15.0;
+        div[r] = step[r] + 1e-6;
       }
-      store8(out + c, r);
+      rdiv[r] = 1.0 / div[r];
+    }
+    for (int64_t c = lane * 8; c < d_in; c += 512) {
+      double sv[8], rs[8];
+      load8s(s + c, sv);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) rs[j] = 1.0 / sv[j];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        if (o0 + r >= d_out) break;  // wave-uniform
+        double wv[8];
+        load8(wr[r] + c, wv);
+        float out[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const double y = wv[j] * sv[j];
+          double q = round_quotient(y, div[r], rdiv[r]);
+          if constexpr (Q == kQuantInt8RowSym) q = q < -127.0 ? -127.0 : (q > 127.0 ? 127.0 : q);
+          out[j] = (float)(div_by(q * step[r], sv[j], rs[j]) - wv[j]);
+        }
+        store8(delta + ((int64_t)k * d_out + o0 + r) * d_in + c, out);
+      }
     }
   }
 }
@@ -248,7 +282,7 @@ hipError_t launch_candidate_scales_ex(const double* act_mean, const double* w_me
 hipError_t launch_quant_delta_row(const WParts& w, int dtype, int64_t d_in, int quantizer, const double* cand_scales,
                                   int n_cand, void* delta, hipStream_t st) {
   const int d_out = (int)w.row_begin[w.n];
-  const dim3 grid((unsigned)((d_out + kRowWaves - 1) / kRowWaves));
+  const dim3 grid((unsigned)((d_out + kRowWaves * kRowsPerWave - 1) / (kRowWaves * kRowsPerWave)));
   if (dtype == 1) {
     if (quantizer == kQuantInt8RowSym)
       hipLaunchKernelGGL((quant_delta_row_kernel<uint16_t, kQuantInt8RowSym>), grid, dim3(kThreads), 0, st, w, d_in,
