@@ -320,12 +320,14 @@ void mlp_hidden_kernel(const uint16_t* __restrict__ x, int64_t ld_x, const uint1
 }
 
 int compute_units() {
-  static thread_local int cus = 0;
+  // compute units of the current device, looked up once per device and thread
+  static thread_local int cus_of[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int cus = cus_of[dev];
   if (cus == 0) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess || cus <= 0) cus = 256;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    cus_of[dev] = cus;
   }
   return cus;
 }

@@ -334,12 +334,14 @@ hipError_t launch_error_sse(const void* x, int64_t ld_x, const void* delta, int 
   const int n_cols = tiles_n * n_cand;
   const int64_t nblk = (int64_t)tiles_m * n_cols;
   // one persistent workgroup per compute unit (the tile order assumes 8 XCDs dealt round-robin)
-  static thread_local int cus = 0;
+  // compute units of the current device, looked up once per device and thread
+  static thread_local int cus_of[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int cus = cus_of[dev];
   if (cus == 0) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess || cus <= 0) cus = 256;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    cus_of[dev] = cus;
   }
   const unsigned grid = (unsigned)std::min<int64_t>(nblk, cus);
   if (dtype == 1)

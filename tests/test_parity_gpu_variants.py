@@ -220,3 +220,28 @@ def test_no_finite_loss_keeps_unit_scales(B):
     with np.errstate(invalid="ignore"):
         _, _, _, best = V.search(X, W, [0.25, 0.5, 0.75], V.FORMULA_MSMODELSLIM, V.QUANT_INT8_ROW_SYM)
     assert np.all(best == 1.0)
+
+
+@pytest.mark.parametrize("quantizer", [V.QUANT_INT4_ROW, V.QUANT_INT8_ROW_SYM])
+def test_row_quantizer_full_size_sampled_rows(B, quantizer):
+    # the bench layer (7B fused QKV: 12288 x 4096 bf16), all 20 candidates in one launch as the bench
+    # times it; 24 sampled rows (part boundaries included) bit-exact against the oracle
+    from workloads import workload
+    wl = workload(2)
+    w = make_w(wl)
+    wt = to_torch(w, "cuda")
+    parts = [wt[0:4096], wt[4096:8192], wt[8192:12288]]
+    rng = np.random.default_rng(12)
+    a = np.exp(rng.normal(0.0, 1.0, 4096))
+    a[rng.integers(0, 4096, 41)] *= 60.0
+    cs = B.awq_candidate_scales_ex(torch.from_numpy(a).cuda(), V.grid_ms(20), V.FORMULA_MSMODELSLIM)
+    print(f"[gpu variants] full-size row quantizer {quantizer}: 12288 x 4096, 20 candidates", flush=True)
+    delta = B.awq_quant_delta_ex(parts, cs, quantizer)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, 4095, 4096, 8191, 8192, 12287], rng.integers(0, 12288, 18)]))
+    cs_np = cs.cpu().numpy()
+    W = to_f32(w[rows]).astype(np.float64)
+    for k in (0, 7, 19):
+        d_or = V.restore(W, cs_np[k], quantizer) - W
+        got = _gpu_bits(delta[k][torch.from_numpy(rows).cuda()], "bf16")
+        assert np.array_equal(got, _stored(d_or, "bf16")), (k, int((got != _stored(d_or, "bf16")).sum()))
