@@ -58,7 +58,8 @@ def _source_digest(*paths) -> str:
     return h.hexdigest()[:16]
 
 
-GEMM_SOURCES = ("post_quantization_mean_amd/csrc/err_gemm.hip", "post_quantization_mean_amd/csrc/gemm.h")
+GEMM_SOURCES = ("post_quantization_mean_amd/csrc/err_gemm.hip", "post_quantization_mean_amd/csrc/gemm.h",
+                "post_quantization_mean_amd/csrc/lds_dma.h")
 
 
 def measured_traffic(workload_name: str):

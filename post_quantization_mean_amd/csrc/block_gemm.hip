@@ -21,14 +21,13 @@
 #include <type_traits>
 
 #include "block.h"
+#include "lds_dma.h"
 
 namespace awq {
 namespace {
 
 constexpr int BM = 256, BN = 256;  // tokens, B rows (128 gate + 128 up) per tile
 constexpr int kHalf = 128;         // hidden units per tile
-constexpr int kSuper = 16;
-constexpr int kXcds = 8;
 constexpr int KB = 128;
 constexpr int kStageBytes = (BM + BN) * KB;  // 64 KiB
 constexpr int kThreads = 256;
@@ -36,66 +35,12 @@ constexpr int kSplit = 8;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
-
-// One 16-byte-per-lane buffer load that writes LDS directly (M0 = the wave's LDS destination).
-// Inline assembly so that the compiler does not make later LDS reads wait for it; the kernel orders
-// it with its own s_waitcnt vmcnt + barrier. M0 is set in the same statement and nothing else in
-// this kernel uses M0.
-__device__ __forceinline__ void dma_load16(i32x4 rsrc, uint32_t lds_addr, int voff, int soff) {
-  asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "buffer_load_dwordx4 %1, %2, %3 offen lds"
-      :
-      : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff)
-      : "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_address(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
-}
-
-// Raw buffer descriptor: 48-bit base, stride 0, num_records bytes (reads at offsets >= num_records
-// return zero), 32-bit data format, no swizzle.
-__device__ __forceinline__ i32x4 make_rsrc(const void* base, int num_records) {
-  const uint64_t a = (uint64_t)(uintptr_t)base;
-  i32x4 r;
-  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-  r.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xFFFF);
-  r.z = __builtin_amdgcn_readfirstlane(num_records);
-  r.w = 0x00020000;
-  return r;
-}
 
 template <bool ZC>
 __device__ __forceinline__ void mma_pair(const uint4& a, const uint4& b, f32x16& c) {
   const f32x16 zero = {};
   c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
                                               ZC ? zero : c, 0, 0, 0);
-}
-
-__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
-
-// Tile order of the error GEMM: the 256 concurrent tiles form a 16 x 16 super-block of (token tile,
-// hidden tile) pairs, 8 x 4 per XCD.
-__device__ __forceinline__ void tile_of(int G, int tiles_m, int n_cols, int& tm, int& col) {
-  const int n_sbm = (tiles_m + kSuper - 1) / kSuper, n_sbn = (n_cols + kSuper - 1) / kSuper;
-  const int r = min(G / (kSuper * n_cols), n_sbm - 1);
-  const int G1 = G - kSuper * r * n_cols;
-  const int h = min(kSuper, tiles_m - kSuper * r);
-  const int c = min(G1 / (h * kSuper), n_sbn - 1);
-  const int G2 = G1 - c * h * kSuper;
-  const int w = min(kSuper, n_cols - kSuper * c);
-  if (h == kSuper && w == kSuper) {
-    const int x = G2 % kXcds, q = G2 / kXcds;
-    tm = kSuper * r + (x / 4) * 8 + q % 8;
-    col = kSuper * c + (x % 4) * 4 + q / 8;
-  } else {
-    tm = kSuper * r + G2 % h;
-    col = kSuper * c + G2 / h;
-  }
 }
 
 struct TileOps {

@@ -24,60 +24,23 @@
 // by row, which leaves the fragment reads free of bank conflicts.
 //
 // Tile order: the 256 concurrently running tiles form a 16 x 16 super-block, split 8 x 4 per XCD
-// (see the kernel), so operand K-slices are shared inside each XCD's L2 and across the XCDs in the
-// memory-side cache.
+// (tile_of in lds_dma.h), so operand K-slices are shared inside each XCD's L2 and across the XCDs in
+// the memory-side cache.
 #include <algorithm>
 #include <type_traits>
 
 #include "gemm.h"
+#include "lds_dma.h"
 
 namespace awq {
 namespace {
 
 constexpr int BM = kTileM, BN = kTileN;
-constexpr int kSuper = 16;  // super-block side of the tile order, in tiles
-constexpr int kXcds = 8;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-// s_waitcnt immediate for "at most n vector-memory operations outstanding" (gfx9 encoding;
-// expcnt and lgkmcnt left at their maxima).
-constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
-
-// One 16-byte-per-lane buffer load that writes LDS directly (M0 = the wave's LDS destination).
-// It is issued from inline assembly so that the compiler does not treat it as a possible
-// writer of every later LDS read and wait for it there: this kernel synchronises the stages
-// itself (s_waitcnt vmcnt + barrier). The instruction has no register results. M0 is set in
-// the same statement; nothing else in this kernel uses M0 (no LDS-DMA builtins, GWS or
-// message sends), so the compiler holds no value there across it.
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ void dma_load16(i32x4 rsrc, uint32_t lds_addr, int voff, int soff) {
-  asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "buffer_load_dwordx4 %1, %2, %3 offen lds"
-      :
-      : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff)
-      : "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_address(const char* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
-}
-
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-// Raw buffer descriptor (gfx9 layout): 48-bit base, stride 0, num_records bytes; reads at byte
-// offsets >= num_records return zero. Word 3 selects 32-bit data format, no swizzle.
-__device__ __forceinline__ i32x4 make_rsrc(const void* base, int num_records) {
-  const uint64_t a = (uint64_t)(uintptr_t)base;
-  i32x4 r;
-  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-  r.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xFFFF);
-  r.z = __builtin_amdgcn_readfirstlane(num_records);
-  r.w = 0x00020000;
-  return r;
-}
 
 // One 16-byte fragment pair: a 32 x 32 x (16 bf16 | 8 f32) product into one accumulator; with ZC
 // the accumulator's old value is not read (the matrix core adds to zero), which starts a tile
@@ -105,30 +68,6 @@ constexpr int kThreads = 256;
 // its use (right after the barrier that frees its buffer) and the rest in the first sub-step
 // of the next step, so the texture unit sees no burst.
 constexpr int kSplit = 8;
-
-// 16-byte slot of K chunk c in LDS row r is c ^ swz(r): the fragment reads below (lane l: row
-// l%32, chunk 2s + l/32) then show no LDS bank-conflict cycles on gfx950.
-__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
-
-// The tile of linear index G (see the tile order above): token tile tm, column col (candidate
-// col / tiles_n, row tile col % tiles_n).
-__device__ __forceinline__ void tile_of(int G, int tiles_m, int n_cols, int& tm, int& col) {
-  const int n_sbm = (tiles_m + kSuper - 1) / kSuper, n_sbn = (n_cols + kSuper - 1) / kSuper;
-  const int r = min(G / (kSuper * n_cols), n_sbm - 1);
-  const int G1 = G - kSuper * r * n_cols;
-  const int h = min(kSuper, tiles_m - kSuper * r);
-  const int c = min(G1 / (h * kSuper), n_sbn - 1);
-  const int G2 = G1 - c * h * kSuper;
-  const int w = min(kSuper, n_cols - kSuper * c);
-  if (h == kSuper && w == kSuper) {
-    const int x = G2 % kXcds, q = G2 / kXcds;
-    tm = kSuper * r + (x / 4) * 8 + q % 8;
-    col = kSuper * c + (x % 4) * 4 + q / 8;
-  } else {
-    tm = kSuper * r + G2 % h;
-    col = kSuper * c + G2 / h;
-  }
-}
 
 // Operand descriptors of one tile: A = its 256 token rows of X, B = its 256 rows of the
 // candidate's delta, each a raw buffer whose range ends at the last valid row.

@@ -17,6 +17,7 @@
 // codes for a whole group are one 16-byte load (32 nibbles) and its activations 64 contiguous bytes.
 #include "w4a16.h"
 #include "device_common.h"
+#include "lds_dma.h"
 
 namespace awq {
 namespace {
@@ -188,43 +189,8 @@ __global__ __launch_bounds__(64 * kSmallWaves) void w4a16_small_kernel(const uin
   }
 }
 
-// s_waitcnt immediate for "no vector-memory operation outstanding" (gfx9 encoding; expcnt and
-// lgkmcnt left at their maxima).
-constexpr int kVmcnt0 = (0x7 << 4) | (0xF << 8);
-
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// One 16-byte-per-lane buffer load that writes LDS directly (M0 = the wave's LDS destination,
-// lane i's 16 bytes at M0 + 16 i). Issued from inline assembly so that the compiler does not make
-// later LDS reads wait for it; the kernel orders it with its own s_waitcnt vmcnt(0) + barrier. M0 is
-// set in the same statement and nothing else in this kernel uses M0.
-__device__ __forceinline__ void dma_load16(i32x4 rsrc, uint32_t lds_addr, int voff, int soff) {
-  asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "buffer_load_dwordx4 %1, %2, %3 offen lds"
-      :
-      : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff)
-      : "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_address(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
-}
-
-// Raw buffer descriptor: 48-bit base, stride 0, num_records bytes (reads at offsets >= num_records
-// return zero), 32-bit data format, no swizzle.
-__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t num_records) {
-  const uint64_t a = (uint64_t)(uintptr_t)base;
-  i32x4 r;
-  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-  r.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xFFFF);
-  r.z = __builtin_amdgcn_readfirstlane((int)num_records);
-  r.w = 0x00020000;
-  return r;
-}
-
-// Many tokens (prefill): a block computes 128 tokens x 256 output rows, each wave 128 tokens x 64
-// rows. Per group the block's activations (128 tokens x 128 inputs, 32 KiB) go global -> LDS by
+// Many tokens (prefill): a block computes 128 tokens x 64 NJ output rows, each wave 128 tokens x
+// 16 NJ rows (NJ = 4 for prefill, 1 up to a few hundred tokens). Per group the block's activations (128 tokens x 128 inputs, 32 KiB) go global -> LDS by
 // DMA, 16-byte chunks of a token row XOR-swizzled by the token so that the 16 lanes of a fragment
 // read hit distinct banks; tokens past the end lie outside the buffer range and read as zero. Every
 // wave dequantizes its own rows' codes in registers. The next group's activations and codes are in
@@ -334,13 +300,13 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_big_kernel(const uint16_t* 
 #pragma unroll
       for (int j = 0; j < NJ; ++j) bcur[j] = bnext[j];
     }
-    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
   };
 
   load_x(0, 0);
   load_w(0, 0);
-  __builtin_amdgcn_s_waitcnt(kVmcnt0);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __syncthreads();
   int g = 0;
   for (; g + 1 < G; g += 2) {
