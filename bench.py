@@ -105,10 +105,42 @@ def cpu_baseline(wl, x_np, w_np, target_s: float) -> dict:
         t = run(rows_full)
         rows = rows_full
     layer_s = t * wl.d_out / rows
-    return {"value": wl.n_grid / layer_s, "unit": "candidates/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"full search (act_mean over all {wl.n_tokens} tokens, {wl.n_grid} candidates, float64) on "
-                      f"the first {rows} of {wl.d_out} weight rows; {t:.1f} s, scaled by d_out/rows to the layer",
-            "layer_seconds_est": layer_s}
+    out = {"value": wl.n_grid / layer_s, "unit": "candidates/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"full search (act_mean over all {wl.n_tokens} tokens, {wl.n_grid} candidates, float64) on "
+                     f"the first {rows} of {wl.d_out} weight rows; {t:.1f} s, scaled by d_out/rows to the layer",
+           "layer_seconds_est": layer_s,
+           # the oracle's dominant work is the error product X (What - W)^T per candidate, in float64
+           "gflops_fp64": 2.0 * wl.n_tokens * wl.d_in * rows * wl.n_grid / t / 1e9,
+           "cpu_model": _cpu_model(), "blas": _blas_name()}
+    if wl.d_out * wl.d_in <= 1 << 20:  # the tiny workload: also the oracle on one thread
+        try:
+            from threadpoolctl import threadpool_limits
+            with threadpool_limits(limits=1):
+                out["single_thread_layer_seconds"] = run(wl.d_out)
+        except Exception:  # pragma: no cover
+            pass
+    return out
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _blas_name() -> str:
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [f"{i.get('internal_api')} {i.get('version')}" for i in threadpool_info() if i.get("user_api") == "blas"]
+        return ", ".join(libs) or "unknown"
+    except Exception:  # pragma: no cover
+        return "unknown"
+
 
 
 def main() -> int:
@@ -231,10 +263,10 @@ def main() -> int:
     info_h = info.cpu().tolist()
     _log(f"k*={info_h[0]} flags={info_h[1]} ms/step={ms_step:.3f} gemm={gemm_ms:.3f} ms ({achieved:.1f} TFLOP/s)")
 
-    # HBM kernels on their own, after the timed steps: before every repetition a 512 MiB buffer is
+    # HBM kernels on their own, after the timed steps: before every repetition a 1 GiB buffer is
     # overwritten so that the 256 MB memory-side cache holds none of the kernel's inputs; the median
     # of 5 repetitions, HIP events on the launch stream
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
 
     def isolated(fn, reps=5):
         ts = []
