@@ -140,13 +140,16 @@ ActStatsPlan act_stats_plan(int dtype, int64_t n_tokens, int64_t d_in) {
   ActStatsPlan p{};
   const int vec = dtype == 1 ? 8 : 4;
   const int64_t vec_lanes = d_in / vec;
-  p.lanes_per_row = (vec_lanes % 64 == 0) ? 64 : (vec_lanes % 32 == 0) ? 32 : 16;
+  // 512-byte row slices (two rows per wave load); 256 bytes when d_in only divides that way
+  p.lanes_per_row = (vec_lanes % 32 == 0) ? 32 : 16;
   p.col_blocks = d_in / (p.lanes_per_row * vec);
   const int64_t rows_per_iter = (64 / p.lanes_per_row) * (kThreads / 64);
-  // aim for ~2048 blocks (8 per CU) while giving every block >= 64 rows
+  // At most 1024 blocks (4 per CU, all resident at once: a second, partial round of blocks
+  // would leave a tail), every block >= 64 rows. Measured on the 7B/70B activation shapes,
+  // this beats 2048 or 4096 blocks and 256-byte or 1 KB slices.
   const int64_t min_rows = rows_per_iter * kUnroll > 64 ? rows_per_iter * kUnroll : 64;
   const int64_t max_chunks = (n_tokens + min_rows - 1) / min_rows;
-  int64_t chunks = (2048 + p.col_blocks - 1) / p.col_blocks;
+  int64_t chunks = 1024 / p.col_blocks;
   if (chunks > max_chunks) chunks = max_chunks;
   if (chunks < 1) chunks = 1;
   int64_t rpc = (n_tokens + chunks - 1) / chunks;
@@ -163,13 +166,11 @@ hipError_t launch_act_stats(const void* x, int dtype, int64_t n_tokens, int64_t 
                             hipStream_t st, bool accumulate) {
   hipError_t e;
   if (dtype == 1) {
-    e = p.lanes_per_row == 64 ? launch_partial<uint16_t, 64>(x, ld_x, n_tokens, d_in, partial, p, st)
-        : p.lanes_per_row == 32 ? launch_partial<uint16_t, 32>(x, ld_x, n_tokens, d_in, partial, p, st)
-                                : launch_partial<uint16_t, 16>(x, ld_x, n_tokens, d_in, partial, p, st);
+    e = p.lanes_per_row == 32 ? launch_partial<uint16_t, 32>(x, ld_x, n_tokens, d_in, partial, p, st)
+                              : launch_partial<uint16_t, 16>(x, ld_x, n_tokens, d_in, partial, p, st);
   } else {
-    e = p.lanes_per_row == 64 ? launch_partial<float, 64>(x, ld_x, n_tokens, d_in, partial, p, st)
-        : p.lanes_per_row == 32 ? launch_partial<float, 32>(x, ld_x, n_tokens, d_in, partial, p, st)
-                                : launch_partial<float, 16>(x, ld_x, n_tokens, d_in, partial, p, st);
+    e = p.lanes_per_row == 32 ? launch_partial<float, 32>(x, ld_x, n_tokens, d_in, partial, p, st)
+                              : launch_partial<float, 16>(x, ld_x, n_tokens, d_in, partial, p, st);
   }
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(act_stats_finalize_kernel, dim3((unsigned)((d_in + 63) / 64)),

@@ -23,7 +23,7 @@ struct WParts {
 
 // ---- a1: activation statistic
 struct ActStatsPlan {
-  int lanes_per_row;   // lanes that cover one row slice (16, 32 or 64)
+  int lanes_per_row;   // lanes that cover one row slice (16 or 32)
   int64_t col_blocks;  // blocks along d_in
   int64_t row_chunks;  // blocks along n_tokens (partial sums kept per chunk)
   int64_t rows_per_chunk;

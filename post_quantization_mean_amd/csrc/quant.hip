@@ -40,13 +40,13 @@ constexpr int kThreads = 256;
 constexpr int kRows = 4;               // rows per wave (per lane)
 constexpr int kRowsPerBlock = 4 * kRows;
 #ifndef AWQ_PACK_ROWS
-#define AWQ_PACK_ROWS 4
+#define AWQ_PACK_ROWS 2
 #endif
 #ifndef AWQ_PACK_NT
 #define AWQ_PACK_NT 1  // the pack reads W once: non-temporal loads (measured 6-9 % faster on large layers)
 #endif
 #ifndef AWQ_PACK_GRID
-#define AWQ_PACK_GRID 768
+#define AWQ_PACK_GRID 1024
 #endif
 #ifndef AWQ_PACK_DEPTH
 #define AWQ_PACK_DEPTH 1
@@ -67,6 +67,10 @@ constexpr int kChansPerBlock = 64 * kChans;
 // 3 * 2^-24) step < 8.6e-6 step of y - r * step in float64. Hence |e| <= (0.5 - kGuard32) step32
 // proves |y/step - r| < 0.5, i.e. r is the float64 definition's round(y/step); the zero point
 // -min * rcp(step32) is within 1.2e-5 of the float64 one and is checked the same way.
+// The pack checks in units of the step instead: t = fl(y32 * inv32 + zero) (one rounding, inv32 =
+// rcp(step32) within 2^-23 relative) is within 15.5 * (2^-23 + 2^-22 * 1.04 + 3 * 2^-24 + 2^-23)
+// + 2^-21 < 1.1e-5 of y / step + zero, so |t - round(t)| <= 0.5 - kGuard32 proves that round(t) is
+// the definition's round(y / step) + zero (no tie within reach, zero an integer).
 constexpr float kGuard32 = 1.0f / 65536.0f;
 constexpr float kHalfGuard32 = 0.5f - kGuard32;
 
@@ -470,27 +474,34 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(WParts w, int64
       for (int j = 0; j < E; ++j) y[j] = wv[i][j] * s[j];
       const FastGroup fg = fast_group<E>(y);
       const float z = rintf(fg.zt);
+      // t = y / step + zero with one rounding, q = round(t) (the code: the zero point is an integer,
+      // so away from ties round(y / step) + zero = round(t)), d = t - q exactly; the codes of the
+      // even and odd channels go into the bytes of two words (v_cvt_pk_u8_f32, exact for the
+      // integers 0..15), which one shift-or turns into nibble pairs.
       float em = 0.f;
-      uint32_t pk[E / 8] = {};
+      uint32_t ev[E / 8], od[E / 8];
 #pragma unroll
       for (int j = 0; j < E; ++j) {
-        const float r = rintf(y[j] * fg.inv);
-        const float e = fmaf(-r, fg.step, y[j]);
-        em = j == 0 ? fabsf(e) : fmaxf(em, fabsf(e));
-        pk[j / 8] |= (uint32_t)(r + z) << (4 * (j % 8));  // in [0, 15] when the checks pass
+        const float t = fmaf(y[j], fg.inv, z);
+        const float q = rintf(t);
+        em = j == 0 ? fabsf(t - q) : fmaxf(em, fabsf(t - q));
+        uint32_t& dst = (j & 1) ? od[j / 8] : ev[j / 8];
+        dst = __builtin_amdgcn_cvt_pk_u8_f32(q, (j % 8) / 2, (j % 8) < 2 ? 0u : dst);
       }
       const int64_t o = row0 + i;
       const bool live = col_ok && o < d_out;
-      const bool ok = fg.ok && em <= kHalfGuard32 * fg.step;
+      const bool ok = fg.ok && em <= kHalfGuard32;
       bad[i] = group_mask(__ballot(live && !ok));
       if (live && !((bad[i] >> lane) & 1)) {
         uint2 v;
-        v.x = pk[0];
-        v.y = pk[1];
-        *reinterpret_cast<uint2*>(codes + o * (d_in / 2) + c0 / 2) = v;
+        v.x = ev[0] | (od[0] << 4);  // q in [0, 15] when the checks pass
+        v.y = ev[1] | (od[1] << 4);
+        // row bases are wave-uniform (scalar registers), the lane offsets 32-bit
+        *reinterpret_cast<uint2*>(codes + (o * (d_in / 2) + cb / 2) + (uint32_t)(lane * (E / 2))) = v;
         if ((lane & 7) == 0) {
-          qscales[o * n_groups + c0 / kGroup] = fg.step;
-          zeros[o * n_groups + c0 / kGroup] = (int32_t)z;
+          const int64_t gb = o * n_groups + cb / kGroup;
+          qscales[gb + (uint32_t)(lane >> 3)] = fg.step;
+          zeros[gb + (uint32_t)(lane >> 3)] = (int32_t)z;
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -541,7 +552,8 @@ hipError_t launch_quant_delta(const WParts& w, int dtype, int64_t d_in, const do
 hipError_t launch_quantize_pack(const WParts& w, int dtype, int64_t d_in, const double* s,
                                 uint8_t* codes, float* qscales, int32_t* zeros, hipStream_t st) {
   const int64_t d_out = w.row_begin[w.n];
-  // about three resident blocks per compute unit, each looping over row blocks
+  // four resident blocks per compute unit (4 waves per SIMD at the kernel's register use), each
+  // looping over row blocks
   const int64_t col_blocks = (d_in + kChansPerBlock - 1) / kChansPerBlock;
   const int64_t row_blocks = (d_out + kPackRowsPerBlock - 1) / kPackRowsPerBlock;
   const int64_t ry = std::max<int64_t>(1, std::min<int64_t>(row_blocks, AWQ_PACK_GRID / col_blocks));
