@@ -30,6 +30,8 @@
 // proof: its codes are r + zero, and flagged groups are redone by the whole wave in float64.
 #include <algorithm>
 
+#include <cfloat>
+
 #include "internal.h"
 #include "device_common.h"
 
@@ -194,6 +196,13 @@ struct FastGroup {
   float step, inv, zt;
   bool ok;
 };
+// Minimum / maximum of a lane's value and a neighbour's (DPP) as one v_med3_f32 against -/+FLT_MAX:
+// exact for finite values; an infinity saturates to -/+FLT_MAX, which makes the group's step
+// exceed the fast path's limit, so the group is redone in float64. (fminf/fmaxf would cost an
+// extra instruction per step to quieten a possible signalling NaN coming out of the lane move.)
+__device__ __forceinline__ float lane_min(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, -FLT_MAX); }
+__device__ __forceinline__ float lane_max(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, FLT_MAX); }
+
 template <int E>
 __device__ __forceinline__ FastGroup fast_group(const float (&y)[E]) {
   float mn = y[0], mx = y[0];
@@ -202,12 +211,12 @@ __device__ __forceinline__ FastGroup fast_group(const float (&y)[E]) {
     mn = fminf(mn, y[j]);
     mx = fmaxf(mx, y[j]);
   }
-  mn = fminf(mn, dpp_f32<kDppXor1>(mn));
-  mx = fmaxf(mx, dpp_f32<kDppXor1>(mx));
-  mn = fminf(mn, dpp_f32<kDppXor2>(mn));
-  mx = fmaxf(mx, dpp_f32<kDppXor2>(mx));
-  mn = fminf(mn, dpp_f32<kDppHalfMirror>(mn));
-  mx = fmaxf(mx, dpp_f32<kDppHalfMirror>(mx));
+  mn = lane_min(mn, dpp_f32<kDppXor1>(mn));
+  mx = lane_max(mx, dpp_f32<kDppXor1>(mx));
+  mn = lane_min(mn, dpp_f32<kDppXor2>(mn));
+  mx = lane_max(mx, dpp_f32<kDppXor2>(mx));
+  mn = lane_min(mn, dpp_f32<kDppHalfMirror>(mn));
+  mx = lane_max(mx, dpp_f32<kDppHalfMirror>(mx));
   FastGroup g;
   g.step = (mx - mn) * (1.0f / 15.0f);
   g.inv = __builtin_amdgcn_rcpf(g.step);
