@@ -117,34 +117,68 @@ def _stream(stream) -> int:
 
 
 def _dev(t: torch.Tensor, name: str) -> int:
-    if not t.is_cuda:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
     return t.data_ptr()
 
 
-def _parts(w_parts):
+def _buf(t: torch.Tensor, name: str, dtype, numel: int, device=None) -> int:
+    """Pointer of a caller-supplied tensor that the library reads or writes as `numel` contiguous
+    elements of `dtype` (`dtype` may be a tuple of accepted dtypes). The C entry points see only a
+    pointer, so a wrong dtype, a strided view or a short buffer is refused here."""
+    p = _dev(t, name)
+    ok = dtype if isinstance(dtype, tuple) else (dtype,)
+    if t.dtype not in ok:
+        raise TypeError(f"{name} must be {' or '.join(str(d) for d in ok)}, not {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, {numel} needed")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the other operands on {device}")
+    return p
+
+
+def _parts(w_parts, dtype=None):
+    """Device pointers and row counts of the weight parts (one dtype, one d_in, one device; with
+    `dtype`, the activations' dtype, which the library assumes for both operands)."""
     if isinstance(w_parts, torch.Tensor):
         w_parts = [w_parts]
     w_parts = list(w_parts)
     if not w_parts:
         raise ValueError("no weight parts")
+    w0 = w_parts[0]
     for i, w in enumerate(w_parts):
-        if w.dim() != 2 or not w.is_contiguous():
+        if not isinstance(w, torch.Tensor) or w.dim() != 2 or not w.is_contiguous():
             raise ValueError(f"weight part {i} must be a contiguous [rows, d_in] matrix")
+        if w.dtype != w0.dtype or w.shape[1] != w0.shape[1] or w.device != w0.device:
+            raise ValueError(f"weight part {i} differs from part 0 in dtype, d_in or device")
+    if dtype is not None and w0.dtype != dtype:
+        raise TypeError(f"the weights are {w0.dtype} and the activations {dtype}: they must agree")
     ptrs = (ctypes.c_void_p * len(w_parts))(*[_dev(w, "weight part") for w in w_parts])
     rows = (ctypes.c_int64 * len(w_parts))(*[w.shape[0] for w in w_parts])
     return w_parts, ptrs, rows, sum(w.shape[0] for w in w_parts)
 
 
 def _x_args(x: torch.Tensor):
-    if x.dim() != 2 or x.stride(1) != 1:
+    if not isinstance(x, torch.Tensor) or x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be a [n_tokens, d_in] matrix with unit stride along d_in")
     return _dev(x, "x"), x.shape[0], x.shape[1], x.stride(0)
+
+
+def _vec(t: torch.Tensor, name: str) -> int:
+    """Length of a 1-D tensor argument."""
+    if not isinstance(t, torch.Tensor) or t.dim() != 1:
+        raise ValueError(f"{name} must be a 1-D tensor")
+    return t.shape[0]
 
 
 def _workspace(nbytes: int, device, workspace):
     if workspace is None:
         return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    _dev(workspace, "workspace")
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
     if workspace.numel() * workspace.element_size() < nbytes:
         raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} bytes, {nbytes} needed")
     return workspace
@@ -167,8 +201,9 @@ def awq_act_stats(x: torch.Tensor, act_mean: torch.Tensor | None = None, workspa
     dt = _dtype_code(x)
     if act_mean is None:
         act_mean = torch.empty(d, dtype=torch.float64, device=x.device)
+    pa = _buf(act_mean, "act_mean", torch.float64, d, x.device)
     ws = _workspace(lib.awq_act_stats_workspace_bytes(dt, n, d), x.device, workspace)
-    _check(lib.awq_act_stats(px, dt, n, d, ld, _dev(act_mean, "act_mean"), ws.data_ptr(),
+    _check(lib.awq_act_stats(px, dt, n, d, ld, pa, ws.data_ptr(),
                              ws.numel() * ws.element_size(), _stream(stream)))
     return act_mean
 
@@ -176,11 +211,12 @@ def awq_act_stats(x: torch.Tensor, act_mean: torch.Tensor | None = None, workspa
 def awq_candidate_scales(act_mean: torch.Tensor, n_grid: int, cand_scales=None, stream=None):
     """a2: float64 [n_grid, d_in] candidate scales."""
     lib = load_library()
-    d = act_mean.shape[0]
+    d = _vec(act_mean, "act_mean")
+    pa = _buf(act_mean, "act_mean", torch.float64, d)
     if cand_scales is None:
         cand_scales = torch.empty((n_grid, d), dtype=torch.float64, device=act_mean.device)
-    _check(lib.awq_candidate_scales(_dev(act_mean, "act_mean"), d, n_grid, _dev(cand_scales, "cand_scales"),
-                                    _stream(stream)))
+    pc = _buf(cand_scales, "cand_scales", torch.float64, max(n_grid, 0) * d, act_mean.device)
+    _check(lib.awq_candidate_scales(pa, d, n_grid, pc, _stream(stream)))
     return cand_scales
 
 
@@ -189,12 +225,20 @@ def awq_quant_delta(w_parts, cand_scales: torch.Tensor, group_size: int = GROUP_
     lib = load_library()
     parts, ptrs, rows, d_out = _parts(w_parts)
     d_in = parts[0].shape[1]
-    n_cand = cand_scales.shape[0]
+    n_cand, pc = _cand_arg(cand_scales, d_in)
     if delta is None:
         delta = torch.empty((n_cand, d_out, d_in), dtype=parts[0].dtype, device=parts[0].device)
-    _check(lib.awq_quant_delta(ptrs, rows, len(parts), _dtype_code(parts[0]), d_in, group_size,
-                               _dev(cand_scales, "cand_scales"), n_cand, _dev(delta, "delta"), _stream(stream)))
+    pd = _buf(delta, "delta", parts[0].dtype, n_cand * d_out * d_in, parts[0].device)
+    _check(lib.awq_quant_delta(ptrs, rows, len(parts), _dtype_code(parts[0]), d_in, group_size, pc, n_cand, pd,
+                               _stream(stream)))
     return delta
+
+
+def _cand_arg(cand_scales: torch.Tensor, d_in: int):
+    """(n_cand, pointer) of a float64 [n_cand, d_in] candidate-scale matrix."""
+    if not isinstance(cand_scales, torch.Tensor) or cand_scales.dim() != 2 or cand_scales.shape[1] != d_in:
+        raise ValueError(f"cand_scales must be a [n_cand, {d_in}] matrix")
+    return cand_scales.shape[0], _buf(cand_scales, "cand_scales", torch.float64, cand_scales.numel())
 
 
 def awq_error_tiles(n_tokens: int, d_out: int) -> int:
@@ -205,14 +249,17 @@ def awq_error_sse(x: torch.Tensor, delta: torch.Tensor, tile_sse=None, stream=No
     """a4: float64 [n_cand, tiles] per-tile sums of squares of x @ delta_j^T."""
     lib = load_library()
     px, n, d, ld = _x_args(x)
+    if not isinstance(delta, torch.Tensor) or delta.dim() != 3:
+        raise ValueError("delta must be a [n_cand, d_out, d_in] tensor")
     n_cand, d_out, d_in = delta.shape
     if d_in != d:
         raise ValueError("x and delta disagree on d_in")
+    pd = _buf(delta, "delta", x.dtype, delta.numel(), x.device)
     tiles = lib.awq_error_tiles(n, d_out)
     if tile_sse is None:
         tile_sse = torch.empty((n_cand, tiles), dtype=torch.float64, device=x.device)
-    _check(lib.awq_error_sse(px, ld, _dev(delta, "delta"), _dtype_code(x), n, d, d_out, n_cand,
-                             _dev(tile_sse, "tile_sse"), _stream(stream)))
+    pt = _buf(tile_sse, "tile_sse", torch.float64, n_cand * tiles, x.device)
+    _check(lib.awq_error_sse(px, ld, pd, _dtype_code(x), n, d, d_out, n_cand, pt, _stream(stream)))
     return tile_sse
 
 
@@ -220,16 +267,41 @@ def awq_loss_argmin(tile_sse: torch.Tensor, n_tokens: int, d_out: int, cand_scal
                     losses=None, best_scales=None, best_info=None, stream=None):
     """a5: (losses [n_grid] f64, best_scales [d_in] f64, best_info [2] i32 = {k*, flags})."""
     lib = load_library()
+    if not isinstance(tile_sse, torch.Tensor) or tile_sse.dim() != 2:
+        raise ValueError("tile_sse must be a [n_grid, tiles] matrix")
     n_grid, tiles = tile_sse.shape
-    d_in = cand_scales.shape[1]
     dev = tile_sse.device
+    pt = _buf(tile_sse, "tile_sse", torch.float64, n_grid * tiles)
+    if not isinstance(cand_scales, torch.Tensor) or cand_scales.dim() != 2 or cand_scales.shape[0] < n_grid:
+        raise ValueError(f"cand_scales must be a [n_grid >= {n_grid}, d_in] matrix")
+    d_in = cand_scales.shape[1]
+    pc = _buf(cand_scales, "cand_scales", torch.float64, n_grid * d_in, dev)
     losses = torch.empty(n_grid, dtype=torch.float64, device=dev) if losses is None else losses
     best_scales = torch.empty(d_in, dtype=torch.float64, device=dev) if best_scales is None else best_scales
     best_info = torch.empty(2, dtype=torch.int32, device=dev) if best_info is None else best_info
-    _check(lib.awq_loss_argmin(_dev(tile_sse, "tile_sse"), tiles, n_grid, n_tokens, d_out,
-                               _dev(cand_scales, "cand_scales"), d_in, _dev(losses, "losses"),
-                               _dev(best_scales, "best_scales"), _dev(best_info, "best_info"), _stream(stream)))
+    _check(lib.awq_loss_argmin(pt, tiles, n_grid, n_tokens, d_out, pc, d_in,
+                               _buf(losses, "losses", torch.float64, n_grid, dev),
+                               _buf(best_scales, "best_scales", torch.float64, d_in, dev),
+                               _buf(best_info, "best_info", torch.int32, 2, dev), _stream(stream)))
     return losses, best_scales, best_info
+
+
+def _search_outputs(out, n_grid: int, d_in: int, dev):
+    """The four outputs of a search (caller-supplied in `out`, else allocated) and their pointers."""
+    out = out or {}
+    spec = {"cand_scales": ((max(n_grid, 1), d_in), torch.float64), "losses": ((max(n_grid, 1),), torch.float64),
+            "best_scales": ((d_in,), torch.float64), "best_info": ((2,), torch.int32)}
+    res, ptrs = {}, []
+    for name, (shape, dtype) in spec.items():
+        t = out.get(name)
+        if t is None:
+            t = torch.empty(shape, dtype=dtype, device=dev)
+        numel = 1
+        for v in shape:
+            numel *= v
+        ptrs.append(_buf(t, name, dtype, numel, dev))
+        res[name] = t
+    return res, ptrs
 
 
 def awq_search_workspace_bytes(dtype: int, n_tokens: int, d_in: int, d_out: int, group_size: int,
@@ -244,31 +316,20 @@ def awq_search_scales(x: torch.Tensor, w_parts, act_mean: torch.Tensor, n_grid: 
     """a2..a5 in one call. Returns device tensors: cand_scales, losses, best_scales, best_info."""
     lib = load_library()
     px, n, d, ld = _x_args(x)
-    parts, ptrs, rows, d_out = _parts(w_parts)
     dt = _dtype_code(x)
+    parts, ptrs, rows, d_out = _parts(w_parts, x.dtype)
+    if parts[0].shape[1] != d:
+        raise ValueError("x and the weights disagree on d_in")
     if cand_per_pass is None:
         cand_per_pass = n_grid
     dev = x.device
-    out = out or {}
-    cand = out.get("cand_scales")
-    if cand is None:
-        cand = torch.empty((n_grid, d), dtype=torch.float64, device=dev)
-    losses = out.get("losses")
-    if losses is None:
-        losses = torch.empty(n_grid, dtype=torch.float64, device=dev)
-    best = out.get("best_scales")
-    if best is None:
-        best = torch.empty(d, dtype=torch.float64, device=dev)
-    info = out.get("best_info")
-    if info is None:
-        info = torch.empty(2, dtype=torch.int32, device=dev)
+    pa = _buf(act_mean, "act_mean", torch.float64, d, dev)
+    res, (pc, pl, pb, pi) = _search_outputs(out, n_grid, d, dev)
     need = lib.awq_search_workspace_bytes(dt, n, d, d_out, group_size, n_grid, cand_per_pass)
     ws = _workspace(need, dev, workspace)
-    _check(lib.awq_search_scales(px, ld, ptrs, rows, len(parts), dt, n, d, _dev(act_mean, "act_mean"),
-                                 group_size, n_grid, cand_per_pass, cand.data_ptr(), losses.data_ptr(),
-                                 best.data_ptr(), info.data_ptr(), ws.data_ptr(),
-                                 ws.numel() * ws.element_size(), _stream(stream)))
-    return {"cand_scales": cand, "losses": losses, "best_scales": best, "best_info": info}
+    _check(lib.awq_search_scales(px, ld, ptrs, rows, len(parts), dt, n, d, pa, group_size, n_grid, cand_per_pass,
+                                 pc, pl, pb, pi, ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream)))
+    return res
 
 
 def awq_quantize_pack(w_parts, s: torch.Tensor, group_size: int = GROUP_SIZE, out=None, stream=None) -> dict:
@@ -289,7 +350,10 @@ def awq_quantize_pack(w_parts, s: torch.Tensor, group_size: int = GROUP_SIZE, ou
     if zs is None:
         zs = torch.empty((d_out, g), dtype=torch.int32, device=dev)
     _check(lib.awq_quantize_pack(ptrs, rows, len(parts), _dtype_code(parts[0]), d_in, group_size,
-                                 _dev(s, "s"), codes.data_ptr(), qs.data_ptr(), zs.data_ptr(), _stream(stream)))
+                                 _buf(s, "s", torch.float64, d_in, dev),
+                                 _buf(codes, "codes", torch.uint8, d_out * (d_in // 2), dev),
+                                 _buf(qs, "qscales", torch.float32, d_out * g, dev),
+                                 _buf(zs, "zeros", torch.int32, d_out * g, dev), _stream(stream)))
     return {"codes": codes, "qscales": qs, "zeros": zs}
 
 
@@ -298,8 +362,9 @@ def awq_act_stats_accumulate(x: torch.Tensor, sums: torch.Tensor, workspace=None
     lib = load_library()
     px, n, d, ld = _x_args(x)
     dt = _dtype_code(x)
+    ps = _buf(sums, "sums", torch.float64, d, x.device)
     ws = _workspace(lib.awq_act_stats_workspace_bytes(dt, n, d), x.device, workspace)
-    _check(lib.awq_act_stats_accumulate(px, dt, n, d, ld, _dev(sums, "sums"), ws.data_ptr(),
+    _check(lib.awq_act_stats_accumulate(px, dt, n, d, ld, ps, ws.data_ptr(),
                                         ws.numel() * ws.element_size(), _stream(stream)))
     return sums
 
@@ -307,9 +372,11 @@ def awq_act_stats_accumulate(x: torch.Tensor, sums: torch.Tensor, workspace=None
 def awq_act_stats_finalize(sums: torch.Tensor, total_tokens: int, act_mean=None, stream=None):
     """act_mean = sums / total_tokens (float64 [d_in])."""
     lib = load_library()
+    d = _vec(sums, "sums")
+    ps = _buf(sums, "sums", torch.float64, d)
     if act_mean is None:
         act_mean = torch.empty_like(sums)
-    _check(lib.awq_act_stats_finalize(_dev(sums, "sums"), sums.shape[0], total_tokens, _dev(act_mean, "act_mean"),
+    _check(lib.awq_act_stats_finalize(ps, d, total_tokens, _buf(act_mean, "act_mean", torch.float64, d, sums.device),
                                       _stream(stream)))
     return act_mean
 
@@ -327,15 +394,20 @@ def awq_fold_scales(src: torch.Tensor, s: torch.Tensor, dst=None, stream=None):
         raise ValueError("dst must match src")
     rows, cols = src2.shape
     _check(lib.awq_fold_scales(_dev(src2, "src"), src2.stride(0) if rows > 1 else cols, _dtype_code(src2), rows,
-                               cols, _dev(s, "s"), _dev(dst2, "dst"), dst2.stride(0) if rows > 1 else cols,
-                               _stream(stream)))
+                               cols, _buf(s, "s", torch.float64, rows, src.device), _dev(dst2, "dst"),
+                               dst2.stride(0) if rows > 1 else cols, _stream(stream)))
     return dst
 
 
 def awq_export_fp16(qscales: torch.Tensor, zeros: torch.Tensor, out=None, stream=None) -> dict:
     """Float16 steps (uint16 bits) and zero points packed two per byte, with the two counts."""
     lib = load_library()
+    if not isinstance(qscales, torch.Tensor) or qscales.dim() != 2:
+        raise ValueError("qscales must be a [rows, groups] matrix")
     rows, g = qscales.shape
+    dev = qscales.device
+    pq = _buf(qscales, "qscales", torch.float32, rows * g)
+    pz = _buf(zeros, "zeros", torch.int32, rows * g, dev)
     out = out or {}
     steps = out.get("steps_f16")
     if steps is None:
@@ -346,8 +418,9 @@ def awq_export_fp16(qscales: torch.Tensor, zeros: torch.Tensor, out=None, stream
     counts = out.get("counts")
     if counts is None:
         counts = torch.zeros(2, dtype=torch.int32, device=qscales.device)
-    _check(lib.awq_export_fp16(_dev(qscales, "qscales"), _dev(zeros, "zeros"), rows, g, steps.data_ptr(),
-                               zu4.data_ptr(), counts.data_ptr(), _stream(stream)))
+    _check(lib.awq_export_fp16(pq, pz, rows, g, _buf(steps, "steps_f16", _HALF_BITS, rows * g, dev),
+                               _buf(zu4, "zeros_u4", torch.uint8, rows * ((g + 1) // 2), dev),
+                               _buf(counts, "counts", torch.int32, 2, dev), _stream(stream)))
     return {"steps_f16": steps, "zeros_u4": zu4, "counts": counts}
 
 
@@ -356,8 +429,7 @@ def _ratios(ratios):
     return (ctypes.c_double * max(len(r), 1))(*r), len(r)
 
 
-def _opt_dev(t, name: str) -> int:
-    return 0 if t is None else _dev(t, name)
+_HALF_BITS = (torch.int16, torch.uint16, torch.float16)  # 16-bit containers of float16 bits
 
 
 def awq_weight_mean(w_parts, w_mean=None, workspace=None, stream=None):
@@ -369,9 +441,10 @@ def awq_weight_mean(w_parts, w_mean=None, workspace=None, stream=None):
     dev = parts[0].device
     if w_mean is None:
         w_mean = torch.empty(d_in, dtype=torch.float64, device=dev)
+    pw = _buf(w_mean, "w_mean", torch.float64, d_in, dev)
     need = max(lib.awq_act_stats_workspace_bytes(dt, r, d_in) for r in rows)
     ws = _workspace(need, dev, workspace)
-    _check(lib.awq_weight_mean(ptrs, rows, len(parts), dt, d_in, _dev(w_mean, "w_mean"), ws.data_ptr(),
+    _check(lib.awq_weight_mean(ptrs, rows, len(parts), dt, d_in, pw, ws.data_ptr(),
                                ws.numel() * ws.element_size(), _stream(stream)))
     return w_mean
 
@@ -380,12 +453,15 @@ def awq_candidate_scales_ex(act_mean: torch.Tensor, ratios, formula: int = AWQ_F
                             w_mean=None, cand_scales=None, stream=None):
     """float64 [len(ratios), d_in] candidate scales of a formula over an explicit ratio list."""
     lib = load_library()
-    d = act_mean.shape[0]
+    d = _vec(act_mean, "act_mean")
+    dev = act_mean.device
+    pa = _buf(act_mean, "act_mean", torch.float64, d)
+    pw = 0 if w_mean is None else _buf(w_mean, "w_mean", torch.float64, d, dev)
     rv, n = _ratios(ratios)
     if cand_scales is None:
-        cand_scales = torch.empty((max(n, 1), d), dtype=torch.float64, device=act_mean.device)
-    _check(lib.awq_candidate_scales_ex(_dev(act_mean, "act_mean"), _opt_dev(w_mean, "w_mean"), d, rv, n, formula,
-                                       _dev(cand_scales, "cand_scales"), _stream(stream)))
+        cand_scales = torch.empty((max(n, 1), d), dtype=torch.float64, device=dev)
+    pc = _buf(cand_scales, "cand_scales", torch.float64, n * d, dev)
+    _check(lib.awq_candidate_scales_ex(pa, pw, d, rv, n, formula, pc, _stream(stream)))
     return cand_scales
 
 
@@ -395,11 +471,12 @@ def awq_quant_delta_ex(w_parts, cand_scales: torch.Tensor, quantizer: int = AWQ_
     lib = load_library()
     parts, ptrs, rows, d_out = _parts(w_parts)
     d_in = parts[0].shape[1]
-    n_cand = cand_scales.shape[0]
+    n_cand, pc = _cand_arg(cand_scales, d_in)
     if delta is None:
         delta = torch.empty((n_cand, d_out, d_in), dtype=parts[0].dtype, device=parts[0].device)
-    _check(lib.awq_quant_delta_ex(ptrs, rows, len(parts), _dtype_code(parts[0]), d_in, quantizer,
-                                  _dev(cand_scales, "cand_scales"), n_cand, _dev(delta, "delta"), _stream(stream)))
+    pd = _buf(delta, "delta", parts[0].dtype, n_cand * d_out * d_in, parts[0].device)
+    _check(lib.awq_quant_delta_ex(ptrs, rows, len(parts), _dtype_code(parts[0]), d_in, quantizer, pc, n_cand, pd,
+                                  _stream(stream)))
     return delta
 
 
@@ -410,32 +487,23 @@ def awq_search_scales_ex(x: torch.Tensor, w_parts, act_mean: torch.Tensor, ratio
     """The search over an explicit ratio list with a scale formula and a quantizer."""
     lib = load_library()
     px, n, d, ld = _x_args(x)
-    parts, ptrs, rows, d_out = _parts(w_parts)
     dt = _dtype_code(x)
+    parts, ptrs, rows, d_out = _parts(w_parts, x.dtype)
+    if parts[0].shape[1] != d:
+        raise ValueError("x and the weights disagree on d_in")
     rv, n_r = _ratios(ratios)
     if cand_per_pass is None:
         cand_per_pass = n_r
     dev = x.device
-    out = out or {}
-    cand = out.get("cand_scales")
-    if cand is None:
-        cand = torch.empty((max(n_r, 1), d), dtype=torch.float64, device=dev)
-    losses = out.get("losses")
-    if losses is None:
-        losses = torch.empty(max(n_r, 1), dtype=torch.float64, device=dev)
-    best = out.get("best_scales")
-    if best is None:
-        best = torch.empty(d, dtype=torch.float64, device=dev)
-    info = out.get("best_info")
-    if info is None:
-        info = torch.empty(2, dtype=torch.int32, device=dev)
+    pa = _buf(act_mean, "act_mean", torch.float64, d, dev)
+    pw = 0 if w_mean is None else _buf(w_mean, "w_mean", torch.float64, d, dev)
+    res, (pc, pl, pb, pi) = _search_outputs(out, n_r, d, dev)
     need = lib.awq_search_workspace_bytes(dt, n, d, d_out, GROUP_SIZE, n_r, cand_per_pass)
     ws = _workspace(need, dev, workspace)
-    _check(lib.awq_search_scales_ex(px, ld, ptrs, rows, len(parts), dt, n, d, _dev(act_mean, "act_mean"),
-                                    _opt_dev(w_mean, "w_mean"), rv, n_r, formula, quantizer, cand_per_pass,
-                                    cand.data_ptr(), losses.data_ptr(), best.data_ptr(), info.data_ptr(),
-                                    ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream)))
-    return {"cand_scales": cand, "losses": losses, "best_scales": best, "best_info": info}
+    _check(lib.awq_search_scales_ex(px, ld, ptrs, rows, len(parts), dt, n, d, pa, pw, rv, n_r, formula, quantizer,
+                                    cand_per_pass, pc, pl, pb, pi, ws.data_ptr(), ws.numel() * ws.element_size(),
+                                    _stream(stream)))
+    return res
 
 
 def awq_w4a16_gemm(x: torch.Tensor, codes: torch.Tensor, steps_f16: torch.Tensor, zeros_u4: torch.Tensor,
@@ -451,7 +519,10 @@ def awq_w4a16_gemm(x: torch.Tensor, codes: torch.Tensor, steps_f16: torch.Tensor
     else:
         raise TypeError("x must be torch.bfloat16 or torch.float16")
     px, n, d_in, ld = _x_args(x)
+    if not isinstance(codes, torch.Tensor) or codes.dim() != 2 or codes.shape[1] * 2 != d_in:
+        raise ValueError(f"codes must be a [d_out, {d_in // 2}] matrix")
     d_out = codes.shape[0]
+    g = d_in // GROUP_SIZE
     if out_dtype == torch.float32:
         yd = AWQ_DTYPE_F32
     elif out_dtype == x.dtype:
@@ -460,33 +531,44 @@ def awq_w4a16_gemm(x: torch.Tensor, codes: torch.Tensor, steps_f16: torch.Tensor
         raise TypeError("out_dtype must be torch.float32 or x's dtype")
     if y is None:
         y = torch.empty((n, d_out), dtype=out_dtype, device=x.device)
-    if y.dim() != 2 or y.stride(1) != 1 or y.dtype != out_dtype:
+    if y.dim() != 2 or tuple(y.shape) != (n, d_out) or y.stride(1) != 1 or y.dtype != out_dtype:
         raise ValueError("y must be a [n_tokens, d_out] matrix of out_dtype with unit stride along d_out")
-    for t, name in ((codes, "codes"), (steps_f16, "steps_f16"), (zeros_u4, "zeros_u4")):
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
-    _check(lib.awq_w4a16_gemm(px, ld, xd, _dev(codes, "codes"), _dev(steps_f16, "steps_f16"),
-                              _dev(zeros_u4, "zeros_u4"), n, d_in, d_out, _dev(y, "y"), y.stride(0), yd,
-                              _stream(stream)))
+    dev = x.device
+    _check(lib.awq_w4a16_gemm(px, ld, xd, _buf(codes, "codes", torch.uint8, d_out * (d_in // 2), dev),
+                              _buf(steps_f16, "steps_f16", _HALF_BITS, d_out * g, dev),
+                              _buf(zeros_u4, "zeros_u4", torch.uint8, d_out * ((g + 1) // 2), dev), n, d_in, d_out,
+                              _dev(y, "y"), y.stride(0), yd, _stream(stream)))
     return y
 
 
-def _bf16_matrix(t: torch.Tensor, name: str):
-    if t.dtype != torch.bfloat16 or t.dim() != 2 or not t.is_contiguous():
-        raise ValueError(f"{name} must be a contiguous bfloat16 matrix")
-    return _dev(t, name)
+def _bf16_matrix(t: torch.Tensor, name: str, shape, device) -> int:
+    if not isinstance(t, torch.Tensor) or t.dim() != 2 or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be a {list(shape)} matrix")
+    return _buf(t, name, torch.bfloat16, t.numel(), device)
+
+
+def _x_bf16(x: torch.Tensor):
+    """x arguments of the block-level entry points, which take bfloat16 activations."""
+    if not isinstance(x, torch.Tensor) or x.dtype != torch.bfloat16:
+        raise TypeError("x must be torch.bfloat16")
+    return _x_args(x)
 
 
 def awq_mlp_hidden_ref(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor, g_ref=None, u_ref=None,
                        stream=None):
     """(g_ref, u_ref) = (x @ w_gate^T, x @ w_up^T) in float32, [n_tokens, d_ff] each."""
     lib = load_library()
-    px, n, d_in, ld = _x_args(x)
+    px, n, d_in, ld = _x_bf16(x)
+    if not isinstance(w_gate, torch.Tensor) or w_gate.dim() != 2:
+        raise ValueError("w_gate must be a [d_ff, d_in] matrix")
     d_ff = w_gate.shape[0]
-    g_ref = torch.empty((n, d_ff), dtype=torch.float32, device=x.device) if g_ref is None else g_ref
-    u_ref = torch.empty((n, d_ff), dtype=torch.float32, device=x.device) if u_ref is None else u_ref
-    _check(lib.awq_mlp_hidden_ref(px, ld, _bf16_matrix(w_gate, "w_gate"), _bf16_matrix(w_up, "w_up"), n, d_in, d_ff,
-                                  _dev(g_ref, "g_ref"), _dev(u_ref, "u_ref"), _stream(stream)))
+    dev = x.device
+    g_ref = torch.empty((n, d_ff), dtype=torch.float32, device=dev) if g_ref is None else g_ref
+    u_ref = torch.empty((n, d_ff), dtype=torch.float32, device=dev) if u_ref is None else u_ref
+    _check(lib.awq_mlp_hidden_ref(px, ld, _bf16_matrix(w_gate, "w_gate", (d_ff, d_in), dev),
+                                  _bf16_matrix(w_up, "w_up", (d_ff, d_in), dev), n, d_in, d_ff,
+                                  _buf(g_ref, "g_ref", torch.float32, n * d_ff, dev),
+                                  _buf(u_ref, "u_ref", torch.float32, n * d_ff, dev), _stream(stream)))
     return g_ref, u_ref
 
 
@@ -494,12 +576,17 @@ def awq_mlp_hidden_delta(x: torch.Tensor, dw_gate: torch.Tensor, dw_up: torch.Te
                          u_ref: torch.Tensor, act: int = AWQ_ACT_SILU, dh=None, stream=None):
     """dh = act(g) u - act(g + x dw_gate^T)(u + x dw_up^T), bfloat16 [n_tokens, d_ff]."""
     lib = load_library()
-    px, n, d_in, ld = _x_args(x)
+    px, n, d_in, ld = _x_bf16(x)
+    if not isinstance(dw_gate, torch.Tensor) or dw_gate.dim() != 2:
+        raise ValueError("dw_gate must be a [d_ff, d_in] matrix")
     d_ff = dw_gate.shape[0]
-    dh = torch.empty((n, d_ff), dtype=torch.bfloat16, device=x.device) if dh is None else dh
-    _check(lib.awq_mlp_hidden_delta(px, ld, _bf16_matrix(dw_gate, "dw_gate"), _bf16_matrix(dw_up, "dw_up"),
-                                    _dev(g_ref, "g_ref"), _dev(u_ref, "u_ref"), act, n, d_in, d_ff, _dev(dh, "dh"),
-                                    _stream(stream)))
+    dev = x.device
+    dh = torch.empty((n, d_ff), dtype=torch.bfloat16, device=dev) if dh is None else dh
+    _check(lib.awq_mlp_hidden_delta(px, ld, _bf16_matrix(dw_gate, "dw_gate", (d_ff, d_in), dev),
+                                    _bf16_matrix(dw_up, "dw_up", (d_ff, d_in), dev),
+                                    _buf(g_ref, "g_ref", torch.float32, n * d_ff, dev),
+                                    _buf(u_ref, "u_ref", torch.float32, n * d_ff, dev), act, n, d_in, d_ff,
+                                    _buf(dh, "dh", torch.bfloat16, n * d_ff, dev), _stream(stream)))
     return dh
 
 
@@ -514,27 +601,24 @@ def awq_search_scales_mlp(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Ten
     """The gate/up search scored at the gated MLP block's output. Device tensors: cand_scales, losses,
     best_scales, best_info."""
     lib = load_library()
-    px, n, d_in, ld = _x_args(x)
+    px, n, d_in, ld = _x_bf16(x)
+    if not isinstance(w_gate, torch.Tensor) or w_gate.dim() != 2 or not isinstance(w_down, torch.Tensor) \
+            or w_down.dim() != 2:
+        raise ValueError("w_gate and w_down must be matrices")
     d_ff, d_model = w_gate.shape[0], w_down.shape[0]
     cand_per_pass = cand_per_pass or n_grid
     dev = x.device
-    out = out or {}
-    cand = out.get("cand_scales")
-    cand = torch.empty((n_grid, d_in), dtype=torch.float64, device=dev) if cand is None else cand
-    losses = out.get("losses")
-    losses = torch.empty(n_grid, dtype=torch.float64, device=dev) if losses is None else losses
-    best = out.get("best_scales")
-    best = torch.empty(d_in, dtype=torch.float64, device=dev) if best is None else best
-    info = out.get("best_info")
-    info = torch.empty(2, dtype=torch.int32, device=dev) if info is None else info
+    pg = _bf16_matrix(w_gate, "w_gate", (d_ff, d_in), dev)
+    pu = _bf16_matrix(w_up, "w_up", (d_ff, d_in), dev)
+    pdn = _bf16_matrix(w_down, "w_down", (d_model, d_ff), dev)
+    pa = _buf(act_mean, "act_mean", torch.float64, d_in, dev)
+    res, (pc, pl, pb, pi) = _search_outputs(out, n_grid, d_in, dev)
     ws = _workspace(lib.awq_search_workspace_bytes_mlp(n, d_in, d_ff, d_model, n_grid, cand_per_pass), dev,
                     workspace)
-    _check(lib.awq_search_scales_mlp(px, ld, _bf16_matrix(w_gate, "w_gate"), _bf16_matrix(w_up, "w_up"),
-                                     _bf16_matrix(w_down, "w_down"), n, d_in, d_ff, d_model,
-                                     _dev(act_mean, "act_mean"), act, n_grid, cand_per_pass, cand.data_ptr(),
-                                     losses.data_ptr(), best.data_ptr(), info.data_ptr(), ws.data_ptr(),
-                                     ws.numel() * ws.element_size(), _stream(stream)))
-    return {"cand_scales": cand, "losses": losses, "best_scales": best, "best_info": info}
+    _check(lib.awq_search_scales_mlp(px, ld, pg, pu, pdn, n, d_in, d_ff, d_model, pa, act, n_grid, cand_per_pass,
+                                     pc, pl, pb, pi, ws.data_ptr(), ws.numel() * ws.element_size(),
+                                     _stream(stream)))
+    return res
 
 
 def awq_layer(x: torch.Tensor, w_parts, n_grid: int = 20, group_size: int = GROUP_SIZE,
