@@ -36,8 +36,9 @@ size_t esize(int dtype) { return dtype == AWQ_DTYPE_BF16 ? 2 : 4; }
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// byte offsets inside a 256-row tile are 32-bit in the error GEMM's buffer descriptors
-constexpr int64_t kMaxTileBytes = (int64_t)1 << 31;
+// byte offsets inside a 256-row tile, up to its end, are signed 32-bit in the error GEMM's
+// buffer descriptors
+constexpr int64_t kMaxTileBytes = ((int64_t)1 << 31) - 1;
 
 int check_dtype(int dtype) {
   if (dtype != AWQ_DTYPE_BF16 && dtype != AWQ_DTYPE_F32)
@@ -62,7 +63,7 @@ int check_x(const void* x, int dtype, int64_t n_tokens, int64_t d_in, int64_t ld
   if ((ld_x * (int64_t)esize(dtype)) % 16)
     return fail(AWQ_ERR_UNSUPPORTED, "ld_x * element size must be a multiple of 16 bytes");
   if (!aligned(x, 16)) return fail(AWQ_ERR_UNSUPPORTED, "x is not 16-byte aligned");
-  if ((int64_t)awq::kTileM * ld_x * (int64_t)esize(dtype) > kMaxTileBytes)
+  if (ld_x > kMaxTileBytes || (int64_t)awq::kTileM * ld_x * (int64_t)esize(dtype) > kMaxTileBytes)
     return fail(AWQ_ERR_UNSUPPORTED, "ld_x %lld too large for 32-bit tile offsets", (long long)ld_x);
   return AWQ_OK;
 }
@@ -102,7 +103,7 @@ int make_parts(const void* const* w_parts, const int64_t* part_rows, int n_parts
 }
 
 int check_d_in_bytes(int dtype, int64_t d_in) {
-  if ((int64_t)awq::kTileN * d_in * (int64_t)esize(dtype) > kMaxTileBytes)
+  if (d_in > kMaxTileBytes || (int64_t)awq::kTileN * d_in * (int64_t)esize(dtype) > kMaxTileBytes)
     return fail(AWQ_ERR_UNSUPPORTED, "d_in %lld too large for 32-bit tile offsets", (long long)d_in);
   if (d_in / AWQ_GROUP_SIZE > 65535) return fail(AWQ_ERR_UNSUPPORTED, "d_in %lld too large", (long long)d_in);
   return AWQ_OK;

@@ -99,6 +99,15 @@ def test_gemm_and_argmin_validation(lib):
     assert lib.awq_error_sse(FAKE, 256, FAKE, 1, 0, 256, 520, 4, FAKE, None) == 3
     assert lib.awq_error_sse(FAKE, 256, FAKE, 1, 600, 256, 0, 4, FAKE, None) == 2
     assert lib.awq_error_sse(FAKE, 256, FAKE, 1, 600, 256, 520, 0, FAKE, None) == 4
+    # a 256-row tile's byte offsets, to its end, must fit a signed 32-bit int: 256 rows of 2^22
+    # bf16 elements span exactly 2^31 bytes, one more than fits
+    assert lib.awq_error_sse(FAKE, 1 << 22, FAKE, 1, 600, 256, 520, 4, FAKE, None) == 5
+    assert "ld_x" in _err(lib)
+    assert lib.awq_error_sse(FAKE, 1 << 22, FAKE, 1, 600, 1 << 22, 520, 4, FAKE, None) == 5
+    assert "d_in" in _err(lib)
+    assert lib.awq_error_sse(FAKE, 1 << 22, FAKE, 1, 600, (1 << 22) - 128, 520, 4, FAKE, None) == 5  # ld_x
+    assert "ld_x" in _err(lib)
+    assert lib.awq_error_sse(FAKE, 1 << 62, FAKE, 1, 600, 256, 520, 4, FAKE, None) == 5  # no int64 overflow
     assert lib.awq_loss_argmin(FAKE, 9, 0, 600, 520, FAKE, 256, FAKE, FAKE, FAKE, None) == 4
     assert lib.awq_loss_argmin(None, 9, 4, 600, 520, FAKE, 256, FAKE, FAKE, FAKE, None) == 1
     assert lib.awq_candidate_scales(FAKE, 256, 0, FAKE, None) == 4
