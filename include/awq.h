@@ -72,7 +72,8 @@ typedef enum {
                               (msModelSlim FAQ, "No activation mean for target module") */
   AWQ_ERR_ARG = 4,         /* n_grid < 1, bad candidate range, ld_x < d_in, too many parts */
   AWQ_ERR_UNSUPPORTED = 5, /* unknown dtype, group_size != 128, misaligned pointer or pitch,
-                              or a size beyond the kernels' 32-bit tile offsets */
+                              or a size beyond the kernels' 32-bit tile offsets (256 rows of
+                              ld_x or d_in elements must span at most 2^31 - 1 bytes) */
   AWQ_ERR_WORKSPACE = 6,   /* workspace missing or smaller than the matching query returns */
   AWQ_ERR_HIP = 7          /* a HIP runtime call or kernel launch failed */
 } awq_status;

@@ -515,8 +515,13 @@ int awq_w4a16_gemm(const void* x, int64_t ld_x, int x_dtype, const uint8_t* code
   if (!aligned(codes, 16) || !aligned(steps_f16, 2))
     return fail(AWQ_ERR_UNSUPPORTED, "codes must be 16-byte and steps_f16 2-byte aligned");
   if (!aligned(y, y_dtype == AWQ_DTYPE_F32 ? 4 : 2)) return fail(AWQ_ERR_UNSUPPORTED, "y is not element-aligned");
-  if (n_tokens > 0x7FFFFFFF - 256 || d_out > 0x7FFFFFFF - 256 || d_in > 0x7FFFFFFF / 2)
+  if (n_tokens > 0x7FFFFFFF - 256 || d_out > 0x7FFFFFFF - 256)
     return fail(AWQ_ERR_UNSUPPORTED, "sizes beyond the kernels' 32-bit indices");
+  // the many-token kernel's activation offsets (128 tokens of ld_x) and per-wave code ranges (64
+  // rows of d_in / 2 bytes) are 32-bit: the GEMMs' 256-row tile bound covers both
+  TRY(check_d_in_bytes(AWQ_DTYPE_BF16, d_in));
+  if (ld_x > kMaxTileBytes || (int64_t)awq::kTileM * ld_x * 2 > kMaxTileBytes)
+    return fail(AWQ_ERR_UNSUPPORTED, "ld_x %lld too large for 32-bit tile offsets", (long long)ld_x);
   hipError_t e = awq::launch_w4a16_gemm(x, ld_x, x_dtype == AWQ_DTYPE_F16 ? 1 : 0, codes, steps_f16, zeros_u4,
                                         n_tokens, d_in, d_out, y, ld_y, y_dtype == AWQ_DTYPE_F32,
                                         (hipStream_t)stream);

@@ -255,6 +255,10 @@ def test_w4a16_validation(lib):
     assert call(a3=FAKE_ODD) == 5   # codes need 16-byte alignment
     assert call(a4=FAKE + 1) == 5
     assert call(a9=FAKE + 2) == 5   # f32 output needs 4-byte alignment
+    assert call(a1=1 << 22) == 5    # 128-token activation offsets beyond 32 bits
+    assert "ld_x" in _err(lib)
+    assert call(a1=1 << 22, a7=1 << 22) == 5
+    assert "d_in" in _err(lib)
 
 
 def test_mlp_block_validation(lib):
