@@ -78,6 +78,7 @@ def _want_bits(yref, out, operand):
     (1, 128, 16), (5, 384, 300), (16, 1152, 272), (17, 256, 40), (32, 640, 33),   # few-token kernel
     (33, 384, 300), (128, 256, 256), (300, 1152, 520), (129, 128, 17),            # many-token kernel,
     (600, 384, 300), (513, 128, 520),                                              # 16 or 64 rows per wave
+    (1024, 256, 300), (1300, 384, 520), (2049, 128, 17),                           # several token blocks
 ])
 def test_exact_arithmetic_bit_exact(B, operand, out, n_tokens, d_in, d_out):
     rng = np.random.default_rng(n_tokens * 1000 + d_in + d_out)
