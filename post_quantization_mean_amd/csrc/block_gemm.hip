@@ -227,20 +227,28 @@ void mlp_hidden_kernel(const uint16_t* __restrict__ x, int64_t ld_x, const uint1
           }
       __syncthreads();
       const bool is_gate = wn == 0;
+      // the reference values of accumulator group n + 1 are in flight while group n is computed
+      float gv[2][16], uv[2][16];
+      auto load_ref = [&](int n, int b) {
+        const int i = n >> 1, jj = n & 1;
+        const int64_t fc = min(f_w + 32 * (jj + 2 * wn) + fr, fmax);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int64_t t = min(tok_w + 32 * i + 8 * (e >> 2) + 4 * fh + (e & 3), tmax);
+          gv[b][e] = g_io[t * d_ff + fc];
+          uv[b][e] = u_io[t * d_ff + fc];
+        }
+      };
+      load_ref(0, 0);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
           const int n = i * 2 + jj;
+          if (n + 1 < FM * 2) load_ref(n + 1, (n + 1) & 1);
           const int64_t f = f_w + 32 * (jj + 2 * wn) + fr;
-          const int64_t fc = min(f, fmax);
-          float gv[16], uv[16];
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int64_t t = min(tok_w + 32 * i + 8 * (e >> 2) + 4 * fh + (e & 3), tmax);
-            gv[e] = g_io[t * d_ff + fc];
-            uv[e] = u_io[t * d_ff + fc];
-          }
+          const float (&gn)[16] = gv[n & 1];
+          const float (&un)[16] = uv[n & 1];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const f32x4 oth = *reinterpret_cast<const f32x4*>(take + ((n * 4 + q) * 64 + lane) * 4);
@@ -250,7 +258,7 @@ void mlp_hidden_kernel(const uint16_t* __restrict__ x, int64_t ld_x, const uint1
               const float own = acc[i][jj][e];
               const float eg = is_gate ? own : oth[r];
               const float eu = is_gate ? oth[r] : own;
-              const float d = act_f<ACT>(gv[e]) * uv[e] - act_f<ACT>(gv[e] + eg) * (uv[e] + eu);
+              const float d = act_f<ACT>(gn[e]) * un[e] - act_f<ACT>(gn[e] + eg) * (un[e] + eu);
               const int64_t t = tok_w + 32 * i + 8 * q + 4 * fh + r;
               if (t < n_tokens && f < d_ff) dh[t * d_ff + f] = (uint16_t)(pack_bf16x2(d, 0.f) & 0xFFFFu);
             }
