@@ -203,6 +203,30 @@ def test_repeat_runs_are_bitwise_identical(B):
         assert np.array_equal(a[key], b[key], equal_nan=True), key
 
 
+def test_side_stream_matches_default_stream(B):
+    # every entry point enqueues on the stream it is given (torch's current stream by default)
+    wl = custom_workload(700, 384, 520, "bf16", n_grid=6, config_id=110)
+    x, w, parts = _case(wl)
+    xt = to_torch(x, "cuda")
+    wp = _gpu_parts(w, parts)
+    torch.cuda.synchronize()
+    want = {k: v.cpu().numpy() for k, v in B.awq_layer(xt, wp, n_grid=6).items()}
+    side = torch.cuda.Stream()  # default priority
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        got = B.awq_layer(xt, wp, n_grid=6)
+    side.synchronize()
+    act = B.awq_act_stats(xt, stream=side)
+    res = B.awq_search_scales(xt, wp, act, 6, stream=side)
+    res.update(B.awq_quantize_pack(wp, res["best_scales"], stream=side))
+    side.synchronize()
+    for key in ("act_mean", "losses", "best_info", "best_scales", "codes", "qscales", "zeros"):
+        assert np.array_equal(got[key].cpu().numpy(), want[key], equal_nan=True), key
+        if key != "act_mean":
+            assert np.array_equal(res[key].cpu().numpy(), want[key], equal_nan=True), key
+    assert np.array_equal(act.cpu().numpy(), want["act_mean"])
+
+
 def test_host_side_errors_do_not_launch(B):
     wl = custom_workload(64, 128, 32, "bf16", n_grid=2, config_id=109)
     x, w, parts = _case(wl)
