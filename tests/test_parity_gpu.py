@@ -227,6 +227,29 @@ def test_side_stream_matches_default_stream(B):
     assert np.array_equal(act.cpu().numpy(), want["act_mean"])
 
 
+def test_concurrent_searches_on_two_streams(B):
+    # the library keeps no device state between calls: two layers searched at once on two streams
+    # (each with its own workspace) give what each gives alone
+    cases = []
+    for cid, (n, d_in, d_out) in ((111, (600, 256, 384)), (112, (900, 384, 260))):
+        wl = custom_workload(n, d_in, d_out, "bf16", n_grid=5, config_id=cid)
+        x, w, parts = _case(wl)
+        cases.append((to_torch(x, "cuda"), _gpu_parts(w, parts)))
+    alone = [{k: v.cpu().numpy() for k, v in B.awq_layer(xt, wp, n_grid=5).items()} for xt, wp in cases]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]  # default priority
+    outs = []
+    for (xt, wp), st in zip(cases, streams):
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            outs.append(B.awq_layer(xt, wp, n_grid=5))
+    for st in streams:
+        st.synchronize()
+    for got, want in zip(outs, alone):
+        for key in ("act_mean", "losses", "best_info", "codes", "qscales", "zeros"):
+            assert np.array_equal(got[key].cpu().numpy(), want[key], equal_nan=True), key
+
+
 def test_host_side_errors_do_not_launch(B):
     wl = custom_workload(64, 128, 32, "bf16", n_grid=2, config_id=109)
     x, w, parts = _case(wl)
