@@ -151,6 +151,7 @@ def main() -> int:
     ap.add_argument("--config", type=int, default=2, help="workload id (2 = 7B fused QKV, the headline)")
     ap.add_argument("--cand-per-pass", type=int, default=0, help="candidates per GEMM launch (0 = all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true", help="also time the step captured once as a HIP graph")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe", type=int, default=0, help="only run a device copy of this many bytes")
     ap.add_argument("--print-digest", action="store_true", help="print the error-GEMM source digest and exit")
@@ -262,6 +263,24 @@ def main() -> int:
     p_bytes = wl.d_out * wl.d_in * (esz + 0.5) + wl.d_out * G * 8 + wl.d_in * 8
     info_h = info.cpu().tolist()
     _log(f"k*={info_h[0]} flags={info_h[1]} ms/step={ms_step:.3f} gemm={gemm_ms:.3f} ms ({achieved:.1f} TFLOP/s)")
+
+    graph_rep = None
+    if args.graph:
+        # the same step captured once as a HIP graph (the library allocates, copies and synchronizes
+        # nothing, so the whole layer is capturable) and replayed: no per-launch host overhead
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(False)
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        g_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        graph_rep = {"ms_per_step": g_ms, "candidates_per_s": wl.n_grid / (g_ms * 1e-3)}
+        _log(f"graph replay: {g_ms:.3f} ms/step")
+        del g
 
     # HBM kernels on their own, after the timed steps: before every repetition a 1 GiB buffer is
     # overwritten so that the 256 MB memory-side cache holds none of the kernel's inputs; the median
@@ -445,6 +464,7 @@ def main() -> int:
                                     "random-init weights): whole search median of 3; per-launch kernels cache "
                                     "flushed, median of 5, TFLOP/s against 2500"),
         "best_k": info_h[0],
+        "graph": graph_rep,
     }
     if not args.no_cpu_baseline:
         _log("cpu baseline (oracle on a row sample)")

@@ -250,6 +250,31 @@ def test_concurrent_searches_on_two_streams(B):
             assert np.array_equal(got[key].cpu().numpy(), want[key], equal_nan=True), key
 
 
+def test_whole_layer_in_a_hip_graph(B):
+    # the library allocates nothing, issues no memset or copy and never synchronizes, so the whole
+    # layer can be captured once and replayed; every replay (new activations copied into the captured
+    # input, eager work and synchronizations in between) must equal an eager run on the same input
+    wl = custom_workload(640, 384, 520, "bf16", n_grid=6, outlier_channels=4, config_id=113)
+    x, w, parts = _case(wl)
+    wp = _gpu_parts(w, parts)
+    x_in = to_torch(x, "cuda").clone()
+    x_variants = [x_in.clone(), (x_in.float() * 0.5).to(torch.bfloat16), x_in.flip(0).contiguous()]
+    B.awq_layer(x_in, wp, n_grid=6)  # warm-up outside the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        captured = B.awq_layer(x_in, wp, n_grid=6)
+    for rep in range(2):
+        for xv in x_variants:
+            want = {k: v.cpu().numpy() for k, v in B.awq_layer(xv, wp, n_grid=6).items()}  # eager
+            x_in.copy_(xv)
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            for key in ("act_mean", "losses", "best_info", "best_scales", "codes", "qscales", "zeros"):
+                assert np.array_equal(captured[key].cpu().numpy(), want[key], equal_nan=True), (rep, key)
+
+
 def test_host_side_errors_do_not_launch(B):
     wl = custom_workload(64, 128, 32, "bf16", n_grid=2, config_id=109)
     x, w, parts = _case(wl)
