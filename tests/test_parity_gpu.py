@@ -18,7 +18,7 @@ def B():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     from post_quantization_mean_amd import binding
-    binding.load_library()  # must exist on a GPU machine: raises otherwise
+    binding.load_library()  # must be built wherever a GPU is present: raises otherwise
     return binding
 
 
