@@ -201,6 +201,47 @@ def search_scales(X, W, group_size: int = 128, n_grid: int = 20) -> SearchResult
     return SearchResult(a, ratios, scales, losses, k_best, scales[k_best].copy())
 
 
+def search_scales_blocked(X, W, group_size: int = 128, n_grid: int = 20,
+                          block: int = 4096) -> SearchResult:
+    """``search_scales`` with the calibration tokens taken ``block`` rows at a time, for layers
+    whose full output matrices do not fit in host memory at once. Same steps in the same
+    order (msModelSlim 缩放因子搜索流程): the statistic (a sum of |X| over the blocks, divided
+    once by the token count), the float reference ``X_b W^T`` of every block computed once and
+    kept across the ratios, then per ratio the candidate scales, ``What``, and the output
+    squared error summed block by block and divided by the number of outputs. Only the order
+    of float64 additions differs from ``search_scales``. ``X`` is any array whose row slices
+    convert to float64 (float32 holds bf16 values exactly)."""
+    W = np.asarray(W, dtype=np.float64)
+    n_tok, d_in = X.shape
+    if d_in != W.shape[1]:
+        raise ValueError("X and W disagree on d_in")
+    if n_tok == 0:
+        raise ValueError("no activation mean: zero calibration tokens")
+    bounds = [(r0, min(n_tok, r0 + block)) for r0 in range(0, n_tok, block)]
+    abs_sum = np.zeros(d_in)
+    targets = []
+    for r0, r1 in bounds:
+        xb = np.asarray(X[r0:r1], dtype=np.float64)
+        abs_sum += np.abs(xb).sum(axis=0)
+        targets.append(xb @ W.T)
+    a = abs_sum / n_tok
+    ratios = grid_ratios(n_grid)
+    scales = np.empty((len(ratios), d_in))
+    losses = np.empty(len(ratios))
+    n_out = n_tok * W.shape[0]
+    for k, r in enumerate(ratios):
+        s = candidate_scales(a, r)
+        W_hat_t = quantize_restore(W, s, group_size).T
+        sse = 0.0
+        for (r0, r1), target in zip(bounds, targets):
+            diff = target - np.asarray(X[r0:r1], dtype=np.float64) @ W_hat_t
+            sse += float(np.einsum("ij,ij->", diff, diff))
+        scales[k] = s
+        losses[k] = sse / n_out
+    k_best = select_best(losses)
+    return SearchResult(a, ratios, scales, losses, k_best, scales[k_best].copy())
+
+
 @dataclass
 class PackedQuant:
     codes: np.ndarray    # uint8 [d_out, d_in / 2]
@@ -218,9 +259,3 @@ def quantize_pack(W, s, group_size: int = 128) -> PackedQuant:
     qr = group_quantize(W * np.asarray(s, np.float64)[None, :], group_size)
     return PackedQuant(codes=pack_int4(qr.q), qscales=qr.scale, zeros=qr.zero.astype(np.int64),
                        q=qr.q, t=qr.t, zt=qr.zt)
-
-
-def awq_layer(X, W, group_size: int = 128, n_grid: int = 20):
-    """Search, then quantize and pack with the chosen scales."""
-    res = search_scales(X, W, group_size, n_grid)
-    return res, quantize_pack(W, res.best_scales, group_size)

@@ -93,18 +93,6 @@ def quantize_restore_row(Y, quantizer: int) -> np.ndarray:
     raise ValueError(quantizer)
 
 
-def row_decisions(Y, quantizer: int):
-    """The pre-rounding values t of the per-row quantizers (for tie bookkeeping)."""
-    Y = np.asarray(Y, dtype=np.float64)
-    if quantizer == QUANT_INT4_ROW:
-        step = (Y.max(axis=1, keepdims=True) - Y.min(axis=1, keepdims=True)) / 15.0
-        return Y / (step + 1e-6)
-    if quantizer == QUANT_INT8_ROW_SYM:
-        step = np.maximum(np.abs(Y).max(axis=1, keepdims=True) / 127.0, 1e-8)
-        return Y / step
-    raise ValueError(quantizer)
-
-
 def restore(W, s, quantizer: int, group_size: int = 128) -> np.ndarray:
     """What = dequant(quant(W * s)) / s for any quantizer."""
     from oracle import awq_oracle as O

@@ -306,3 +306,24 @@ def test_nonfinite_inputs_fall_back_to_unit_scales():
     assert np.all(np.isnan(res.scales[1:]))
     assert np.all(np.isnan(res.losses))
     assert res.best_k == 0 and np.all(res.best_scales == 1.0)
+
+
+def test_blocked_search_matches_gram_form_and_whole_search():
+    """The token-blocked search (used for the full-size layers' stored results) against the
+    Gram form and the whole search, with a ragged last block and float32 storage of X."""
+    rng = np.random.default_rng(13)
+    X = rng.standard_normal((300, 256)).astype(np.float32)
+    X[:, 9] *= 60.0
+    W = rng.standard_normal((40, 256)) * 0.02
+    res = O.search_scales_blocked(X, W, 128, 7, block=64)
+    whole = O.search_scales(X.astype(np.float64), W, 128, 7)
+    np.testing.assert_allclose(res.act_mean, whole.act_mean, rtol=1e-14)
+    np.testing.assert_array_equal(res.scales, whole.scales)
+    np.testing.assert_allclose(res.losses, whole.losses, rtol=1e-12)
+    assert res.best_k == whole.best_k
+    X64 = X.astype(np.float64)
+    G = X64.T @ X64
+    for k in range(7):
+        d = O.quantize_restore(W, res.scales[k], 128) - W
+        gram = float(np.einsum("oc,cd,od->", d, G, d)) / (X.shape[0] * W.shape[0])
+        assert math.isclose(res.losses[k], gram, rel_tol=1e-10)
