@@ -149,10 +149,11 @@ AWQ_API int awq_candidate_scales(const double* act_mean, int64_t d_in, int n_gri
  *   consecutive channels of a row, gsyq section 二), dequantize, divide by s, and write
  *   delta[j, o, c] = What[o, c] - W[o, c]   in dtype (bfloat16 rounds to nearest even).
  * Every quantizer decision (step, zero point, code) equals the float64 definition's; delta is
- * within 1.6e-5 * step / s of the float64 value before its rounding to dtype.
+ * within 1e-5 * step / s of the float64 value before its rounding to dtype (float32 evaluation:
+ * 8.6e-6 * step from the residual, plus the two float32 roundings of the unscaling).
  *   w_parts    host array of n_parts device pointers; part p is [part_rows[p], d_in] of dtype.
  *   part_rows  host array of n_parts row counts (d_out = their sum).
- *   cand_scales device, float64 [n_cand, d_in].
+ *   cand_scales device, float64 [n_cand, d_in], 16-byte aligned (AWQ_ERR_UNSUPPORTED otherwise).
  *   delta      device, [n_cand, d_out, d_in] of dtype, written. */
 AWQ_API int awq_quant_delta(const void* const* w_parts, const int64_t* part_rows, int n_parts, int dtype,
                     int64_t d_in, int group_size, const double* cand_scales, int n_cand,
@@ -202,7 +203,7 @@ AWQ_API size_t awq_search_workspace_bytes(int dtype, int64_t n_tokens, int64_t d
  * cand_per_pass candidates, then a5 (msModelSlim 缩放因子搜索流程, in that order).
  *   x, ld_x, w_parts, part_rows, n_parts, dtype: as above.
  *   act_mean    device, float64 [d_in] (from awq_act_stats).
- *   cand_scales device, float64 [n_grid, d_in], written (all candidates).
+ *   cand_scales device, float64 [n_grid, d_in], 16-byte aligned, written (all candidates).
  *   losses, best_scales, best_info: as awq_loss_argmin.
  *   workspace   device, >= awq_search_workspace_bytes(...) bytes. */
 AWQ_API int awq_search_scales(const void* x, int64_t ld_x, const void* const* w_parts,
@@ -222,7 +223,7 @@ AWQ_API int awq_search_scales(const void* x, int64_t ld_x, const void* const* w_
  *                    saturated to the int32 range),
  * so that W*s ~= (q - zero) * step. s is usually best_scales from the search; the caller
  * divides the layer input by s (folds diag(s)^-1 into the previous op, gsyq section 四).
- *   s  device, float64 [d_in]. */
+ *   s  device, float64 [d_in], 16-byte aligned (AWQ_ERR_UNSUPPORTED otherwise). */
 AWQ_API int awq_quantize_pack(const void* const* w_parts, const int64_t* part_rows, int n_parts, int dtype,
                       int64_t d_in, int group_size, const double* s, uint8_t* codes,
                       float* qscales, int32_t* zeros, void* stream);

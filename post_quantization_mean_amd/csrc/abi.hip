@@ -153,6 +153,7 @@ int run_search(const void* x, int64_t ld_x, const void* const* w_parts, const in
   const int64_t d_out = w.row_begin[w.n];
   if (!act_mean || !cand_scales || !losses || !best_scales || !best_info)
     return fail(AWQ_ERR_NULL, "a required pointer is NULL");
+  if (!aligned(cand_scales, 16)) return fail(AWQ_ERR_UNSUPPORTED, "cand_scales is not 16-byte aligned");
   awq::RatioList rl;
   if (ratios) {
     TRY(check_ratios(ratios, n_grid, formula, w_mean, &rl));
@@ -275,6 +276,8 @@ int awq_quant_delta(const void* const* w_parts, const int64_t* part_rows, int n_
   if (!cand_scales || !delta) return fail(AWQ_ERR_NULL, "cand_scales or delta is NULL");
   if (n_cand < 1) return fail(AWQ_ERR_ARG, "n_cand %d < 1", n_cand);
   if (!aligned(delta, 16)) return fail(AWQ_ERR_UNSUPPORTED, "delta is not 16-byte aligned");
+  // the kernel reads the scales two float64 at a time
+  if (!aligned(cand_scales, 16)) return fail(AWQ_ERR_UNSUPPORTED, "cand_scales is not 16-byte aligned");
   hipError_t e = awq::launch_quant_delta(w, dtype, d_in, cand_scales, n_cand, delta, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "quant_delta launch");
   return ok();
@@ -352,6 +355,8 @@ int awq_quantize_pack(const void* const* w_parts, const int64_t* part_rows, int 
   if (!s || !codes || !qscales || !zeros) return fail(AWQ_ERR_NULL, "s, codes, qscales or zeros is NULL");
   if (!aligned(codes, 16) || !aligned(qscales, 4) || !aligned(zeros, 4))
     return fail(AWQ_ERR_UNSUPPORTED, "codes must be 16-byte aligned, qscales and zeros 4-byte aligned");
+  // the kernel reads s two float64 at a time
+  if (!aligned(s, 16)) return fail(AWQ_ERR_UNSUPPORTED, "s is not 16-byte aligned");
   hipError_t e = awq::launch_quantize_pack(w, dtype, d_in, s, codes, qscales, zeros, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "quantize_pack launch");
   return ok();
@@ -583,6 +588,7 @@ int awq_search_scales_mlp(const void* x, int64_t ld_x, const void* w_gate, const
     return fail(AWQ_ERR_NULL, "a required pointer is NULL");
   if (!aligned(w_gate, 16) || !aligned(w_up, 16) || !aligned(w_down, 16))
     return fail(AWQ_ERR_UNSUPPORTED, "weights must be 16-byte aligned");
+  if (!aligned(cand_scales, 16)) return fail(AWQ_ERR_UNSUPPORTED, "cand_scales is not 16-byte aligned");
   if (d_ff > ((int64_t)65535 * 128) / 2) return fail(AWQ_ERR_UNSUPPORTED, "d_ff %lld too large", (long long)d_ff);
   if (n_grid < 1 || n_grid > 65535) return fail(AWQ_ERR_ARG, "n_grid %d outside [1, 65535]", n_grid);
   if (cand_per_pass < 1 || cand_per_pass > n_grid)

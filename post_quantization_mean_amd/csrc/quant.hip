@@ -23,8 +23,9 @@
 // the same way. A group that fails a check (a value within 2^-16 of a rounding tie, a zero point
 // outside [-0.5, 15.5], a step near the 1e-8 floor, a non-finite value) is recomputed by the
 // whole wave in float64 with exact divisions, as the definition is written. The float32 delta
-// is within 1e-5 * step / s of the float64 value (below the bfloat16 rounding of delta for all
-// but the smallest elements).
+// -e * (-1/s) is within 1e-5 * step / s of the float64 value: 8.6e-6 * step / s from e (bound at
+// kGuard32) plus two float32 roundings (of -1/s and of the product) on |e| / s <= step / (2 s).
+// That is below the bfloat16 rounding of delta for all but the smallest elements.
 //
 // quantize_pack (the final export, one scale vector) uses the same layout, float32 fast path and
 // proof: its codes are r + zero, and flagged groups are redone by the whole wave in float64.

@@ -212,25 +212,28 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_big_kernel(const uint16_t* 
   const int row0 = blockIdx.x * (4 * kRowsPerWave) + wave * kRowsPerWave;
 
   // activations: wave w fills LDS chunks p = 512 w + 64 j + lane (token p / 16, slot p % 16) with
-  // the global chunk (p % 16) ^ (token % 16) of that token's 256-byte group slice; the chunk pattern
-  // repeats every 4 instructions (16 tokens), so 4 offsets and a scalar token step cover all 8
+  // the global chunk (p % 16) ^ (token % 16) of that token's 256-byte group slice. The buffer range
+  // check covers the per-lane offset only, not the scalar one, so the token's row offset is in the
+  // per-lane offset (a token past the end then reads zero) and the scalar offset holds only the group's
+  // position inside the row (g * 256 + 16 <= d_in * 2 <= ld_x * 2, so a valid token stays in its row).
   const int valid_tok = min(kBigTokens, n_tokens - tok0);
   const i32x4 xr = make_rsrc(x + (int64_t)tok0 * ld_x, (uint32_t)valid_tok * (uint32_t)ld_x * 2u);
-  int xoff[4];
+  int xoff[8];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int tr = 32 * wave + 4 * j + (lane >> 4);
+  for (int j = 0; j < 8; ++j) {
+    const int tr = 32 * wave + 16 * (j >> 2) + 4 * (j & 3) + (lane >> 4);
     xoff[j] = tr * (int)ld_x * 2 + (((lane & 15) ^ (tr & 15)) * 16);
   }
-  const int x16 = 16 * (int)ld_x * 2;  // 16 tokens further
   auto load_x = [&](int g, int buf) {
     const uint32_t base = lds_address(&xs[buf][512 * wave]);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) dma_load16(xr, base + 1024 * j, xoff[j & 3], (j >> 2) * x16 + g * (kGroup * 2));
+    for (int j = 0; j < 8; ++j) dma_load16(xr, base + 1024 * j, xoff[j], g * (kGroup * 2));
   };
-  // codes, steps and zero points of the wave's 64 rows through buffer descriptors whose range ends at
-  // the last valid row (rows past it read zero; their results are not stored). Lane (n, kq) holds the
-  // 32 codes k = 32 kq .. 32 kq + 31 of group g of row row0 + 16 j + n.
+  // codes, steps and zero points of the wave's rows through buffer descriptors whose range ends at
+  // the last valid row; rows past it read zero and their results are not stored. Lane (n, kq) holds
+  // the 32 codes k = 32 kq .. 32 kq + 31 of group g of row row0 + 16 j + n. As for the activations,
+  // the row (16 j + n) is in the per-lane offset, which the range check covers, and the scalar offset
+  // holds only the group's position inside the row.
   const int vrows = max(0, min(kRowsPerWave, d_out - row0));
   const int64_t r0 = min(row0, d_out - 1);
   const __amdgpu_buffer_rsrc_t cr =
@@ -246,9 +249,9 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_big_kernel(const uint16_t* 
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       cw[set][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                 cr, c_off, 16 * j * (d_in / 2) + g * (kGroup / 2), 0));
-      sr[set][j] = __builtin_amdgcn_raw_buffer_load_b16(sres, s_off, 16 * j * G * 2 + g * 2, 0);
-      zr[set][j] = __builtin_amdgcn_raw_buffer_load_b8(zres, z_off, 16 * j * GZ + (g >> 1), 0);
+                                                 cr, c_off + 16 * j * (d_in / 2), g * (kGroup / 2), 0));
+      sr[set][j] = __builtin_amdgcn_raw_buffer_load_b16(sres, s_off + 16 * j * G * 2, g * 2, 0);
+      zr[set][j] = __builtin_amdgcn_raw_buffer_load_b8(zres, z_off + 16 * j * GZ, g >> 1, 0);
     }
   };
 

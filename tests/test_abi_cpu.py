@@ -89,6 +89,11 @@ def test_quant_and_pack_validation(lib):
     assert lib.awq_quantize_pack(p, r, 2, 1, 256, 128, None, FAKE, FAKE, FAKE, None) == 1
     assert lib.awq_quantize_pack(p, r, 2, 2, 256, 128, FAKE, FAKE, FAKE, FAKE, None) == 5
     assert lib.awq_quantize_pack(p, r, 2, 1, 256, 128, FAKE, FAKE + 4, FAKE, FAKE, None) == 5
+    # the scale vectors are read two float64 at a time: 8-byte alignment is refused
+    assert lib.awq_quant_delta(p, r, 2, 1, 256, 128, FAKE_ODD, 3, FAKE, None) == 5
+    assert "cand_scales" in _err(lib)
+    assert lib.awq_quantize_pack(p, r, 2, 1, 256, 128, FAKE_ODD, FAKE, FAKE, FAKE, None) == 5
+    assert "s is not 16-byte aligned" in _err(lib)
 
 
 def test_gemm_and_argmin_validation(lib):
@@ -142,6 +147,8 @@ def test_search_workspace_and_validation(lib):
     assert call(bi=None) == 1
     assert call(g=32) == 5
     assert call(ws=FAKE_ODD) == 5
+    assert call(cs=FAKE_ODD) == 5
+    assert "cand_scales" in _err(lib)
 
 
 def test_accumulate_finalize_validation(lib):
@@ -291,4 +298,6 @@ def test_mlp_block_validation(lib):
     assert call(a11=0) == 4
     assert call(a18=ws - 8) == 6
     assert call(a17=FAKE + 16) == 5
+    assert call(a13=FAKE_ODD) == 5   # cand_scales
+    assert "cand_scales" in _err(lib)
     assert call(a5=0) == 3
