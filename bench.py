@@ -9,6 +9,12 @@ Prints one JSON line. `value` = candidate evaluations per second for the whole l
 (n_grid / seconds per step). `roofline` is for the error GEMM (the dominant kernel), timed with
 HIP events on the stream it runs on. `cpu_baseline` times the CPU oracle on a bounded row sample
 of the same layer and scales it to the whole layer.
+
+The default workload is the largest single-GPU layer, the 70B down_proj stress layer (X 65536 x
+28672 bf16, W 8192 x 28672, n_grid 40); `--config N` selects another. The only error-GEMM launches
+of a default run are the timed steps' (and the warm-up's), so a kernel trace of the same command
+averages exactly those launches; `--variant-searches` adds whole searches with the other pages'
+formula / grid / quantizer pairings.
 """
 from __future__ import annotations
 
@@ -148,10 +154,13 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--config", type=int, default=2, help="workload id (2 = 7B fused QKV, the headline)")
+    ap.add_argument("--config", type=int, default=5,
+                    help="workload id (5 = 70B down_proj stress, the largest single-GPU layer)")
     ap.add_argument("--cand-per-pass", type=int, default=0, help="candidates per GEMM launch (0 = all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="also time the step captured once as a HIP graph")
+    ap.add_argument("--variant-searches", action="store_true",
+                    help="also time whole searches with the other pages' formula/grid/quantizer pairings")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe", type=int, default=0, help="only run a device copy of this many bytes")
     ap.add_argument("--print-digest", action="store_true", help="print the error-GEMM source digest and exit")
@@ -395,13 +404,14 @@ def main() -> int:
                 "quant_delta_int4_row": q_bytes / (var_ms["quant_delta_int4_row"] * 1e-3) / 1e9,
                 "quant_delta_int8_row_sym": q_bytes / (var_ms["quant_delta_int8_row_sym"] * 1e-3) / 1e9}
     ws_s = torch.empty(B.awq_search_workspace_bytes(dt, wl.n_tokens, wl.d_in, wl.d_out, 128, 20,
-                                                    min(cpp, 20)), dtype=torch.uint8, device=dev)
+                                                    min(cpp, 20)) if args.variant_searches else 0,
+                       dtype=torch.uint8, device=dev)
     pairings = {"duo/linspace20/int4_row": (B.AWQ_FORMULA_DUO, [k / 19 for k in range(20)], B.AWQ_QUANT_INT4_ROW),
                 "rms/tenths/int4_group": (B.AWQ_FORMULA_RMS, [k / 10 for k in range(11)], B.AWQ_QUANT_INT4_GROUP),
                 "msmodelslim/ms20/int8_row_sym": (B.AWQ_FORMULA_MSMODELSLIM, [k / 20 for k in range(20)],
                                                   B.AWQ_QUANT_INT8_ROW_SYM)}
     search_ms = {}
-    for name, (formula, ratios, quantizer) in pairings.items():
+    for name, (formula, ratios, quantizer) in (pairings.items() if args.variant_searches else ()):
         c = min(cpp, len(ratios))
         fn = lambda: B.awq_search_scales_ex(x, w_parts, act, ratios, formula, quantizer, w_mean=wm,
                                             cand_per_pass=c, workspace=ws_s)

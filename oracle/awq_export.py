@@ -27,6 +27,16 @@ Readings taken where the pages are silent:
   its bias) is divided by s[c]. The quotient is formed in float64, rounded to float32 and then to
   the storage dtype (round to nearest even at each step), as a float32 computation stored in the
   model's dtype would round it.
+* Output-value subgraph with grouped KV heads (MQA, GQA; MHA is the case of one query head per KV
+  head): o_proj input channel (h, d) (query head h, head dimension d, channel h * head_dim + d) is
+  the attention output of head h, a mix of the value rows of KV head h // g with
+  g = n_heads / n_kv_heads (consecutive query heads share a KV head). Dividing v_proj output row
+  (kv, d) by t scales every channel (h, d) with h // g = kv by 1 / t, so the forward scales of
+  o_proj must be tied across the g query heads of a group: s[(h, d)] = t[(h // g, d)]. The search
+  then runs on a tied statistic: channel (h, d) takes the mean, over the g query heads of its group
+  in head order, of the per-channel means of |X| (the mean of |X| over all the entries one v_proj
+  scale reaches); the candidate formula applied to it gives tied scales, and v_proj row (kv, d) is
+  folded with the scale of channel (kv * g, d).
 * Deployment form: each float32 step rounded to float16 (nearest even); zero points packed two per
   byte along the groups of a row, even group in the low nibble, clipped to [0, 15] (a zero point
   outside that range — only one-signed groups have one — is counted, since the packed form cannot
@@ -114,3 +124,49 @@ def export_fp16(qscales_f32, zeros):
     if g > 1:
         packed[:, : g // 2] |= (zc[:, 1::2].astype(np.uint8) << 4)
     return hb, packed, int(bad_zero.sum()), int(bad_step.sum())
+
+
+def _head_groups(n_heads: int, n_kv_heads: int, head_dim: int) -> int:
+    if n_heads < 1 or n_kv_heads < 1 or head_dim < 1 or n_heads % n_kv_heads:
+        raise ValueError("n_heads must be a positive multiple of n_kv_heads")
+    return n_heads // n_kv_heads
+
+
+def tie_heads(act_mean, n_heads: int, n_kv_heads: int, head_dim: int) -> np.ndarray:
+    """Statistic of the o_proj input channels with each channel (h, d) replaced by the mean over
+    the query heads sharing its KV head (msModelSlim 支持的子图类型, OVSubgraph: MHA, MQA, GQA;
+    o_proj forward scaling, v_proj inverse). Sum in head order, divided once by the group size."""
+    g = _head_groups(n_heads, n_kv_heads, head_dim)
+    a = np.asarray(act_mean, dtype=np.float64)
+    if a.shape != (n_heads * head_dim,):
+        raise ValueError("act_mean must have n_heads * head_dim channels")
+    a = a.reshape(n_kv_heads, g, head_dim)
+    tot = a[:, 0, :].copy()
+    for j in range(1, g):
+        tot = tot + a[:, j, :]
+    mean = tot / g
+    return np.repeat(mean[:, None, :], g, axis=1).reshape(-1)
+
+
+def head_group_scales(s, n_heads: int, n_kv_heads: int, head_dim: int) -> np.ndarray:
+    """Scales of the v_proj output rows: row (kv, d) takes o_proj channel (kv * g, d), the first
+    query head of its group (all heads of a group carry the same tied scale)."""
+    g = _head_groups(n_heads, n_kv_heads, head_dim)
+    s = np.asarray(s, dtype=np.float64)
+    if s.shape != (n_heads * head_dim,):
+        raise ValueError("s must have n_heads * head_dim channels")
+    return s.reshape(n_kv_heads, g, head_dim)[:, 0, :].reshape(-1).copy()
+
+
+def search_scales_tied(X, W, n_heads: int, n_kv_heads: int, head_dim: int, group_size: int = 128,
+                       n_grid: int = 20):
+    """The main search (msModelSlim 缩放因子搜索流程) on o_proj with the tied statistic: the
+    candidate scales come from ``tie_heads(act_mean(X))``; quantizer, loss and choice unchanged."""
+    from oracle import awq_oracle as O
+    X = np.asarray(X, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    a = tie_heads(O.act_mean(X), n_heads, n_kv_heads, head_dim)
+    scales = np.stack([O.candidate_scales(a, r) for r in O.grid_ratios(n_grid)])
+    losses = np.array([O.output_mse(X, W, O.quantize_restore(W, sk, group_size)) for sk in scales])
+    k = O.select_best(losses)
+    return O.SearchResult(a, O.grid_ratios(n_grid), scales, losses, k, scales[k].copy())
