@@ -58,7 +58,7 @@ extern "C" {
 #define AWQ_API
 #endif
 
-#define AWQ_ABI_VERSION 3
+#define AWQ_ABI_VERSION 4
 #define AWQ_MAX_PARTS 8
 #define AWQ_GROUP_SIZE 128
 #define AWQ_MAX_RATIOS 64
@@ -255,6 +255,31 @@ AWQ_API int awq_act_stats_finalize(const double* sums, int64_t d_in, int64_t tot
  *   s         device, float64 [rows] (usually best_scales). */
 AWQ_API int awq_fold_scales(const void* src, int64_t ld_src, int dtype, int64_t rows, int64_t cols,
                     const double* s, void* dst, int64_t ld_dst, void* stream);
+
+/* Output-value subgraph with grouped KV heads (msModelSlim 支持的子图类型, OVSubgraph: MHA, MQA and
+ * GQA; o_proj gets the forward scaling, v_proj the inverse). o_proj input channel h * head_dim + d
+ * is the attention output of query head h, which mixes the value rows of KV head h / g
+ * (g = n_heads / n_kv_heads; consecutive query heads share a KV head). Dividing v_proj row
+ * kv * head_dim + d by one scale therefore reaches the g channels (kv * g + j) * head_dim + d,
+ * j < g, and the o_proj scales must be equal across them. The search runs on a tied statistic:
+ *   tied[(kv * g + j) * head_dim + d] = (sum over j' < g, in order, of
+ *                                        act_mean[(kv * g + j') * head_dim + d]) / g   (float64)
+ * for every j < g. Passed to awq_search_scales as its act_mean, it gives tied candidate scales
+ * (the formula is per channel, and the normaliser's max and min are unchanged by repeating values).
+ *   act_mean, tied  device, float64 [n_heads * head_dim]; tied may equal act_mean.
+ * n_heads must be a positive multiple of n_kv_heads (AWQ_ERR_SHAPE); MHA (n_kv_heads == n_heads)
+ * copies act_mean. */
+AWQ_API int awq_tie_heads(const double* act_mean, int64_t n_heads, int64_t n_kv_heads, int64_t head_dim,
+                          double* tied, void* stream);
+
+/* The v_proj side of the same fold: s_kv[kv * head_dim + d] = s[(kv * g) * head_dim + d], the tied
+ * o_proj scale of the group's first query head (all g are equal after awq_tie_heads); then
+ * awq_fold_scales(v_proj weight [n_kv_heads * head_dim, d_model] (and its bias), s_kv) divides each
+ * v_proj row by its scale.
+ *   s     device, float64 [n_heads * head_dim] (usually best_scales of the tied search).
+ *   s_kv  device, float64 [n_kv_heads * head_dim], written. */
+AWQ_API int awq_head_group_scales(const double* s, int64_t n_heads, int64_t n_kv_heads, int64_t head_dim,
+                                  double* s_kv, void* stream);
 
 /* Deployment form of an export from awq_quantize_pack (bjdmk "GPU 硬件级反量化算子内联融合":
  * FP16 per-group scales, 4-bit values two per byte), for [rows, n_groups] qscales / zeros:

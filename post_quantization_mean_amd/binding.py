@@ -53,6 +53,8 @@ _SIGNATURES = {
     "awq_act_stats_finalize": (_c_int, [_vp, _c_i64, _c_i64, _vp, _vp]),
     "awq_fold_scales": (_c_int, [_vp, _c_i64, _c_int, _c_i64, _c_i64, _vp, _vp, _c_i64, _vp]),
     "awq_export_fp16": (_c_int, [_vp, _vp, _c_i64, _c_i64, _vp, _vp, _vp, _vp]),
+    "awq_tie_heads": (_c_int, [_vp, _c_i64, _c_i64, _c_i64, _vp, _vp]),
+    "awq_head_group_scales": (_c_int, [_vp, _c_i64, _c_i64, _c_i64, _vp, _vp]),
     "awq_weight_mean": (_c_int, [_vp, _vp, _c_int, _c_int, _c_i64, _vp, _vp, _c_size, _vp]),
     "awq_candidate_scales_ex": (_c_int, [_vp, _vp, _c_i64, _vp, _c_int, _c_int, _vp, _vp]),
     "awq_quant_delta_ex": (_c_int, [_vp, _vp, _c_int, _c_int, _c_i64, _c_int, _vp, _c_int, _vp, _vp]),
@@ -397,6 +399,31 @@ def awq_fold_scales(src: torch.Tensor, s: torch.Tensor, dst=None, stream=None):
                                cols, _buf(s, "s", torch.float64, rows, src.device), _dev(dst2, "dst"),
                                dst2.stride(0) if rows > 1 else cols, _stream(stream)))
     return dst
+
+
+def awq_tie_heads(act_mean: torch.Tensor, n_heads: int, n_kv_heads: int, head_dim: int, out=None, stream=None):
+    """Statistic of the o_proj input channels tied across the query heads that share a KV head
+    (float64 [n_heads * head_dim]); `out` may be act_mean."""
+    lib = load_library()
+    n = n_heads * head_dim
+    a = _buf(act_mean, "act_mean", torch.float64, n)
+    if out is None:
+        out = torch.empty(n, dtype=torch.float64, device=act_mean.device)
+    _check(lib.awq_tie_heads(a, n_heads, n_kv_heads, head_dim, _buf(out, "out", torch.float64, n, act_mean.device),
+                             _stream(stream)))
+    return out
+
+
+def awq_head_group_scales(s: torch.Tensor, n_heads: int, n_kv_heads: int, head_dim: int, out=None, stream=None):
+    """The v_proj row scales (float64 [n_kv_heads * head_dim]) of tied o_proj scales s."""
+    lib = load_library()
+    p = _buf(s, "s", torch.float64, n_heads * head_dim)
+    if out is None:
+        out = torch.empty(n_kv_heads * head_dim, dtype=torch.float64, device=s.device)
+    _check(lib.awq_head_group_scales(p, n_heads, n_kv_heads, head_dim,
+                                     _buf(out, "out", torch.float64, n_kv_heads * head_dim, s.device),
+                                     _stream(stream)))
+    return out
 
 
 def awq_export_fp16(qscales: torch.Tensor, zeros: torch.Tensor, out=None, stream=None) -> dict:

@@ -410,6 +410,38 @@ int awq_fold_scales(const void* src, int64_t ld_src, int dtype, int64_t rows, in
   return ok();
 }
 
+namespace {
+int check_heads(int64_t n_heads, int64_t n_kv_heads, int64_t head_dim) {
+  if (n_heads <= 0 || n_kv_heads <= 0 || head_dim <= 0)
+    return fail(AWQ_ERR_SHAPE, "n_heads %lld, n_kv_heads %lld and head_dim %lld must be > 0", (long long)n_heads,
+                (long long)n_kv_heads, (long long)head_dim);
+  if (n_heads % n_kv_heads)
+    return fail(AWQ_ERR_SHAPE, "n_heads %lld is not a multiple of n_kv_heads %lld", (long long)n_heads,
+                (long long)n_kv_heads);
+  if (n_heads > (1 << 20) || head_dim > (1 << 20) || n_heads * head_dim > ((int64_t)1 << 31))
+    return fail(AWQ_ERR_UNSUPPORTED, "n_heads * head_dim too large");
+  return AWQ_OK;
+}
+}  // namespace
+
+int awq_tie_heads(const double* act_mean, int64_t n_heads, int64_t n_kv_heads, int64_t head_dim, double* tied,
+                  void* stream) {
+  if (!act_mean || !tied) return fail(AWQ_ERR_NULL, "act_mean or tied is NULL");
+  TRY(check_heads(n_heads, n_kv_heads, head_dim));
+  hipError_t e = awq::launch_tie_heads(act_mean, n_heads, n_kv_heads, head_dim, tied, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "tie_heads launch");
+  return ok();
+}
+
+int awq_head_group_scales(const double* s, int64_t n_heads, int64_t n_kv_heads, int64_t head_dim, double* s_kv,
+                          void* stream) {
+  if (!s || !s_kv) return fail(AWQ_ERR_NULL, "s or s_kv is NULL");
+  TRY(check_heads(n_heads, n_kv_heads, head_dim));
+  hipError_t e = awq::launch_head_group_scales(s, n_heads, n_kv_heads, head_dim, s_kv, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "head_group_scales launch");
+  return ok();
+}
+
 int awq_export_fp16(const float* qscales, const int32_t* zeros, int64_t rows, int64_t n_groups, uint16_t* steps_f16,
                     uint8_t* zeros_u4, int32_t* counts, void* stream) {
   if (!qscales || !zeros || !steps_f16 || !zeros_u4 || !counts)

@@ -6,7 +6,10 @@
 // v_proj, up_proj) so that X W^T = (X diag(s)^-1)(W diag(s))^T needs no extra operator
 // (gsyq.cn "AWQ 离群激活平滑实操", section 四). Row r of the source (the norm weight, or row r of
 // the source linear's weight or bias) is divided by s[r]; the quotient is float64, rounded to
-// float32 and then to the storage dtype, both to nearest even.
+// float32 and then to the storage dtype, both to nearest even. The output-value subgraph with
+// grouped KV heads (MQA, GQA: msModelSlim 支持的子图类型, OVSubgraph) ties the o_proj scales across
+// the query heads that share a KV head (tie_heads_kernel on the statistic) and folds v_proj row
+// (kv, d) with the scale of o_proj channel (kv * g, d) (head_group_scales_kernel).
 //
 // Deployment form: float16 per-group scales and 4-bit values two per byte (bjdmk.com.cn AWQ
 // article, section "GPU 硬件级反量化算子内联融合"): steps rounded to float16, zero points clipped
@@ -22,7 +25,25 @@ namespace {
 
 constexpr int kThreads = 256;
 
-__device__ __forceinline__ float fold1(float v, double s) { return (float)((double)v / s); }
+// v / s correctly rounded in float64, then rounded to float32. rs is the correctly rounded 1/s (one
+// exact division per row), and a row flag `fast` says that s is a positive normal number in
+// [2^-500, 2^500]. For a finite non-zero v the product q = v * rs, its exact residual
+// r = v - q * s (one fma) and the fused correction q + r * rs give the correctly rounded quotient
+// (Markstein's theorem on division by multiplication with a correctly rounded reciprocal; with
+// |v| in the float32 range and s in that range nothing under- or overflows). Zeros, infinities and
+// NaN (and rows whose s is outside the range) take the exact division, which also keeps the sign
+// of a zero.
+__device__ __forceinline__ float fold1(float v, double s, double rs, bool fast) {
+  const double a = (double)v;
+  if (fast && a != 0.0 && __builtin_isfinite(a)) {
+    const double q = a * rs;
+    const double r = fma(-q, s, a);
+    return (float)fma(r, rs, q);
+  }
+  return (float)(a / s);
+}
+
+__device__ __forceinline__ bool fold_fast_row(double s) { return s >= 0x1p-500 && s <= 0x1p500; }
 
 // 8 consecutive elements of one row per thread (16-byte aligned rows, cols % 8 == 0).
 template <typename T>
@@ -34,6 +55,8 @@ __global__ __launch_bounds__(kThreads) void fold_vec_kernel(const T* __restrict_
   if (j >= cols8 * 8) return;
   for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
     const double sr = s[r];
+    const bool fast = fold_fast_row(sr);
+    const double rs = 1.0 / sr;
     const T* p = src + r * ld_src + j;
     T* q = dst + r * ld_dst + j;
     if constexpr (sizeof(T) == 2) {
@@ -42,13 +65,16 @@ __global__ __launch_bounds__(kThreads) void fold_vec_kernel(const T* __restrict_
       uint32_t o[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k)
-        o[k] = pack_bf16x2(fold1(bf16_to_f32(w[k] & 0xFFFFu), sr), fold1(bf16_to_f32(w[k] >> 16), sr));
+        o[k] = pack_bf16x2(fold1(bf16_to_f32(w[k] & 0xFFFFu), sr, rs, fast),
+                           fold1(bf16_to_f32(w[k] >> 16), sr, rs, fast));
       *reinterpret_cast<uint4*>(q) = make_uint4(o[0], o[1], o[2], o[3]);
     } else {
       const f32x4 a = *reinterpret_cast<const f32x4*>(p);
       const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
-      const f32x4 oa = {fold1(a.x, sr), fold1(a.y, sr), fold1(a.z, sr), fold1(a.w, sr)};
-      const f32x4 ob = {fold1(b.x, sr), fold1(b.y, sr), fold1(b.z, sr), fold1(b.w, sr)};
+      const f32x4 oa = {fold1(a.x, sr, rs, fast), fold1(a.y, sr, rs, fast), fold1(a.z, sr, rs, fast),
+                        fold1(a.w, sr, rs, fast)};
+      const f32x4 ob = {fold1(b.x, sr, rs, fast), fold1(b.y, sr, rs, fast), fold1(b.z, sr, rs, fast),
+                        fold1(b.w, sr, rs, fast)};
       *reinterpret_cast<f32x4*>(q) = oa;
       *reinterpret_cast<f32x4*>(q + 4) = ob;
     }
@@ -65,10 +91,13 @@ __global__ __launch_bounds__(kThreads) void fold_any_kernel(const T* __restrict_
   if (j >= cols) return;
   for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
     const T v = src[r * ld_src + j];
+    const double sr = s[r];
+    const bool fast = fold_fast_row(sr);
+    const double rs = 1.0 / sr;
     if constexpr (sizeof(T) == 2) {
-      dst[r * ld_dst + j] = (uint16_t)(pack_bf16x2(fold1(bf16_to_f32(v), s[r]), 0.f) & 0xFFFFu);
+      dst[r * ld_dst + j] = (uint16_t)(pack_bf16x2(fold1(bf16_to_f32(v), sr, rs, fast), 0.f) & 0xFFFFu);
     } else {
-      dst[r * ld_dst + j] = fold1(v, s[r]);
+      dst[r * ld_dst + j] = fold1(v, sr, rs, fast);
     }
   }
 }
@@ -114,7 +143,48 @@ __global__ __launch_bounds__(kThreads) void export_fp16_kernel(const float* __re
   }
 }
 
+// Output-value subgraph with grouped KV heads: output channel (kv * g + j, d) of the statistic,
+// for every j < g, is the mean over j of the input channels (kv * g + j, d) — summed in head order,
+// divided once by g. One thread per (kv, d); it reads and writes only its own g channels, so the
+// output may be the input.
+__global__ __launch_bounds__(kThreads) void tie_heads_kernel(const double* a, int64_t n_kv, int64_t g,
+                                                             int64_t hd, double* out) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= n_kv * hd) return;
+  const int64_t kv = i / hd, d = i % hd;
+  const double* p = a + kv * g * hd + d;
+  double t = p[0];
+  for (int64_t j = 1; j < g; ++j) t += p[j * hd];
+  t = t / (double)g;
+  for (int64_t j = 0; j < g; ++j) out[(kv * g + j) * hd + d] = t;
+}
+
+// v_proj row (kv, d) takes the scale of o_proj input channel (kv * g, d).
+__global__ __launch_bounds__(kThreads) void head_group_scales_kernel(const double* __restrict__ s, int64_t n_kv,
+                                                                     int64_t g, int64_t hd,
+                                                                     double* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= n_kv * hd) return;
+  out[i] = s[(i / hd) * g * hd + i % hd];
+}
+
 }  // namespace
+
+hipError_t launch_tie_heads(const double* act_mean, int64_t n_heads, int64_t n_kv, int64_t head_dim, double* tied,
+                            hipStream_t st) {
+  const int64_t n = n_kv * head_dim;
+  hipLaunchKernelGGL(tie_heads_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0, st,
+                     act_mean, n_kv, n_heads / n_kv, head_dim, tied);
+  return hipGetLastError();
+}
+
+hipError_t launch_head_group_scales(const double* s, int64_t n_heads, int64_t n_kv, int64_t head_dim, double* s_kv,
+                                    hipStream_t st) {
+  const int64_t n = n_kv * head_dim;
+  hipLaunchKernelGGL(head_group_scales_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                     st, s, n_kv, n_heads / n_kv, head_dim, s_kv);
+  return hipGetLastError();
+}
 
 hipError_t launch_fold_scales(const void* src, int64_t ld_src, int dtype, int64_t rows, int64_t cols,
                               const double* s, void* dst, int64_t ld_dst, bool vec, hipStream_t st) {

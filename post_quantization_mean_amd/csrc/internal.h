@@ -54,6 +54,10 @@ hipError_t launch_quantize_pack(const WParts& w, int dtype, int64_t d_in, const 
 // ---- around the search: source fold and deployment form
 hipError_t launch_fold_scales(const void* src, int64_t ld_src, int dtype, int64_t rows, int64_t cols,
                               const double* s, void* dst, int64_t ld_dst, bool vec, hipStream_t stream);
+hipError_t launch_tie_heads(const double* act_mean, int64_t n_heads, int64_t n_kv, int64_t head_dim, double* tied,
+                            hipStream_t stream);
+hipError_t launch_head_group_scales(const double* s, int64_t n_heads, int64_t n_kv, int64_t head_dim, double* s_kv,
+                                    hipStream_t stream);
 hipError_t launch_export_fp16(const float* qscales, const int32_t* zeros, int64_t rows, int64_t n_groups,
                               uint16_t* steps_f16, uint8_t* zeros_u4, int32_t* counts, hipStream_t stream);
 

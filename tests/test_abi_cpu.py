@@ -30,11 +30,11 @@ def _declared():
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
     names = _declared()
-    assert len(names) == 26
+    assert len(names) == 28
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(b.exported_symbols()) == names
-    assert lib.awq_abi_version() == 3
+    assert lib.awq_abi_version() == 4
 
 
 def test_status_strings(lib):
@@ -301,3 +301,14 @@ def test_mlp_block_validation(lib):
     assert call(a13=FAKE_ODD) == 5   # cand_scales
     assert "cand_scales" in _err(lib)
     assert call(a5=0) == 3
+
+
+def test_head_tie_validation(lib):
+    assert lib.awq_tie_heads(None, 8, 2, 128, FAKE, None) == 1
+    assert lib.awq_tie_heads(FAKE, 8, 3, 128, FAKE, None) == 2      # 8 heads do not split into 3 groups
+    assert "multiple" in _err(lib)
+    assert lib.awq_tie_heads(FAKE, 8, 0, 128, FAKE, None) == 2
+    assert lib.awq_tie_heads(FAKE, 8, 2, 0, FAKE, None) == 2
+    assert lib.awq_tie_heads(FAKE, 1 << 21, 1, 128, FAKE, None) == 5
+    assert lib.awq_head_group_scales(FAKE, 8, 2, 128, None, None) == 1
+    assert lib.awq_head_group_scales(FAKE, 6, 4, 128, FAKE, None) == 2

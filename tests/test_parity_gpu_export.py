@@ -72,6 +72,34 @@ def test_fold_shapes(B, dtype):
     _fold_case(B, base.copy(), s, dtype, inplace=True)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_fold_special_values(B, dtype):
+    """Signed zeros, infinities, NaN, float32 subnormals and extreme values in the source, and scales
+    outside the range where the fold uses the reciprocal (1e-200, 1e200): the quotient is still the
+    float64 division's, rounded to float32 and then to the dtype."""
+    rng = np.random.default_rng(12)
+    rows, cols = 6, 64
+    v = (rng.standard_normal((rows, cols)) * 3).astype(np.float32)
+    v[0, :8] = [0.0, -0.0, np.inf, -np.inf, np.nan, 1e-45, -1e-40, 3.0e38]
+    v[1, :4] = [1e-38, -2.5e-39, 6.5e4, -1e30]
+    src = f32_to_bf16_bits(v) if dtype == "bf16" else v
+    s_np = np.array([0.37, 1e-200, 1e200, 2.0 ** -499, 3.5, 1e-4])
+    src_t = to_torch(src, "cuda")
+    got_t = B.awq_fold_scales(src_t, torch.from_numpy(s_np).cuda())
+    torch.cuda.synchronize()
+    want = X.fold_scales(to_f32(src).astype(np.float64), s_np, dtype)
+    if dtype == "bf16":
+        got = got_t.cpu().view(torch.int16).numpy().view(np.uint16)
+        nan_w = np.isnan(to_f32(want))
+        nan_g = np.isnan(to_f32(got))
+    else:
+        got = got_t.cpu().numpy()
+        nan_w, nan_g = np.isnan(want), np.isnan(got)
+        got, want = got.view(np.uint32), want.view(np.uint32)
+    assert np.array_equal(nan_g, nan_w)
+    assert np.array_equal(got[~nan_w], want[~nan_w]), int((got[~nan_w] != want[~nan_w]).sum())
+
+
 def test_fold_full_size_up_proj(B):
     # the source of the 7B down_proj search is up_proj: [11008, 4096] bf16, one scale per row
     wl = workload(3)
@@ -107,3 +135,65 @@ def test_export_fp16(B):
     assert np.array_equal(ex3["steps_f16"].cpu().numpy().view(np.uint16), hb3)
     assert np.array_equal(ex3["zeros_u4"].cpu().numpy(), packed3)
     assert list(ex3["counts"].cpu().numpy()) == [bz3, bs3]
+
+
+# ------------------------------------------------------------------ output-value subgraph, grouped KV heads
+
+@pytest.mark.parametrize("n_heads,n_kv,hd", [(8, 2, 128), (32, 8, 128), (8, 1, 64), (4, 4, 128), (6, 3, 96)])
+def test_tie_heads_and_group_scales_bit_exact(B, n_heads, n_kv, hd):
+    rng = np.random.default_rng(n_heads * 100 + n_kv * 10 + hd)
+    a = np.exp(rng.uniform(-3, 4, n_heads * hd))
+    at = torch.from_numpy(a).cuda()
+    tied = B.awq_tie_heads(at, n_heads, n_kv, hd)
+    want = X.tie_heads(a, n_heads, n_kv, hd)
+    assert np.array_equal(tied.cpu().numpy(), want)
+    # in place
+    a2 = at.clone()
+    B.awq_tie_heads(a2, n_heads, n_kv, hd, out=a2)
+    assert np.array_equal(a2.cpu().numpy(), want)
+    s = rng.uniform(0.1, 10, n_heads * hd)
+    got = B.awq_head_group_scales(torch.from_numpy(s).cuda(), n_heads, n_kv, hd).cpu().numpy()
+    assert np.array_equal(got, X.head_group_scales(s, n_heads, n_kv, hd))
+
+
+@pytest.mark.parametrize("n_heads,n_kv", [(4, 2), (4, 1), (4, 4)])
+def test_gqa_search_pack_and_v_proj_fold(B, n_heads, n_kv):
+    """o_proj (input n_heads x 128, output 384) searched on the tied statistic, its codes packed, and
+    v_proj ([n_kv x 128, 384] bf16) folded with the group scales, against the oracle."""
+    hd, d_model, n_grid = 128, 384, 8
+    wl = custom_workload(300, n_heads * hd, d_model, "bf16", n_grid=n_grid, outlier_channels=5,
+                         config_id=220 + n_kv)
+    x, w = make_x(wl), make_w(wl)
+    print(f"[gpu export] GQA search n_heads={n_heads} n_kv={n_kv}", flush=True)
+    xt, wt = to_torch(x, "cuda"), to_torch(w, "cuda")
+    act = B.awq_act_stats(xt)
+    tied = B.awq_tie_heads(act, n_heads, n_kv, hd)
+    res = B.awq_search_scales(xt, [wt], tied, n_grid=n_grid)
+    pk = B.awq_quantize_pack([wt], res["best_scales"])
+    s_kv = B.awq_head_group_scales(res["best_scales"], n_heads, n_kv, hd)
+    rng = np.random.default_rng(n_kv)
+    wv = f32_to_bf16_bits((rng.standard_normal((n_kv * hd, d_model)) * 0.02).astype(np.float32))
+    wv_t = to_torch(wv, "cuda")
+    wv_f = B.awq_fold_scales(wv_t, s_kv)
+    torch.cuda.synchronize()
+
+    Xo, Wo = to_f32(x).astype(np.float64), to_f32(w).astype(np.float64)
+    ref = X.search_scales_tied(Xo, Wo, n_heads, n_kv, hd, 128, n_grid)
+    assert P.max_rel(tied.cpu().numpy(), ref.act_mean) < 1e-11
+    assert P.max_rel(res["cand_scales"].cpu().numpy(), ref.scales) < 1e-12
+    losses = res["losses"].cpu().numpy()
+    assert P.max_rel(losses, ref.losses) < P.LOSS_RTOL
+    k = int(res["best_info"][0].item())
+    assert P.kstar_ok(k, ref.best_k, ref.losses)
+    best = res["best_scales"].cpu().numpy()
+    # the chosen scales are tied across the query heads of each group
+    g = n_heads // n_kv
+    bh = best.reshape(n_kv, g, hd)
+    assert np.array_equal(bh, np.repeat(bh[:, :1, :], g, axis=1))
+    c = P.compare_codes(pk["codes"].cpu().numpy(), pk["qscales"].cpu().numpy(), pk["zeros"].cpu().numpy(),
+                        O.quantize_pack(Wo, ref.scales[k], 128))
+    assert c["mismatch"] == 0 and c["zero_mismatch"] == 0 and c["step_max_rel"] < P.STEP_RTOL, c
+    got = wv_f.cpu().view(torch.int16).numpy().view(np.uint16)
+    want = X.fold_scales(to_f32(wv).astype(np.float64), X.head_group_scales(best, n_heads, n_kv, hd), "bf16")
+    assert np.array_equal(got, want), int((got != want).sum())
+    print(f"  k*={k} oracle {ref.best_k}; codes {c}", flush=True)
