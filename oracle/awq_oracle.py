@@ -41,6 +41,11 @@ Readings taken where the pages are silent, garbled or disagree:
   is ``k = 0``, whose scale is exactly all ones.
 * Packing: along ``d_in``, element ``2j`` in the low nibble and ``2j+1`` in the high
   nibble of byte ``j`` (bjdmk names the low and high 4 bits, not their order).
+* Non-finite weights: the group's max and min propagate NaN (as torch's and numpy's do), so
+  a group holding a NaN has a NaN step and every restored value in it is NaN; an infinity
+  gives an infinite step and NaN restored values (0 times infinity). A NaN code or zero point
+  has no 4-bit value: the stored form writes it as 0. Zero points are stored as int32 and
+  saturate to its range.
 """
 from __future__ import annotations
 
@@ -104,6 +109,7 @@ def group_quantize(Y, group_size: int = 128) -> GroupQuant:
     zero = np.rint(zt)
     t = g / scale
     q = np.clip(np.rint(t) + zero, 0, QMAX)
+    q = np.where(np.isnan(q), 0.0, q)  # no 4-bit value for a NaN code (non-finite group)
     return GroupQuant(q=q.reshape(rows, d).astype(np.int64), scale=scale[..., 0],
                       zero=zero[..., 0], t=t.reshape(rows, d), zt=zt[..., 0])
 
@@ -257,5 +263,6 @@ def quantize_pack(W, s, group_size: int = 128) -> PackedQuant:
     (gsyq section 二 quantizer; qqiyuan ``group_quantize`` outputs; bjdmk packing)."""
     W = np.asarray(W, dtype=np.float64)
     qr = group_quantize(W * np.asarray(s, np.float64)[None, :], group_size)
-    return PackedQuant(codes=pack_int4(qr.q), qscales=qr.scale, zeros=qr.zero.astype(np.int64),
+    z = np.clip(np.where(np.isnan(qr.zero), 0.0, qr.zero), -2.0 ** 31, 2.0 ** 31 - 1)
+    return PackedQuant(codes=pack_int4(qr.q), qscales=qr.scale, zeros=z.astype(np.int64),
                        q=qr.q, t=qr.t, zt=qr.zt)

@@ -327,3 +327,40 @@ def test_blocked_search_matches_gram_form_and_whole_search():
         d = O.quantize_restore(W, res.scales[k], 128) - W
         gram = float(np.einsum("oc,cd,od->", d, G, d)) / (X.shape[0] * W.shape[0])
         assert math.isclose(res.losses[k], gram, rel_tol=1e-10)
+
+
+def test_nonfinite_weight_groups():
+    """A NaN weight makes its group's step NaN (max and min propagate NaN) and every restored value
+    of the group NaN; an infinity makes the step infinite and the restored values NaN (0 * inf);
+    stored codes and zero points of such groups are 0; other groups are untouched."""
+    rng = np.random.default_rng(16)
+    W = rng.standard_normal((3, 8)) * 0.1
+    W[0, 1] = np.nan          # row 0, group 0
+    W[1, 6] = np.inf          # row 1, group 1
+    W[2, 2] = -np.inf         # row 2, group 0
+    W[2, 3] = np.inf
+    with np.errstate(invalid="ignore"):
+        pq = O.quantize_pack(W, np.ones(8), 4)
+        wh = O.quantize_restore(W, np.ones(8), 4)
+    assert np.isnan(pq.qscales[0, 0]) and pq.qscales[1, 1] == np.inf and pq.qscales[2, 0] == np.inf
+    for r, gi in ((0, 0), (1, 1), (2, 0)):
+        assert np.all(pq.q[r, 4 * gi:4 * gi + 4] == 0) and pq.zeros[r, gi] == 0
+        assert np.all(np.isnan(wh[r, 4 * gi:4 * gi + 4]))
+    # the finite groups are quantized as usual
+    for r, gi in ((0, 1), (1, 0), (2, 1)):
+        ref = O.quantize_pack(W[r:r + 1, 4 * gi:4 * gi + 4], np.ones(4), 4)
+        assert np.array_equal(pq.q[r, 4 * gi:4 * gi + 4], ref.q[0]) and pq.zeros[r, gi] == ref.zeros[0, 0]
+        assert np.all(np.isfinite(wh[r, 4 * gi:4 * gi + 4]))
+    # the search's losses are then NaN for every ratio, so the ones fallback is chosen
+    X = rng.standard_normal((6, 8))
+    with np.errstate(invalid="ignore"):
+        res = O.search_scales(X, W, 4, 3)
+    assert np.all(np.isnan(res.losses)) and res.best_k == 0 and np.all(res.best_scales == 1.0)
+
+
+def test_zero_point_saturates_to_int32():
+    # a constant one-signed group: step floor 1e-8, zero point -min/step = -5e8 fits; -50 gives -5e9
+    W = np.array([[5.0, 5.0, 5.0, 5.0], [-50.0, -50.0, -50.0, -50.0]])
+    pq = O.quantize_pack(W, np.ones(4), 4)
+    assert pq.qscales[0, 0] == 1e-8 and pq.zeros[0, 0] == -500000000
+    assert pq.zeros[1, 0] == 2 ** 31 - 1
