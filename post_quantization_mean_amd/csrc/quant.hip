@@ -197,20 +197,21 @@ struct FastGroup {
   float step, inv, zt;
   bool ok;
 };
-// Minimum / maximum of a lane's value and a neighbour's (DPP) as one v_med3_f32 against -/+FLT_MAX:
-// exact for finite values; an infinity saturates to -/+FLT_MAX, which makes the group's step
-// exceed the fast path's limit, so the group is redone in float64. (fminf/fmaxf would cost an
-// extra instruction per step to quieten a possible signalling NaN coming out of the lane move.)
-__device__ __forceinline__ float lane_min(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, -FLT_MAX); }
-__device__ __forceinline__ float lane_max(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, FLT_MAX); }
+// The group's extremes with NaN-propagating minimum / maximum (v_minimum3_f32 / v_maximum3_f32,
+// IEEE 754-2019): a NaN weight (or scale) makes the step NaN, an infinity makes it infinite, and
+// either fails the step test below, so the group is redone in float64, where the definition's max
+// and min propagate NaN too. (IEEE minNum / maxNum, fminf / fmaxf, would drop a NaN and quantize the
+// rest of the group with a finite step.)
+__device__ __forceinline__ float lane_min(float a, float b) { return __builtin_elementwise_minimum(a, b); }
+__device__ __forceinline__ float lane_max(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
 template <int E>
 __device__ __forceinline__ FastGroup fast_group(const float (&y)[E]) {
   float mn = y[0], mx = y[0];
 #pragma unroll
   for (int j = 1; j < E; ++j) {
-    mn = fminf(mn, y[j]);
-    mx = fmaxf(mx, y[j]);
+    mn = lane_min(mn, y[j]);
+    mx = lane_max(mx, y[j]);
   }
   mn = lane_min(mn, dpp_f32<kDppXor1>(mn));
   mx = lane_max(mx, dpp_f32<kDppXor1>(mx));
@@ -258,6 +259,17 @@ __device__ __forceinline__ double readlane_f64(double v, int l) {
 }
 
 // Minimum and maximum over the whole wave: within rows of 16 lanes, then across the 4 rows.
+// Group minimum and maximum over the wave's 128 values (two per lane), propagating NaN as the
+// definition's max / min do (fmin / fmax alone would drop a NaN operand): a group holding a NaN
+// gets a NaN step, hence NaN restored values and codes (stored as 0).
+__device__ __forceinline__ void wave_minmax_f64(double& mn, double& mx);
+__device__ __forceinline__ void group_minmax_f64(double y0, double y1, double& mn, double& mx) {
+  mn = fmin(y0, y1);
+  mx = fmax(y0, y1);
+  wave_minmax_f64(mn, mx);
+  if (__ballot(y0 != y0 || y1 != y1)) mn = mx = __builtin_nan("");
+}
+
 __device__ __forceinline__ void wave_minmax_f64(double& mn, double& mx) {
   mn = fmin(mn, dpp_f64<kDppXor1>(mn));
   mx = fmax(mx, dpp_f64<kDppXor1>(mx));
@@ -276,8 +288,8 @@ __device__ __forceinline__ void exact_group(float wa, float wb, const double* s_
   const double w0 = wa, w1 = wb;
   const double s0 = s_lds[0], s1 = s_lds[1];
   const double y0 = w0 * s0, y1 = w1 * s1;
-  double mn = fmin(y0, y1), mx = fmax(y0, y1);
-  wave_minmax_f64(mn, mx);
+  double mn, mx;
+  group_minmax_f64(y0, y1, mn, mx);
   const double st = group_step(mn, mx);
   const double zero = rint(-mn / st);
   const double q0 = exact_code(y0, st, zero), q1 = exact_code(y1, st, zero);
@@ -406,8 +418,8 @@ __global__ __launch_bounds__(kThreads) void quant_delta_kernel(WParts w, int64_t
 __device__ __forceinline__ void exact_pack_group(float wa, float wb, const double* s, uint8_t* code, float* qs,
                                                  int32_t* zp, int lane) {
   const double y0 = (double)wa * s[0], y1 = (double)wb * s[1];
-  double mn = fmin(y0, y1), mx = fmax(y0, y1);
-  wave_minmax_f64(mn, mx);
+  double mn, mx;
+  group_minmax_f64(y0, y1, mn, mx);
   const double st = group_step(mn, mx);
   const double zero = rint(-mn / st);
   double q0 = exact_code(y0, st, zero), q1 = exact_code(y1, st, zero);

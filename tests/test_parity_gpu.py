@@ -194,6 +194,63 @@ def test_nonfinite_activation_falls_back_to_unit_scales(B):
     assert np.all(g["best_scales"] == 1.0)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_zero_activation_channels_end_to_end(B, dtype):
+    """Channels whose activations are all zero have act_mean 0: s = 0^0 = 1 at r = 0 and the floor
+    1e-4 at r > 0, which the normaliser turns into extreme group scales (msModelSlim 算法公式); the
+    whole search and the pack still match the oracle."""
+    wl = custom_workload(500, 384, 300, dtype, n_grid=6, outlier_channels=3, config_id=111)
+    x, w, parts = _case(wl)
+    x = x.copy()
+    x[:, [4, 130, 383]] = 0
+    g, ref, _, _ = _check_full(B, x, w, parts, 6)
+    assert np.all(g["act_mean"][[4, 130, 383]] == 0.0)
+    assert np.all(ref.scales[1:, 4] == ref.scales[1:].min(axis=1))  # the floored channel is the minimum
+
+
+def test_nonfinite_weights_end_to_end(B):
+    """NaN and +/-Inf weights: their groups' steps are NaN / infinite, every loss is NaN (the group's
+    restored values reach every token's output), so the search keeps the unit scales (gsyq section 二)
+    and flags it; the pack at ones matches the oracle: codes and zero points of those groups 0, the
+    others bit-exact; delta of those groups NaN."""
+    wl = custom_workload(300, 384, 260, "bf16", n_grid=5, outlier_channels=2, config_id=112)
+    x, w, parts = _case(wl)
+    w = w.copy()
+    w[3, 5] = 0x7FC0                        # NaN in row 3, group 0
+    w[17, 200] = 0x7F80                     # +Inf in row 17, group 1
+    w[250, 300], w[250, 301] = 0xFF80, 0x7F80  # -Inf and +Inf in row 250, group 2
+    g, xt, wp = _run_gpu(B, x, w, parts, 5)
+    assert np.all(np.isnan(g["losses"]))
+    assert list(g["best_info"]) == [0, 1]
+    assert np.all(g["best_scales"] == 1.0)
+    W = to_f32(w).astype(np.float64)
+    with np.errstate(invalid="ignore"):
+        pk = O.quantize_pack(W, np.ones(384), 128)
+    assert np.array_equal(P.unpack_codes(g["codes"]), pk.q)
+    assert np.array_equal(g["zeros"], pk.zeros)
+    qs = g["qscales"].astype(np.float64)
+    nan_w = np.isnan(pk.qscales)
+    assert np.array_equal(np.isnan(qs), nan_w) and nan_w[3, 0]
+    fin = np.isfinite(pk.qscales)
+    assert np.array_equal(np.isinf(qs), np.isinf(pk.qscales)) and not fin[17, 1] and not fin[250, 2]
+    assert np.max(np.abs(qs[fin] - pk.qscales[fin]) / pk.qscales[fin]) < P.STEP_RTOL
+    # delta at two candidates: NaN on exactly the non-finite groups, the rest within tolerance
+    cand = torch.from_numpy(np.stack([np.ones(384), O.candidate_scales(g["act_mean"], 0.4)])).cuda()
+    d = B.awq_quant_delta(wp, cand, 128)
+    torch.cuda.synchronize()
+    for kk in range(2):
+        sk = cand[kk].cpu().numpy()
+        with np.errstate(invalid="ignore"):
+            d_or = O.quantize_restore(W, sk, 128) - W
+            pq = O.quantize_pack(W, sk, 128)
+        d_gpu = d[kk].float().cpu().numpy().astype(np.float64)
+        assert np.array_equal(np.isnan(d_gpu), np.isnan(d_or))
+        ok = np.isfinite(d_or)
+        em, _ = P.exempt_masks(pq.t, pq.zt)
+        tol = P.delta_tolerance(d_or, W, np.nan_to_num(pq.qscales), sk)
+        assert np.all((np.abs(d_gpu - d_or) <= tol) | em | ~ok)
+
+
 def test_repeat_runs_are_bitwise_identical(B):
     wl = custom_workload(1024, 512, 768, "bf16", n_grid=5, config_id=108)
     x, w, parts = _case(wl)
