@@ -60,6 +60,7 @@ extern "C" {
 
 #define AWQ_ABI_VERSION 4
 #define AWQ_MAX_PARTS 8
+#define AWQ_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20) /* device scratch of awq_search_scales_noalloc */
 #define AWQ_GROUP_SIZE 128
 #define AWQ_MAX_RATIOS 64
 
@@ -212,6 +213,23 @@ AWQ_API int awq_search_scales(const void* x, int64_t ld_x, const void* const* w_
                       int cand_per_pass, double* cand_scales, double* losses,
                       double* best_scales, int32_t* best_info, void* workspace,
                       size_t workspace_bytes, void* stream);
+
+/* The same search for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): no workspace argument and no allocation.
+ * Its temporaries live in a fixed device scratch of AWQ_NOALLOC_SCRATCH_BYTES (64 MiB) inside the
+ * library, one per GPU, held from the first use on that GPU until the process ends: the tile sums
+ * of all candidates, then the delta of one candidate for a chunk of whole 256-row tiles of the
+ * stacked rows (all rows when they fit), chunk after chunk. Slower than awq_search_scales with a
+ * full workspace (one quantize->delta and one error-GEMM launch per candidate and chunk). Calls that
+ * overlap on one GPU (on any streams) share the scratch and race; serialise them.
+ *   Arguments as awq_search_scales, without cand_per_pass and the workspace.
+ *   AWQ_ERR_WORKSPACE when n_grid * awq_error_tiles(n_tokens, d_out) float64 sums and 256 rows of
+ *   delta (d_in * element size bytes each; fewer when d_out is smaller) do not fit the scratch. */
+AWQ_API int awq_search_scales_noalloc(const void* x, int64_t ld_x, const void* const* w_parts,
+                                      const int64_t* part_rows, int n_parts, int dtype, int64_t n_tokens,
+                                      int64_t d_in, const double* act_mean, int group_size, int n_grid,
+                                      double* cand_scales, double* losses, double* best_scales,
+                                      int32_t* best_info, void* stream);
 
 /* ------------------------------------------------------------------ a6: final quantize + pack */
 

@@ -48,6 +48,8 @@ _SIGNATURES = {
     "awq_search_workspace_bytes": (_c_size, [_c_int, _c_i64, _c_i64, _c_i64, _c_int, _c_int, _c_int]),
     "awq_search_scales": (_c_int, [_vp, _c_i64, _vp, _vp, _c_int, _c_int, _c_i64, _c_i64, _vp, _c_int,
                                    _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
+    "awq_search_scales_noalloc": (_c_int, [_vp, _c_i64, _vp, _vp, _c_int, _c_int, _c_i64, _c_i64, _vp, _c_int,
+                                           _c_int, _vp, _vp, _vp, _vp, _vp]),
     "awq_quantize_pack": (_c_int, [_vp, _vp, _c_int, _c_int, _c_i64, _c_int, _vp, _vp, _vp, _vp, _vp]),
     "awq_act_stats_accumulate": (_c_int, [_vp, _c_int, _c_i64, _c_i64, _c_i64, _vp, _vp, _c_size, _vp]),
     "awq_act_stats_finalize": (_c_int, [_vp, _c_i64, _c_i64, _vp, _vp]),
@@ -331,6 +333,24 @@ def awq_search_scales(x: torch.Tensor, w_parts, act_mean: torch.Tensor, n_grid: 
     ws = _workspace(need, dev, workspace)
     _check(lib.awq_search_scales(px, ld, ptrs, rows, len(parts), dt, n, d, pa, group_size, n_grid, cand_per_pass,
                                  pc, pl, pb, pi, ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream)))
+    return res
+
+
+def awq_search_scales_noalloc(x: torch.Tensor, w_parts, act_mean: torch.Tensor, n_grid: int = 20,
+                              group_size: int = GROUP_SIZE, out=None, stream=None) -> dict:
+    """awq_search_scales with the library's fixed device scratch instead of a workspace: the C call
+    allocates nothing (pass `out` to allocate nothing here either). Overlapping calls on one GPU race."""
+    lib = load_library()
+    px, n, d, ld = _x_args(x)
+    dt = _dtype_code(x)
+    parts, ptrs, rows, d_out = _parts(w_parts, x.dtype)
+    if parts[0].shape[1] != d:
+        raise ValueError("x and the weights disagree on d_in")
+    dev = x.device
+    pa = _buf(act_mean, "act_mean", torch.float64, d, dev)
+    res, (pc, pl, pb, pi) = _search_outputs(out, n_grid, d, dev)
+    _check(lib.awq_search_scales_noalloc(px, ld, ptrs, rows, len(parts), dt, n, d, pa, group_size, n_grid, pc, pl,
+                                         pb, pi, _stream(stream)))
     return res
 
 

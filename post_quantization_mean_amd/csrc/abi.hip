@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "awq.h"
 #include "internal.h"
 #include "variants.h"
@@ -668,6 +670,122 @@ int awq_search_scales_mlp(const void* x, int64_t ld_x, const void* w_gate, const
     }
   }
   e = awq::launch_loss_argmin(tile_sse, tiles, n_grid, n_tokens, d_model, cand_scales, d_in, losses, best_scales,
+                              best_info, st);
+  if (e != hipSuccess) return hip_fail(e, "loss_argmin launch");
+  return ok();
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------ search without allocation
+
+namespace {
+
+// Device scratch of awq_search_scales_noalloc: the tile sums of every candidate, then the delta of
+// one candidate for one chunk of whole 256-row tiles. Every call on a GPU uses that GPU's copy of
+// this array (held from the library's first use on the device until the process ends), so calls
+// that overlap on one GPU race. In host code `scratch` stands for the device variable and is not a
+// device address: its address comes from hipGetSymbolAddress, per device.
+constexpr size_t kNoAllocScratchBytes = AWQ_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// This device's address of `scratch`, looked up once per device (with that device current).
+int scratch_on_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(AWQ_ERR_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p || !aligned(p, 256)) return fail(AWQ_ERR_HIP, "scratch has no usable device address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return AWQ_OK;
+}
+
+// Stacked rows [r0, r1) of a fused set, as a set of parts of their own.
+awq::WParts slice_rows(const awq::WParts& w, int64_t r0, int64_t r1, int64_t row_bytes) {
+  awq::WParts out;
+  memset(&out, 0, sizeof out);
+  int n = 0;
+  for (int p = 0; p < w.n; ++p) {
+    const int64_t b = w.row_begin[p], e = w.row_begin[p + 1];
+    const int64_t lo = b > r0 ? b : r0, hi = e < r1 ? e : r1;
+    if (lo >= hi) continue;
+    out.ptr[n] = static_cast<const char*>(w.ptr[p]) + (lo - b) * row_bytes;
+    out.row_begin[n] = lo - r0;
+    ++n;
+  }
+  out.n = n;
+  for (int p = n; p <= awq::kMaxParts; ++p) out.row_begin[p] = r1 - r0;
+  return out;
+}
+
+}  // namespace
+
+extern "C" {
+
+int awq_search_scales_noalloc(const void* x, int64_t ld_x, const void* const* w_parts, const int64_t* part_rows,
+                              int n_parts, int dtype, int64_t n_tokens, int64_t d_in, const double* act_mean,
+                              int group_size, int n_grid, double* cand_scales, double* losses, double* best_scales,
+                              int32_t* best_info, void* stream) {
+  TRY(check_dtype(dtype));
+  TRY(check_group(group_size, d_in));
+  TRY(check_d_in_bytes(dtype, d_in));
+  TRY(check_x(x, dtype, n_tokens, d_in, ld_x));
+  awq::WParts w;
+  TRY(make_parts(w_parts, part_rows, n_parts, dtype, d_in, &w));
+  const int64_t d_out = w.row_begin[w.n];
+  if (!act_mean || !cand_scales || !losses || !best_scales || !best_info)
+    return fail(AWQ_ERR_NULL, "a required pointer is NULL");
+  if (!aligned(cand_scales, 16)) return fail(AWQ_ERR_UNSUPPORTED, "cand_scales is not 16-byte aligned");
+  if (n_grid < 1 || n_grid > 65535) return fail(AWQ_ERR_ARG, "n_grid %d outside [1, 65535]", n_grid);
+  // scratch plan: tile sums of all candidates, then the delta of the largest chunk of whole
+  // 256-row tiles (all rows when they fit) that the rest of the scratch holds
+  const int64_t tiles_m = (n_tokens + awq::kTileM - 1) / awq::kTileM;
+  const int64_t tiles = awq_error_tiles(n_tokens, d_out);
+  const size_t sse_bytes = round_up((size_t)n_grid * (size_t)tiles * sizeof(double), 256);
+  const size_t row_bytes = (size_t)d_in * esize(dtype);
+  if (sse_bytes >= kNoAllocScratchBytes)
+    return fail(AWQ_ERR_WORKSPACE, "%d candidates x %lld tiles of sums exceed the %zu-byte scratch", n_grid,
+                (long long)tiles, kNoAllocScratchBytes);
+  const int64_t fit_rows = (int64_t)((kNoAllocScratchBytes - sse_bytes) / row_bytes);
+  const int64_t chunk = d_out <= fit_rows ? d_out : fit_rows / awq::kTileN * awq::kTileN;
+  if (chunk < 1)
+    return fail(AWQ_ERR_WORKSPACE, "the %zu-byte scratch holds no 256-row chunk of delta (d_in %lld)",
+                kNoAllocScratchBytes, (long long)d_in);
+  void* base = nullptr;
+  TRY(scratch_on_current_device(&base));
+  double* tile_sse = static_cast<double*>(base);
+  void* delta = static_cast<char*>(base) + sse_bytes;
+
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = awq::launch_candidate_scales(act_mean, d_in, n_grid, cand_scales, st);
+  if (e != hipSuccess) return hip_fail(e, "candidate_scales launch");
+  // the tile sums of candidate k are laid out as the one-launch search lays them out per candidate
+  // (tiles_m x tiles_n, here chunk after chunk: token tile major within each chunk), and the
+  // loss is their fixed-order sum as there; every value is written before it is read, so nothing
+  // needs clearing
+  for (int64_t r0 = 0; r0 < d_out; r0 += chunk) {
+    const int64_t r1 = r0 + chunk < d_out ? r0 + chunk : d_out;
+    const awq::WParts wc = slice_rows(w, r0, r1, (int64_t)row_bytes);
+    for (int k = 0; k < n_grid; ++k) {
+      e = awq::launch_quant_delta(wc, dtype, d_in, cand_scales + (int64_t)k * d_in, 1, delta, st);
+      if (e != hipSuccess) return hip_fail(e, "quant_delta launch");
+      e = awq::launch_error_sse(x, ld_x, delta, dtype, n_tokens, d_in, r1 - r0, 1,
+                                tile_sse + (int64_t)k * tiles + tiles_m * (r0 / awq::kTileN), st);
+      if (e != hipSuccess) return hip_fail(e, "error_sse launch");
+    }
+  }
+  e = awq::launch_loss_argmin(tile_sse, tiles, n_grid, n_tokens, d_out, cand_scales, d_in, losses, best_scales,
                               best_info, st);
   if (e != hipSuccess) return hip_fail(e, "loss_argmin launch");
   return ok();

@@ -30,7 +30,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
     names = _declared()
-    assert len(names) == 28
+    assert len(names) == 29
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(b.exported_symbols()) == names
@@ -149,6 +149,26 @@ def test_search_workspace_and_validation(lib):
     assert call(ws=FAKE_ODD) == 5
     assert call(cs=FAKE_ODD) == 5
     assert "cand_scales" in _err(lib)
+
+
+def test_search_noalloc_validation(lib):
+    p, r = _parts(1, rows=520)
+
+    def call(tok=600, d=256, ng=7, cs=FAKE, ld=None, rr=r, pp=p):
+        return lib.awq_search_scales_noalloc(FAKE, ld or d, pp, rr, 1, 1, tok, d, FAKE, 128, ng, cs, FAKE, FAKE,
+                                             FAKE, None)
+    assert call(tok=0) == 3
+    assert call(ng=0) == 4
+    assert call(cs=None) == 1
+    assert call(cs=FAKE_ODD) == 5
+    assert call(d=200) == 2
+    # 256 rows of a 131072-wide bf16 delta (64 MiB) plus the tile sums do not fit the scratch
+    p2, r2 = _parts(1, rows=600)
+    assert call(d=131072, rr=r2, pp=p2) == 6
+    assert "scratch" in _err(lib)
+    # nor do the tile sums of 65535 candidates on a large layer
+    p3, r3 = _parts(1, rows=8192)
+    assert call(tok=65536, d=256, ng=65535, rr=r3, pp=p3) == 6
 
 
 def test_accumulate_finalize_validation(lib):
