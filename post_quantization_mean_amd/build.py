@@ -1,6 +1,6 @@
 """Builds libawq_mi355x.so (the C ABI of include/awq.h) in-tree with hipcc for gfx950.
 
-    python -m post_quantization_mean_amd.build [-v]
+    python -m post_quantization_mean_amd.build [-v] [--sanitize]
 """
 from __future__ import annotations
 
@@ -50,24 +50,37 @@ def _run(cmd: list[str], verbose: bool) -> None:
         print("\n".join(lines), flush=True)
 
 
-def build(verbose: bool = False, jobs: int | None = None) -> str:
-    """Compiles every HIP source for gfx950 and links the shared library. Always rebuilds."""
+# host code only: the device code of a sanitized build is the same as the product's
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=undefined"]
+SANITIZED_LIB_PATH = os.path.join(BUILD_DIR, "sanitized", "libawq_mi355x_asan_ubsan.so")
+
+
+def build(verbose: bool = False, jobs: int | None = None, sanitize: bool = False) -> str:
+    """Compiles every HIP source for gfx950 and links the shared library. Always rebuilds.
+
+    With `sanitize`, the host code is built with AddressSanitizer and UndefinedBehaviorSanitizer
+    into a separate library under the build folder (for host-side checks of the C ABI; load it
+    with the sanitizer runtime preloaded)."""
     cc = hipcc()
-    os.makedirs(BUILD_DIR, exist_ok=True)
+    out_dir = os.path.dirname(SANITIZED_LIB_PATH) if sanitize else BUILD_DIR
+    lib_path = SANITIZED_LIB_PATH if sanitize else LIB_PATH
+    extra = SANITIZE_FLAGS if sanitize else []
+    os.makedirs(out_dir, exist_ok=True)
     objs = []
 
     def compile_one(src: str) -> str:
-        obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
-        _run([cc, *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        obj = os.path.join(out_dir, src.replace(".hip", ".o"))
+        _run([cc, *COMMON_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
         return obj
 
     with cf.ThreadPoolExecutor(jobs or min(len(SOURCES), os.cpu_count() or 1)) as ex:
         objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB_PATH + ".tmp"
-    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    tmp = lib_path + ".tmp"
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *extra, "-o", tmp, *objs], verbose)
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, sanitize="--sanitize" in sys.argv))

@@ -62,7 +62,7 @@ int check_x(const void* x, int dtype, int64_t n_tokens, int64_t d_in, int64_t ld
   if (n_tokens == 0) return fail(AWQ_ERR_NO_TOKENS, "n_tokens == 0: no activation mean");
   if (!x) return fail(AWQ_ERR_NULL, "x is NULL");
   if (ld_x < d_in) return fail(AWQ_ERR_ARG, "ld_x %lld < d_in %lld", (long long)ld_x, (long long)d_in);
-  if ((ld_x * (int64_t)esize(dtype)) % 16)
+  if (ld_x % (16 / (int64_t)esize(dtype)))  // the row pitch in bytes is a multiple of 16 (no product: ld_x may be huge)
     return fail(AWQ_ERR_UNSUPPORTED, "ld_x * element size must be a multiple of 16 bytes");
   if (!aligned(x, 16)) return fail(AWQ_ERR_UNSUPPORTED, "x is not 16-byte aligned");
   if (ld_x > kMaxTileBytes || (int64_t)awq::kTileM * ld_x * (int64_t)esize(dtype) > kMaxTileBytes)
@@ -206,7 +206,7 @@ int check_mlp_dims(int64_t n_tokens, int64_t d_in, int64_t d_ff) {
     return fail(AWQ_ERR_SHAPE, "d_ff %lld is not a positive multiple of 128", (long long)d_ff);
   TRY(check_d_in_bytes(AWQ_DTYPE_BF16, d_in));
   TRY(check_d_in_bytes(AWQ_DTYPE_BF16, d_ff));
-  if (n_tokens * d_ff > ((int64_t)1 << 40)) return fail(AWQ_ERR_UNSUPPORTED, "n_tokens * d_ff too large");
+  if (n_tokens > ((int64_t)1 << 40) / d_ff) return fail(AWQ_ERR_UNSUPPORTED, "n_tokens * d_ff too large");
   return AWQ_OK;
 }
 
@@ -405,8 +405,8 @@ int awq_fold_scales(const void* src, int64_t ld_src, int dtype, int64_t rows, in
   if (!aligned(src, es) || !aligned(dst, es)) return fail(AWQ_ERR_UNSUPPORTED, "src or dst is not element-aligned");
   if (cols > ((int64_t)1 << 31) - 256) return fail(AWQ_ERR_UNSUPPORTED, "cols %lld too large", (long long)cols);
   // 16-byte vectors when every row start is 16-byte aligned and the rows are whole vectors
-  const bool vec = cols % 8 == 0 && aligned(src, 16) && aligned(dst, 16) && (ld_src * (int64_t)es) % 16 == 0 &&
-                   (ld_dst * (int64_t)es) % 16 == 0;
+  const bool vec = cols % 8 == 0 && aligned(src, 16) && aligned(dst, 16) && ld_src % (16 / (int64_t)es) == 0 &&
+                   ld_dst % (16 / (int64_t)es) == 0;
   hipError_t e = awq::launch_fold_scales(src, ld_src, dtype, rows, cols, s, dst, ld_dst, vec, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "fold_scales launch");
   return ok();
@@ -450,7 +450,7 @@ int awq_export_fp16(const float* qscales, const int32_t* zeros, int64_t rows, in
     return fail(AWQ_ERR_NULL, "qscales, zeros, steps_f16, zeros_u4 or counts is NULL");
   if (rows <= 0 || n_groups <= 0)
     return fail(AWQ_ERR_SHAPE, "rows %lld and n_groups %lld must be > 0", (long long)rows, (long long)n_groups);
-  if (rows * ((n_groups + 1) / 2) > ((int64_t)1 << 40)) return fail(AWQ_ERR_UNSUPPORTED, "export too large");
+  if (rows > ((int64_t)1 << 40) / ((n_groups + 1) / 2)) return fail(AWQ_ERR_UNSUPPORTED, "export too large");
   if (!aligned(qscales, 4) || !aligned(zeros, 4) || !aligned(steps_f16, 2) || !aligned(counts, 4))
     return fail(AWQ_ERR_UNSUPPORTED, "qscales, zeros, counts must be 4-byte and steps_f16 2-byte aligned");
   hipError_t e = awq::launch_export_fp16(qscales, zeros, rows, n_groups, steps_f16, zeros_u4, counts,
