@@ -72,3 +72,37 @@ def block_search(X, Wg, Wu, Wd, n_grid: int = 20, kind: int = ACT_SILU, group_si
     k = O.select_best(losses)
     best = scales[k] if any(np.isfinite(losses)) else np.ones(X.shape[1])
     return np.stack(scales), np.array(losses), k, best
+
+
+def _bf16(v) -> np.ndarray:
+    """float64 -> float32 -> bfloat16 values, each rounding to nearest even (the sequence of a float32
+    value stored as a bfloat16 operand)."""
+    from oracle.awq_export import f32_to_bf16_rne
+    bits = f32_to_bf16_rne(np.asarray(v, dtype=np.float64).astype(np.float32))
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def block_losses_bf16_operands(X, Wg, Wu, Wd, scales, kind: int = ACT_SILU, group_size: int = 128,
+                               round_operands: bool = True) -> np.ndarray:
+    """The block losses of ``block_search`` computed through the difference form a bfloat16 matrix-core
+    path takes: y_ref - y_k = dh_k Wd^T with dh_k = act(G) U - act(G + E_g)(U + E_u), G = X Wg^T,
+    E_g = X dWg^T (likewise up), where the two GEMM operands that the path holds in bfloat16, the
+    weight differences dW = What - W and the hidden difference dh, are rounded to bfloat16; everything
+    else is float64. With ``round_operands=False`` it is the float64 difference form of the same
+    losses. A diagnostic for how far those two specified roundings alone move the losses."""
+    from oracle import awq_oracle as O
+    X = np.asarray(X, dtype=np.float64)
+    Wg = np.asarray(Wg, dtype=np.float64)
+    Wu = np.asarray(Wu, dtype=np.float64)
+    Wd = np.asarray(Wd, dtype=np.float64)
+    rnd = _bf16 if round_operands else (lambda v: np.asarray(v, dtype=np.float64))
+    G, U = X @ Wg.T, X @ Wu.T
+    h_ref = act(G, kind) * U
+    out = []
+    for s in np.asarray(scales, dtype=np.float64):
+        dWg = rnd(O.quantize_restore(Wg, s, group_size) - Wg)
+        dWu = rnd(O.quantize_restore(Wu, s, group_size) - Wu)
+        Eg, Eu = X @ dWg.T, X @ dWu.T
+        dh = rnd(h_ref - act(G + Eg, kind) * (U + Eu))
+        out.append(float(np.mean((dh @ Wd.T) ** 2)))
+    return np.array(out)

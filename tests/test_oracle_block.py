@@ -74,3 +74,22 @@ def test_nonfinite_falls_back_to_ones():
     with np.errstate(invalid="ignore"):
         _, losses, k, best = K.block_search(X, W, W, rng.standard_normal((3, 4)), n_grid=3)
     assert np.all(np.isnan(losses)) and k == 0 and np.all(best == 1.0)
+
+
+def test_bf16_operand_losses_reduce_to_the_block_losses():
+    """Without the operand roundings the difference form equals the block search's losses (the
+    linearity of down_proj); with them, bfloat16 operands that are already exact change nothing."""
+    rng = np.random.default_rng(31)
+    X = rng.standard_normal((24, 128))
+    X[:, 5] *= 30
+    Wg, Wu = rng.standard_normal((64, 128)) * 0.05, rng.standard_normal((64, 128)) * 0.05
+    Wd = rng.standard_normal((16, 64)) * 0.05
+    for kind in (K.ACT_SILU, K.ACT_RELU):
+        scales, losses, _, _ = K.block_search(X, Wg, Wu, Wd, 4, kind)
+        diff = K.block_losses_bf16_operands(X, Wg, Wu, Wd, scales, kind, round_operands=False)
+        np.testing.assert_allclose(diff, losses, rtol=1e-9)
+        rounded = K.block_losses_bf16_operands(X, Wg, Wu, Wd, scales, kind)
+        assert np.all(np.abs(rounded - losses) <= 5e-3 * losses)  # two roundings of 2^-9 each
+    # round to nearest even at the bfloat16 precision: 1 + 2^-8 is a tie between 1 and 1 + 2^-7
+    assert K._bf16(np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -9)])).tolist() == \
+        [1.0, 1.0 + 2.0 ** -6, -1.0]
