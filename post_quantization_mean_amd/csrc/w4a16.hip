@@ -15,6 +15,8 @@
 // assignment of the contraction index to (lane group, element) works as long as A and B use the same
 // one; here lane group kq of sub-step t of a 128-wide group holds k = 32 kq + 8 t + e, so that a lane's
 // codes for a whole group are one 16-byte load (32 nibbles) and its activations 64 contiguous bytes.
+#include <type_traits>
+
 #include "w4a16.h"
 #include "device_common.h"
 #include "lds_dma.h"
@@ -333,13 +335,276 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_big_kernel(const uint16_t* 
   }
 }
 
+// Prefill at scale (thousands of tokens): the error GEMM's tiling with the weight operand produced in
+// LDS. A block computes 256 tokens x 256 output rows; four waves as 2 x 2, each 128 x 128 as 4 x 4
+// accumulators of v_mfma_f32_32x32x16_{bf16,f16}. A K step is 64 inputs: the activations (256 rows
+// x 128 bytes) move global -> LDS by buffer DMA, and the weights are dequantized by the block's
+// threads, one output row each (64 codes, the group's float16 step and zero point), into the same
+// swizzled LDS layout, so every weight is dequantized once per 256 tokens and read by two waves.
+// Two LDS stages: the activations of step kt+2 are loaded, and its weights dequantized, into the
+// stage step kt has just freed, while step kt's last and step kt+1's first sub-steps run; the
+// codes of step kt+3 are loaded into registers a step before their dequantization. Tiles in the super-block order of
+// the error GEMM (one block per compute unit at a time).
+constexpr int kTileTok = 256, kTileRows = 256, kTileKB = 128;
+constexpr int kTileStage = (kTileTok + kTileRows) * kTileKB;  // 64 KiB
+constexpr int64_t kTileMinTokens = 1024;
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+template <int KIND, bool ZC>
+__device__ __forceinline__ void mma32(const uint4& a, const uint4& b, f32x16& c) {
+  const f32x16 zero = {};
+  if constexpr (KIND == 0)
+    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                ZC ? zero : c, 0, 0, 0);
+  else
+    c = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b),
+                                               ZC ? zero : c, 0, 0, 0);
+}
+
+// Byte j of a word as a float (v_cvt_f32_ubyte{j}: one instruction; written out because the compiler
+// otherwise extracts the byte with a bit-field instruction first when it knows the upper bits are zero).
+template <int J>
+__device__ __forceinline__ float ubyte_f32(uint32_t w) {
+  float f;
+  if constexpr (J == 0) asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(f) : "v"(w));
+  else if constexpr (J == 1) asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(f) : "v"(w));
+  else if constexpr (J == 2) asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(f) : "v"(w));
+  else asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(f) : "v"(w));
+  return f;
+}
+
+// 8 codes (one word: element 2j in the low nibble of byte j, 2j+1 in the high one) -> 8 operands,
+// (q - zero) * step rounded once to the 16-bit type; the low and high nibbles are masked four at a
+// time and each byte converted directly.
+template <int KIND>
+__device__ __forceinline__ uint4 dequant8_bytes(uint32_t w, float st, float nzs) {
+  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+  const float v[8] = {fmaf(ubyte_f32<0>(lo), st, nzs), fmaf(ubyte_f32<0>(hi), st, nzs),
+                      fmaf(ubyte_f32<1>(lo), st, nzs), fmaf(ubyte_f32<1>(hi), st, nzs),
+                      fmaf(ubyte_f32<2>(lo), st, nzs), fmaf(ubyte_f32<2>(hi), st, nzs),
+                      fmaf(ubyte_f32<3>(lo), st, nzs), fmaf(ubyte_f32<3>(hi), st, nzs)};
+  return make_uint4(pack2(v[0], v[1], KIND), pack2(v[2], v[3], KIND), pack2(v[4], v[5], KIND),
+                    pack2(v[6], v[7], KIND));
+}
+
+template <int KIND, typename OutT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void w4a16_tile_kernel(const uint16_t* __restrict__ x, int64_t ld_x, const uint8_t* __restrict__ codes,
+                       const uint16_t* __restrict__ steps, const uint8_t* __restrict__ zeros, int n_tokens,
+                       int d_in, int d_out, OutT* __restrict__ y, int64_t ld_y, int tiles_m, int tiles_n) {
+  constexpr int FM = 4, FN = 4, NR = 8, KB = kTileKB, BM = kTileTok;
+  __shared__ __attribute__((aligned(1024))) char lds[2 * kTileStage];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int tm, tn;
+  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int64_t m0 = (int64_t)tm * kTileTok, n0 = (int64_t)tn * kTileRows;
+  const int G = d_in / kGroup, GZ = (G + 1) / 2;
+  const int k_steps = d_in / 64;  // >= 2
+
+  // activations: DMA load j of wave w covers token rows (4 j + w) * 8 .. + 7 (as the error GEMM's A);
+  // tokens past the end lie outside the descriptor's range and read as zero (their rows are not stored)
+  const int lda_bytes = (int)ld_x * 2;
+  const int rows_a = (int)min((int64_t)kTileTok, (int64_t)n_tokens - m0);
+  const i32x4 ra = make_rsrc(x + m0 * ld_x, (uint32_t)((rows_a - 1) * lda_bytes + d_in * 2));
+  int voff_a[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int row = (4 * j + wave) * 8 + (lane >> 3);
+    voff_a[j] = row * lda_bytes + (((lane & 7) ^ swz(row)) << 4);
+  }
+  const uint32_t lds_base = __builtin_amdgcn_readfirstlane(lds_address(lds));
+  auto dma_a = [&](uint32_t stage, int j, int kstep) {
+    dma_load16(ra, __builtin_amdgcn_readfirstlane(stage + (4 * j + wave) * 8 * KB), voff_a[j], kstep * KB);
+  };
+
+  // weights: thread t dequantizes output row n0 + t; rows past d_out read zero codes, steps and zero
+  // points through range-checked descriptors (the row offset is in the range-checked per-lane offset)
+  const int vrows = (int)max((int64_t)0, min((int64_t)kTileRows, (int64_t)d_out - n0));
+  const int64_t r0 = min(n0, (int64_t)d_out - 1);
+  const __amdgpu_buffer_rsrc_t cr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(codes + r0 * (d_in / 2)), (short)0, vrows * (d_in / 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc((void*)(steps + r0 * G), (short)0,
+                                                                     vrows * G * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t zr = __builtin_amdgcn_make_buffer_rsrc((void*)(zeros + r0 * GZ), (short)0,
+                                                                     vrows * GZ, 0x00020000);
+  const int c_off = tid * (d_in / 2), s_off = tid * G * 2, z_off = tid * GZ;
+  uint4 cw[2][2];           // codes of two K steps (64 each) in flight / in use
+  uint32_t sw[2], zw[2];    // their group's raw float16 step and zero-point byte
+  auto load_codes = [&](int set, int kstep) {
+    cw[set][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(cr, c_off, kstep * 32, 0));
+    cw[set][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(cr, c_off + 16, kstep * 32, 0));
+    sw[set] = __builtin_amdgcn_raw_buffer_load_b16(sr, s_off, (kstep >> 1) * 2, 0);
+    zw[set] = __builtin_amdgcn_raw_buffer_load_b8(zr, z_off, kstep >> 2, 0);
+  };
+  // chunk c (inputs 8 c .. 8 c + 7 of the step) of this thread's row, into the stage's weight rows
+  const uint32_t brow = BM * KB + tid * KB;
+  auto code_word = [&](int set, int c) -> uint32_t {
+    const uint4 u = cw[set][c >> 2];
+    return (c & 3) == 0 ? u.x : (c & 3) == 1 ? u.y : (c & 3) == 2 ? u.z : u.w;
+  };
+  auto dequant_chunk = [&](char* stage, int set, int kstep, int c) {
+    float st, nzs;
+    group_params(sw[set], zw[set], kstep >> 1, st, nzs);
+    *reinterpret_cast<uint4*>(stage + brow + ((c ^ swz(tid)) << 4)) =
+        dequant8_bytes<KIND>(code_word(set, c), st, nzs);
+  };
+  // the same in halves into registers (a half-chunk is ~13 VALU instructions, less than a pair of
+  // MFMAs covers), written to LDS once the stage is free
+  uint32_t dq[8][4];
+  float dq_st = 0.f, dq_nzs = 0.f;
+  auto dequant_half = [&](int set, int kstep, int h) {  // h = 2 c + half, 0 .. 15
+    if (h == 0) group_params(sw[set], zw[set], kstep >> 1, dq_st, dq_nzs);
+    const int c = h >> 1, j0 = (h & 1) * 2;
+    const uint32_t wd = code_word(set, c);
+    const uint32_t lo = wd & 0x0F0F0F0Fu, hi = (wd >> 4) & 0x0F0F0F0Fu;
+    if (j0 == 0) {
+      dq[c][0] = pack2(fmaf(ubyte_f32<0>(lo), dq_st, dq_nzs), fmaf(ubyte_f32<0>(hi), dq_st, dq_nzs), KIND);
+      dq[c][1] = pack2(fmaf(ubyte_f32<1>(lo), dq_st, dq_nzs), fmaf(ubyte_f32<1>(hi), dq_st, dq_nzs), KIND);
+    } else {
+      dq[c][2] = pack2(fmaf(ubyte_f32<2>(lo), dq_st, dq_nzs), fmaf(ubyte_f32<2>(hi), dq_st, dq_nzs), KIND);
+      dq[c][3] = pack2(fmaf(ubyte_f32<3>(lo), dq_st, dq_nzs), fmaf(ubyte_f32<3>(hi), dq_st, dq_nzs), KIND);
+    }
+  };
+  auto write_chunk = [&](char* stage, int c) {
+    *reinterpret_cast<uint4*>(stage + brow + ((c ^ swz(tid)) << 4)) = make_uint4(dq[c][0], dq[c][1], dq[c][2], dq[c][3]);
+  };
+
+  const int wm = wave >> 1, wn = wave & 1;
+  const int fr = lane & 31, fh = lane >> 5;
+  const int ra_off = (wm * 128 + fr) * KB;
+  const int rb_off = BM * KB + (wn * 128 + fr) * KB;
+  int slot[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) slot[q] = ((2 * q + fh) ^ swz(fr)) << 4;
+  f32x16 acc[FM][FN];
+  auto frag = [&](const char* stage, int sl, int r) -> uint4 {
+    const int off = r < FM ? ra_off + r * 32 * KB : rb_off + (r - FM) * 32 * KB;
+    return *reinterpret_cast<const uint4*>(stage + off + sl);
+  };
+  // one sub-step: 16 MFMAs on `use` while the next sub-step's fragments are read (if `reads`); after
+  // MFMA i of the 16, aux(i): at most one load, one LDS write or half a chunk of dequantization
+  auto substep = [&](auto zc, const uint4 (&use)[NR], uint4 (&nxt)[NR], const char* src, int sl, bool reads,
+                     auto aux) {
+    constexpr bool ZC = decltype(zc)::value;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      const int fm = g >> 1, fn = (g & 1) * 2;
+      mma32<KIND, ZC>(use[fm], use[FM + fn], acc[fm][fn]);
+      __builtin_amdgcn_sched_barrier(0);
+      aux(2 * g);
+      if (reads) nxt[g] = frag(src, sl, g);
+      __builtin_amdgcn_sched_barrier(0);
+      mma32<KIND, ZC>(use[fm], use[FM + fn + 1], acc[fm][fn + 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      aux(2 * g + 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  const std::false_type acc_in{};
+  const std::true_type acc_zero{};
+  auto none = [](int) {};
+
+  // prologue: stage 0 (activations and weights) into buffer 0, stage 1 into buffer 1, codes of step 2
+  // in flight
+  char* const buf[2] = {lds, lds + kTileStage};
+  const uint32_t bufa[2] = {lds_base, lds_base + kTileStage};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) dma_a(bufa[0], j, 0);
+  load_codes(0, 0);
+  load_codes(1, 1);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+#pragma unroll
+  for (int c = 0; c < 8; ++c) dequant_chunk(buf[0], 0, 0, c);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) dma_a(bufa[1], j, 1);
+#pragma unroll
+  for (int c = 0; c < 8; ++c) dequant_chunk(buf[1], 1, 1, c);
+  if (k_steps > 2) load_codes(0, 2);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __syncthreads();
+  uint4 f0[NR], f1[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) f0[r] = frag(buf[0], slot[0], r);
+  substep(acc_zero, f0, f1, buf[0], slot[1], true, none);
+
+  // step kt: B C | barrier | D A' — D loads the activations of step kt+2 into the buffer of step kt
+  // (freed by the barrier), A' dequantizes step kt+2's weights into it and loads the codes of step
+  // kt+3.
+  // The parity of kt (buffer and codes register set) is a template argument: register arrays indexed
+  // at run time would be placed in scratch memory.
+  auto step = [&](int kt, auto parity) {
+    constexpr int P = decltype(parity)::value;
+    char* cur = buf[P];
+    char* nxt = buf[P ^ 1];
+    const bool pre2 = kt + 2 < k_steps, pre3 = kt + 3 < k_steps;
+    // B, C: step kt+2's weights dequantized into registers (its codes arrived a step ago)
+    // (16 half-chunks over the 32 MFMAs of B and C: one per pair of MFMAs)
+    substep(acc_in, f1, f0, cur, slot[2], true, [&](int i) {
+      if (pre2 && (i & 1) == 0) dequant_half(P, kt + 2, i >> 1);
+    });
+    substep(acc_in, f0, f1, cur, slot[3], true, [&](int i) {
+      if (pre2 && (i & 1) == 0) dequant_half(P, kt + 2, 8 + (i >> 1));
+    });
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();
+    // D: its activations into the freed buffer; A': its weights written there, and the codes of step
+    // kt+3 requested (a whole step ahead of their dequantization)
+    substep(acc_in, f1, f0, nxt, slot[0], true, [&](int i) {
+      if (pre2 && (i & 1) == 0) dma_a(bufa[P], i >> 1, kt + 2);
+    });
+    substep(acc_in, f0, f1, nxt, slot[1], true, [&](int i) {
+      if (i == 0 && pre3) load_codes(P ^ 1, kt + 3);
+      if (pre2 && (i & 1) == 1) write_chunk(cur, i >> 1);
+    });
+  };
+  const std::integral_constant<int, 0> even{};
+  const std::integral_constant<int, 1> odd{};
+  // k_steps = d_in / 64 is even: steps 0 .. k_steps - 2 in pairs and one, then the last (odd) one
+  int kt = 0;
+  for (; kt + 2 < k_steps - 1; kt += 2) {
+    step(kt, even);
+    step(kt + 1, odd);
+  }
+  step(kt, even);
+  {  // the last step (k_steps - 1, odd): B C D
+    const char* cur = buf[1];
+    substep(acc_in, f1, f0, cur, slot[2], true, none);
+    substep(acc_in, f0, f1, cur, slot[3], true, none);
+    substep(acc_in, f1, f0, cur, slot[0], false, none);
+  }
+
+  // element e of accumulator (i, j) in lane l: token 32 i + 8 (e / 4) + 4 (l / 32) + e % 4 of the
+  // wave's 128, output row 32 j + l % 32 of its 128
+  const int64_t t_w = m0 + wm * 128, f_w = n0 + wn * 128;
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int64_t f = f_w + 32 * j + fr;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t t = t_w + 32 * i + 8 * (e >> 2) + 4 * fh + (e & 3);
+        if (t < n_tokens && f < d_out) y[t * ld_y + f] = to_out<OutT>(acc[i][j][e], KIND);
+      }
+    }
+}
+
 template <int KIND, typename OutT>
 hipError_t launch_kind(const void* x, int64_t ld_x, const uint8_t* codes, const uint16_t* steps,
                        const uint8_t* zeros, int n_tokens, int d_in, int d_out, void* y, int64_t ld_y, bool big,
                        hipStream_t st) {
   const uint16_t* xp = static_cast<const uint16_t*>(x);
   OutT* yp = static_cast<OutT*>(y);
-  if (big) {
+  const int64_t tiles64 =
+      ((int64_t)(n_tokens + kTileTok - 1) / kTileTok) * ((int64_t)(d_out + kTileRows - 1) / kTileRows);
+  if (big && n_tokens >= kTileMinTokens && tiles64 <= 0x7FFFFFFF) {
+    const int tiles_m = (n_tokens + kTileTok - 1) / kTileTok, tiles_n = (d_out + kTileRows - 1) / kTileRows;
+    hipLaunchKernelGGL((w4a16_tile_kernel<KIND, OutT>), dim3((unsigned)(tiles_m * tiles_n)), dim3(kThreads), 0, st,
+                       xp, ld_x, codes, steps, zeros, n_tokens, d_in, d_out, yp, ld_y, tiles_m, tiles_n);
+  } else if (big) {
     const unsigned gy = (unsigned)((n_tokens + kBigTokens - 1) / kBigTokens);
     if (n_tokens > kMidMaxTokens)
       hipLaunchKernelGGL((w4a16_big_kernel<KIND, OutT, kBigNJ>), dim3((unsigned)((d_out + 64 * kBigNJ - 1) / (64 * kBigNJ)), gy),

@@ -111,6 +111,20 @@ def test_strided_activations_and_output(B):
     assert torch.all(y_full[:, 48:] == -7.0)  # outside ld_y's used columns nothing is written
 
 
+def test_strided_operands_tile_kernel(B):
+    # 1100 tokens (the 256 x 256 tile kernel), activations and output with row pitches beyond their widths
+    rng = np.random.default_rng(78)
+    x, codes, sb, zp = _exact_case(rng, 1100, 384, 300)
+    xt_full = torch.zeros((1100, 392), dtype=torch.bfloat16, device="cuda")
+    xt_full[:, :384] = _x_torch(x, "bf16")
+    y_full = torch.full((1100, 320), -7.0, dtype=torch.float32, device="cuda")
+    B.awq_w4a16_gemm(xt_full[:, :384], *_dev(codes, sb, zp), y=y_full[:, :300])
+    torch.cuda.synchronize()
+    yref = Q.w4a16_matmul(x, codes, sb, zp, "bf16")
+    assert np.array_equal(y_full[:, :300].cpu().numpy().astype(np.float64), yref)
+    assert torch.all(y_full[:, 300:] == -7.0)
+
+
 def _chain(B, wl, parts, n_tokens_use):
     """search -> pack -> float16 export on the GPU; returns device export + host copies."""
     x, w = make_x(wl), make_w(wl)

@@ -1,5 +1,6 @@
-"""Host model of the many-token W4A16 kernel's buffer addressing (csrc/w4a16.hip,
-``w4a16_big_kernel``): every load the hardware may perform stays inside its tensor.
+"""Host model of the many-token W4A16 kernels' buffer addressing (csrc/w4a16.hip,
+``w4a16_big_kernel`` and the 256 x 256 ``w4a16_tile_kernel``): every load the hardware may perform
+stays inside its tensor.
 
 A raw buffer load (stride 0) returns zero without touching memory when its per-lane offset is at
 or past the descriptor's ``num_records``; the scalar offset is added to the address but is not part
@@ -99,3 +100,59 @@ def test_activation_loads_stay_inside(n_tokens, d_in, ld_x):
 def test_model_detects_row_steps_outside_the_range_check():
     # with the 16-row step in the scalar offset, rows 32..63 of a 17-row matrix would be read
     assert _check_rows(2049, 128, 17, row_step_in_voffset=False) > 0
+
+
+# ------------------------------------------------------------------ the 256 x 256 tile kernel (>= 1024 tokens)
+
+TILE = 256
+
+
+def _swz(row):
+    return (row & 7) ^ ((row >> 3) & 1)
+
+
+def _check_tile(n_tokens, d_in, d_out, ld_x):
+    """Activation DMA (8 loads per wave and K step, the row in the per-lane offset, the K step in the
+    scalar one) and the per-thread codes / step / zero-point loads of every tile."""
+    x_bytes = ((n_tokens - 1) * ld_x + d_in) * 2
+    G, GZ = d_in // 128, (d_in // 128 + 1) // 2
+    k_steps = d_in // 64
+    lane = np.arange(64)
+    tid = np.arange(256)
+    bad = 0
+    for tm in range((n_tokens + TILE - 1) // TILE):
+        m0 = tm * TILE
+        rows_a = min(TILE, n_tokens - m0)
+        base = m0 * ld_x * 2
+        nrec = (rows_a - 1) * ld_x * 2 + d_in * 2
+        for wave in range(4):
+            for j in range(8):
+                row = (4 * j + wave) * 8 + (lane >> 3)
+                voff = row * ld_x * 2 + (((lane & 7) ^ _swz(row)) << 4)
+                live = voff < nrec
+                for ks in range(k_steps):
+                    lo = base + voff + ks * 128
+                    bad += int(np.sum(live & ((lo < 0) | (lo + 16 > x_bytes))))
+    for tn in range((d_out + TILE - 1) // TILE):
+        n0 = tn * TILE
+        vrows = max(0, min(TILE, d_out - n0))
+        r0 = min(n0, d_out - 1)
+        for row_bytes, inrow, size, soffs in (
+                (d_in // 2, 0, 16, [ks * 32 for ks in range(k_steps)]),
+                (d_in // 2, 16, 16, [ks * 32 for ks in range(k_steps)]),
+                (G * 2, 0, 2, [(ks >> 1) * 2 for ks in range(k_steps)]),
+                (GZ, 0, 1, [ks >> 2 for ks in range(k_steps)])):
+            total = d_out * row_bytes
+            voff = tid * row_bytes + inrow
+            live = voff < vrows * row_bytes
+            for so in soffs:
+                lo = r0 * row_bytes + voff + so
+                bad += int(np.sum(live & ((lo < 0) | (lo + size > total))))
+    return bad
+
+
+@pytest.mark.parametrize("n_tokens,d_in,d_out,ld_x", [
+    (1024, 256, 300, 256), (1300, 384, 520, 384), (2049, 128, 17, 128), (1100, 384, 300, 392),
+    (4096, 4096, 12288, 4096), (1024, 11008, 4096, 11008)])
+def test_tile_kernel_loads_stay_inside(n_tokens, d_in, d_out, ld_x):
+    assert _check_tile(n_tokens, d_in, d_out, ld_x) == 0
