@@ -341,10 +341,10 @@ __global__ __launch_bounds__(kThreads, 2) void w4a16_big_kernel(const uint16_t* 
 // x 128 bytes) move global -> LDS by buffer DMA, and the weights are dequantized by the block's
 // threads, one output row each (64 codes, the group's float16 step and zero point), into the same
 // swizzled LDS layout, so every weight is dequantized once per 256 tokens and read by two waves.
-// Two LDS stages: the activations of step kt+2 are loaded, and its weights dequantized, into the
-// stage step kt has just freed, while step kt's last and step kt+1's first sub-steps run; the
-// codes of step kt+3 are loaded into registers a step before their dequantization. Tiles in the super-block order of
-// the error GEMM (one block per compute unit at a time).
+// Two LDS stages: the activations of step kt+2 are loaded into the stage step kt has just freed, and
+// its weights dequantized there, spread over the four sub-steps that follow (half a chunk of eight
+// weights per four MFMAs); each step's codes are requested a step before their dequantization
+// begins. Tiles in the super-block order of the error GEMM (one block per compute unit at a time).
 constexpr int kTileTok = 256, kTileRows = 256, kTileKB = 128;
 constexpr int kTileStage = (kTileTok + kTileRows) * kTileKB;  // 64 KiB
 constexpr int64_t kTileMinTokens = 1024;
@@ -386,6 +386,19 @@ __device__ __forceinline__ uint4 dequant8_bytes(uint32_t w, float st, float nzs)
                       fmaf(ubyte_f32<3>(lo), st, nzs), fmaf(ubyte_f32<3>(hi), st, nzs)};
   return make_uint4(pack2(v[0], v[1], KIND), pack2(v[2], v[3], KIND), pack2(v[4], v[5], KIND),
                     pack2(v[6], v[7], KIND));
+}
+
+// group_params reading only the zero-point byte's low 8 bits (one byte-to-float conversion, the nibble
+// then split off in exact float arithmetic): a byte loaded in one loop iteration and used in the next
+// then needs no zero extension, which the compiler would otherwise place at the loop head and wait
+// there for the load in flight
+__device__ __forceinline__ void tile_group_params(uint32_t step_bits, uint32_t zbyte, int g, float& st, float& nzs) {
+  const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)step_bits);
+  const float zb = (float)(zbyte & 0xFFu);           // 0 .. 255
+  const float zhi = __builtin_floorf(zb * 0.0625f);  // high nibble (exact)
+  const float z = (g & 1) ? zhi : __builtin_fmaf(-16.f, zhi, zb);
+  st = s;
+  nzs = -z * s;  // exact: 4-bit integer times an 11-bit mantissa
 }
 
 template <int KIND, typename OutT>
@@ -445,31 +458,44 @@ void w4a16_tile_kernel(const uint16_t* __restrict__ x, int64_t ld_x, const uint8
     const uint4 u = cw[set][c >> 2];
     return (c & 3) == 0 ? u.x : (c & 3) == 1 ? u.y : (c & 3) == 2 ? u.z : u.w;
   };
-  auto dequant_chunk = [&](char* stage, int set, int kstep, int c) {
-    float st, nzs;
-    group_params(sw[set], zw[set], kstep >> 1, st, nzs);
+  float gst[2], gnzs[2];  // the group's step and -zero * step for the step whose codes are in set 0 / 1
+  auto params = [&](int set, int kstep) { tile_group_params(sw[set], zw[set], kstep >> 1, gst[set], gnzs[set]); };
+  auto dequant_chunk = [&](char* stage, int set, int c) {
     *reinterpret_cast<uint4*>(stage + brow + ((c ^ swz(tid)) << 4)) =
-        dequant8_bytes<KIND>(code_word(set, c), st, nzs);
+        dequant8_bytes<KIND>(code_word(set, c), gst[set], gnzs[set]);
   };
-  // the same in halves into registers (a half-chunk is ~13 VALU instructions, less than a pair of
-  // MFMAs covers), written to LDS once the stage is free
-  uint32_t dq[8][4];
-  float dq_st = 0.f, dq_nzs = 0.f;
-  auto dequant_half = [&](int set, int kstep, int h) {  // h = 2 c + half, 0 .. 15
-    if (h == 0) group_params(sw[set], zw[set], kstep >> 1, dq_st, dq_nzs);
-    const int c = h >> 1, j0 = (h & 1) * 2;
-    const uint32_t wd = code_word(set, c);
-    const uint32_t lo = wd & 0x0F0F0F0Fu, hi = (wd >> 4) & 0x0F0F0F0Fu;
-    if (j0 == 0) {
-      dq[c][0] = pack2(fmaf(ubyte_f32<0>(lo), dq_st, dq_nzs), fmaf(ubyte_f32<0>(hi), dq_st, dq_nzs), KIND);
-      dq[c][1] = pack2(fmaf(ubyte_f32<1>(lo), dq_st, dq_nzs), fmaf(ubyte_f32<1>(hi), dq_st, dq_nzs), KIND);
+  // the same as a pipeline of eight parts of at most four VALU instructions, one part after each MFMA
+  // (a chunk per eight MFMAs): the parts' dependency chains span several MFMAs instead of stalling
+  // the issue of the next one; part 7 writes the chunk to LDS
+  uint32_t dlo = 0, dhi = 0, dq[4];
+  float dv[4];
+  auto dequant_part = [&](char* stage, int set, int c, int m) {
+    const float st = gst[set], nzs = gnzs[set];
+    if (m == 0) {
+      const uint32_t wd = code_word(set, c);
+      dlo = wd & 0x0F0F0F0Fu;
+      dhi = (wd >> 4) & 0x0F0F0F0Fu;
+    } else if (m == 1) {
+      dv[0] = fmaf(ubyte_f32<0>(dlo), st, nzs);
+      dv[1] = fmaf(ubyte_f32<0>(dhi), st, nzs);
+    } else if (m == 2) {
+      dq[0] = pack2(dv[0], dv[1], KIND);
+      dv[2] = ubyte_f32<1>(dlo);
+      dv[3] = ubyte_f32<1>(dhi);
+    } else if (m == 3) {
+      dq[1] = pack2(fmaf(dv[2], st, nzs), fmaf(dv[3], st, nzs), KIND);
+    } else if (m == 4) {
+      dv[0] = fmaf(ubyte_f32<2>(dlo), st, nzs);
+      dv[1] = fmaf(ubyte_f32<2>(dhi), st, nzs);
+    } else if (m == 5) {
+      dq[2] = pack2(dv[0], dv[1], KIND);
+      dv[2] = ubyte_f32<3>(dlo);
+      dv[3] = ubyte_f32<3>(dhi);
+    } else if (m == 6) {
+      dq[3] = pack2(fmaf(dv[2], st, nzs), fmaf(dv[3], st, nzs), KIND);
     } else {
-      dq[c][2] = pack2(fmaf(ubyte_f32<2>(lo), dq_st, dq_nzs), fmaf(ubyte_f32<2>(hi), dq_st, dq_nzs), KIND);
-      dq[c][3] = pack2(fmaf(ubyte_f32<3>(lo), dq_st, dq_nzs), fmaf(ubyte_f32<3>(hi), dq_st, dq_nzs), KIND);
+      *reinterpret_cast<uint4*>(stage + brow + ((c ^ swz(tid)) << 4)) = make_uint4(dq[0], dq[1], dq[2], dq[3]);
     }
-  };
-  auto write_chunk = [&](char* stage, int c) {
-    *reinterpret_cast<uint4*>(stage + brow + ((c ^ swz(tid)) << 4)) = make_uint4(dq[c][0], dq[c][1], dq[c][2], dq[c][3]);
   };
 
   const int wm = wave >> 1, wn = wave & 1;
@@ -507,8 +533,9 @@ void w4a16_tile_kernel(const uint16_t* __restrict__ x, int64_t ld_x, const uint8
   const std::true_type acc_zero{};
   auto none = [](int) {};
 
-  // prologue: stage 0 (activations and weights) into buffer 0, stage 1 into buffer 1, codes of step 2
-  // in flight
+  // prologue: stage 0 (activations and weights) into buffer 0; stage 1's activations and the first
+  // half of its weights into buffer 1 (the second half is done by step 0's first two sub-steps); the
+  // codes of step 2 requested
   char* const buf[2] = {lds, lds + kTileStage};
   const uint32_t bufa[2] = {lds_base, lds_base + kTileStage};
 #pragma unroll
@@ -516,13 +543,17 @@ void w4a16_tile_kernel(const uint16_t* __restrict__ x, int64_t ld_x, const uint8
   load_codes(0, 0);
   load_codes(1, 1);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  params(0, 0);
 #pragma unroll
-  for (int c = 0; c < 8; ++c) dequant_chunk(buf[0], 0, 0, c);
+  for (int c = 0; c < 8; ++c) dequant_chunk(buf[0], 0, c);
 #pragma unroll
   for (int j = 0; j < 8; ++j) dma_a(bufa[1], j, 1);
+  params(1, 1);
 #pragma unroll
-  for (int c = 0; c < 8; ++c) dequant_chunk(buf[1], 1, 1, c);
-  if (k_steps > 2) load_codes(0, 2);
+  for (int c = 0; c < 4; ++c) dequant_chunk(buf[1], 1, c);
+  // (past the last step the last step's codes are loaded again and not used: the loads stay
+  // unconditional, so no register is carried around the loop by a branch and copied while in flight)
+  load_codes(0, min(2, k_steps - 1));
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __syncthreads();
   uint4 f0[NR], f1[NR];
@@ -530,34 +561,35 @@ void w4a16_tile_kernel(const uint16_t* __restrict__ x, int64_t ld_x, const uint8
   for (int r = 0; r < NR; ++r) f0[r] = frag(buf[0], slot[0], r);
   substep(acc_zero, f0, f1, buf[0], slot[1], true, none);
 
-  // step kt: B C | barrier | D A' — D loads the activations of step kt+2 into the buffer of step kt
-  // (freed by the barrier), A' dequantizes step kt+2's weights into it and loads the codes of step
-  // kt+3.
+  // step kt: B C | barrier | D A'. The weights of step kt+1 are finished (chunks 4..7) in B and C,
+  // into its stage (read only after the barrier); D loads the activations of step kt+2 into the stage
+  // of step kt (freed by the barrier), and D and A' dequantize chunks 0..3 of step kt+2's weights into
+  // it; A' requests the codes of step kt+3 (into the register set B and C have just finished with).
+  // Codes are thus requested before the barrier that precedes their first use, whose wait covers
+  // them: the load counter completes in issue order, so a wait for codes requested after an
+  // activation DMA would also wait for that DMA, long before its barrier needs it.
   // The parity of kt (buffer and codes register set) is a template argument: register arrays indexed
   // at run time would be placed in scratch memory.
   auto step = [&](int kt, auto parity) {
     constexpr int P = decltype(parity)::value;
     char* cur = buf[P];
     char* nxt = buf[P ^ 1];
-    const bool pre2 = kt + 2 < k_steps, pre3 = kt + 3 < k_steps;
-    // B, C: step kt+2's weights dequantized into registers (its codes arrived a step ago)
-    // (16 half-chunks over the 32 MFMAs of B and C: one per pair of MFMAs)
-    substep(acc_in, f1, f0, cur, slot[2], true, [&](int i) {
-      if (pre2 && (i & 1) == 0) dequant_half(P, kt + 2, i >> 1);
-    });
-    substep(acc_in, f0, f1, cur, slot[3], true, [&](int i) {
-      if (pre2 && (i & 1) == 0) dequant_half(P, kt + 2, 8 + (i >> 1));
-    });
+    const bool pre2 = kt + 2 < k_steps;
+    // a part of a chunk after every MFMA: B chunks 4, 5 and C chunks 6, 7 of step kt+1
+    substep(acc_in, f1, f0, cur, slot[2], true, [&](int i) { dequant_part(nxt, P ^ 1, 4 + (i >> 3), i & 7); });
+    substep(acc_in, f0, f1, cur, slot[3], true, [&](int i) { dequant_part(nxt, P ^ 1, 6 + (i >> 3), i & 7); });
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
-    // D: its activations into the freed buffer; A': its weights written there, and the codes of step
-    // kt+3 requested (a whole step ahead of their dequantization)
+    // D: step kt+2's activations into the freed stage (a load per pair of MFMAs) and its weight
+    // chunks 0, 1; A': the codes of step kt+3 and chunks 2, 3
     substep(acc_in, f1, f0, nxt, slot[0], true, [&](int i) {
       if (pre2 && (i & 1) == 0) dma_a(bufa[P], i >> 1, kt + 2);
+      if (pre2 && i == 0) params(P, kt + 2);
+      if (pre2) dequant_part(cur, P, i >> 3, i & 7);
     });
     substep(acc_in, f0, f1, nxt, slot[1], true, [&](int i) {
-      if (i == 0 && pre3) load_codes(P ^ 1, kt + 3);
-      if (pre2 && (i & 1) == 1) write_chunk(cur, i >> 1);
+      if (i == 0) load_codes(P ^ 1, min(kt + 3, k_steps - 1));
+      if (pre2) dequant_part(cur, P, 2 + (i >> 3), i & 7);
     });
   };
   const std::integral_constant<int, 0> even{};
