@@ -2,7 +2,9 @@
 
 One step = one whole layer: activation statistic, candidate scales, quantize->delta for every
 candidate, the error GEMM with its fused squared-error epilogue, losses + argmin, and the final
-quantize + pack, each through the C ABI on the current stream. Inputs are generated on the host
+quantize + pack, each through the C ABI on the current stream. Where awq_search_scales would take
+the Gram form of the loss (more tokens than input channels: G = X^T X once, then one quadratic form
+delta G delta^T per candidate), the step does the same: G, float16 delta, the quadratic-form GEMM. Inputs are generated on the host
 (seeded, synthetic) and copied to HBM before timing; outputs and workspaces are preallocated.
 
 Prints one JSON line. `value` = candidate evaluations per second for the whole layer search
@@ -68,11 +70,13 @@ GEMM_SOURCES = ("post_quantization_mean_amd/csrc/err_gemm.hip", "post_quantizati
                 "post_quantization_mean_amd/csrc/lds_dma.h")
 
 
-def measured_traffic(workload_name: str):
-    """HBM bytes per error-GEMM launch from the committed rocprofv3 counter summary (FETCH_SIZE and
-    WRITE_SIZE, scaled by a plain copy's readings), or None when the kernel source has changed
-    since the counters were taken or no summary exists for this workload."""
-    path = os.path.join(ROOT, "profiles", f"error_sse_{workload_name.replace('-', '_')}_traffic.md")
+def measured_traffic(workload_name: str, gram: bool = False):
+    """HBM bytes per launch of the dominant kernel (the error GEMM, or in the Gram form the
+    quadratic-form GEMM) from the committed rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE,
+    scaled by a plain copy's readings), or None when the kernel source has changed since the
+    counters were taken or no summary exists for this workload."""
+    stem = "gram_error_sse" if gram else "error_sse"
+    path = os.path.join(ROOT, "profiles", f"{stem}_{workload_name.replace('-', '_')}_traffic.md")
     if not os.path.exists(path):
         return None
     rec = None
@@ -157,6 +161,8 @@ def main() -> int:
     ap.add_argument("--config", type=int, default=5,
                     help="workload id (5 = 70B down_proj stress, the largest single-GPU layer)")
     ap.add_argument("--cand-per-pass", type=int, default=0, help="candidates per GEMM launch (0 = all)")
+    ap.add_argument("--loss-form", choices=("auto", "direct", "gram"), default="auto",
+                    help="the error GEMM or the Gram form of the loss (auto: what awq_search_scales chooses)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="also time the step captured once as a HIP graph")
     ap.add_argument("--variant-searches", action="store_true",
@@ -204,7 +210,20 @@ def main() -> int:
     act = torch.empty(wl.d_in, dtype=torch.float64, device=dev)
     ws_act = torch.empty(B.awq_act_stats_workspace_bytes(dt, wl.n_tokens, wl.d_in), dtype=torch.uint8, device=dev)
     cand = torch.empty((wl.n_grid, wl.d_in), dtype=torch.float64, device=dev)
-    delta = torch.empty((cpp, wl.d_out, wl.d_in), dtype=x.dtype, device=dev)
+    if args.loss_form == "auto":
+        gram = B.awq_search_loss_form(dt, wl.n_tokens, wl.d_in, wl.d_out, wl.n_grid) == B.AWQ_LOSS_GRAM
+    else:
+        gram = args.loss_form == "gram"
+    if gram:
+        # the Gram form: float16 G, its exponent and X^T / float32 G workspace; delta in float16
+        g16 = torch.empty((wl.d_in, wl.d_in), dtype=torch.float16, device=dev)
+        gexp = torch.empty(1, dtype=torch.int32, device=dev)
+        ws_gram = torch.empty(B.awq_gram_workspace_bytes(wl.n_tokens, wl.d_in), dtype=torch.uint8, device=dev)
+        dexp = torch.empty(cpp + 1, dtype=torch.int32, device=dev)
+        delta16 = torch.empty((cpp, wl.d_out, wl.d_in), dtype=torch.float16, device=dev)
+        delta = delta16.view(torch.bfloat16)  # the same bytes, for the bfloat16 delta timed alone below
+    else:
+        delta = torch.empty((cpp, wl.d_out, wl.d_in), dtype=x.dtype, device=dev)
     sse = torch.empty((wl.n_grid, n_tiles), dtype=torch.float64, device=dev)
     losses = torch.empty(wl.n_grid, dtype=torch.float64, device=dev)
     best = torch.empty(wl.d_in, dtype=torch.float64, device=dev)
@@ -225,14 +244,26 @@ def main() -> int:
             mark("act0")
         B.awq_act_stats(x, act, ws_act)
         B.awq_candidate_scales(act, wl.n_grid, cand)
+        if gram:
+            if timed:
+                mark("gram0")
+            B.awq_gram(x, g16, gexp, ws_gram)
+            if timed:
+                mark("gram1")
         for k0 in range(0, wl.n_grid, cpp):
             nk = min(cpp, wl.n_grid - k0)
             if timed:
                 mark("q0")
-            B.awq_quant_delta(w_parts, cand[k0:k0 + nk], wl.group_size, delta[:nk])
+            if gram:
+                B.awq_quant_delta_f16(w_parts, cand[k0:k0 + nk], wl.group_size, delta16[:nk], dexp)
+            else:
+                B.awq_quant_delta(w_parts, cand[k0:k0 + nk], wl.group_size, delta[:nk])
             if timed:
                 mark("g0")
-            B.awq_error_sse(x, delta[:nk], sse[k0:k0 + nk])
+            if gram:
+                B.awq_gram_error_sse(g16, gexp, delta16[:nk], dexp, wl.n_tokens, sse[k0:k0 + nk])
+            else:
+                B.awq_error_sse(x, delta[:nk], sse[k0:k0 + nk])
             if timed:
                 mark("g1")
         B.awq_loss_argmin(sse, wl.n_tokens, wl.d_out, cand, losses, best, info)
@@ -262,9 +293,17 @@ def main() -> int:
     gemm_ms = span("g0", "g1") / n_gemm
     quant_ms = span("q0", "g0") / n_gemm
     pack_ms = span("p0", "p1") / args.steps
-    act_ms = float(sum(ev["act0"][i].elapsed_time(ev["q0"][i * (n_gemm // args.steps)])
+    first = "gram0" if gram else "q0"
+    act_ms = float(sum(ev["act0"][i].elapsed_time(ev[first][i * (1 if gram else n_gemm // args.steps)])
                        for i in range(args.steps))) / args.steps
-    flops_launch = 2.0 * wl.n_tokens * wl.d_in * wl.d_out * min(cpp, wl.n_grid)
+    gram_ms = span("gram0", "gram1") / args.steps if gram else None
+    n_pad = (wl.n_tokens + 63) // 64 * 64
+    # algorithmic flops of one launch of the dominant kernel: the error GEMM's products, or in the
+    # Gram form the quadratic form's delta G products (G itself is timed apart)
+    if gram:
+        flops_launch = 2.0 * wl.d_out * wl.d_in * wl.d_in * min(cpp, wl.n_grid)
+    else:
+        flops_launch = 2.0 * wl.n_tokens * wl.d_in * wl.d_out * min(cpp, wl.n_grid)
     peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
     achieved = flops_launch / (gemm_ms * 1e-3) / 1e12
     esz = 2 if wl.dtype == "bf16" else 4
@@ -314,6 +353,9 @@ def main() -> int:
         "quant_delta": isolated(lambda: B.awq_quant_delta(w_parts, cand[:cpp], wl.group_size, delta[:cpp])),
         "quantize_pack": isolated(lambda: B.awq_quantize_pack(w_parts, best, wl.group_size, pack_out)),
     }
+    if gram:  # the step's own delta: float16 with the per-candidate scales (max |W| pass included)
+        iso_ms["quant_delta_f16"] = isolated(
+            lambda: B.awq_quant_delta_f16(w_parts, cand[:cpp], wl.group_size, delta16[:cpp], dexp))
     # Around the search: the fold of best_scales into the source operator of this layer (the
     # norm weight for a fused norm-linear set, the up_proj rows for a down_proj search), and the
     # float16 / packed-zero export of the pack's output
@@ -434,6 +476,8 @@ def main() -> int:
                 "quantize_pack": p_bytes / (iso_ms["quantize_pack"] * 1e-3) / 1e9,
                 "fold_scales": f_bytes / (iso_ms["fold_scales"] * 1e-3) / 1e9,
                 "export_fp16": e_bytes / (iso_ms["export_fp16"] * 1e-3) / 1e9}
+    if gram:
+        iso_gbps["quant_delta_f16"] = q_bytes / (iso_ms["quant_delta_f16"] * 1e-3) / 1e9
 
     out = {
         "metric": METRIC,
@@ -450,13 +494,20 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": wl.name, "n_tokens": wl.n_tokens, "d_in": wl.d_in, "d_out": wl.d_out,
                    "parts": parts, "group_size": wl.group_size, "n_grid": wl.n_grid, "cand_per_pass": cpp},
-        "roofline": {"bound": "mfma", "kernel": "error_sse_kernel", "achieved": achieved, "peak": peak,
-                     "unit": "TFLOP/s", "frac": achieved / peak, "traffic": measured_traffic(wl.name),
+        "loss_form": "gram" if gram else "direct",
+        "roofline": {"bound": "mfma",
+                     "kernel": "error_sse_kernel<unsigned short, 2> (quadratic form, float16)" if gram
+                     else "error_sse_kernel<unsigned short, 0>",
+                     "achieved": achieved, "peak": peak,
+                     "unit": "TFLOP/s", "frac": achieved / peak, "traffic": measured_traffic(wl.name, gram),
                      "launch_ms": gemm_ms, "flops_per_launch": flops_launch},
         "search_ms": ms_step,
         "error_gemm_tflops": achieved,
         "kernels_ms": {"act_stats+candidate_scales": act_ms, "quant_delta": quant_ms, "error_sse": gemm_ms,
                        "quantize_pack": pack_ms},
+        "gram": None if not gram else {
+            "ms": gram_ms, "note": "X^T, G = X^T X (every 256 x 256 tile, float32), its scale and float16 form",
+            "gram_gemm_tflops": 2.0 * wl.d_in * wl.d_in * n_pad / (gram_ms * 1e-3) / 1e12},
         "hbm_kernels": {"note": "each kernel alone, memory-side cache flushed before every repetition, median of 5; "
                                 "algorithmic bytes / time against 8000 GB/s",
                         "fold_source": src_kind, "ms": iso_ms, "gbps": iso_gbps,

@@ -58,7 +58,7 @@ extern "C" {
 #define AWQ_API
 #endif
 
-#define AWQ_ABI_VERSION 4
+#define AWQ_ABI_VERSION 5
 #define AWQ_MAX_PARTS 8
 #define AWQ_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20) /* device scratch of awq_search_scales_noalloc */
 #define AWQ_GROUP_SIZE 128
@@ -177,6 +177,60 @@ AWQ_API int64_t awq_error_tiles(int64_t n_tokens, int64_t d_out);
 AWQ_API int awq_error_sse(const void* x, int64_t ld_x, const void* delta, int dtype, int64_t n_tokens,
                   int64_t d_in, int64_t d_out, int n_cand, double* tile_sse, void* stream);
 
+/* ------------------------------------------------------------------ a4 in the Gram form */
+
+/* The same losses through the Gram matrix of the activations. By linearity the loss of a ratio is
+ * sum_o ||X delta[o]^T||^2 / (N d_out) (gsyq section 二 target_out - actual_out; bjdmk L(s)), and
+ * ||X v||^2 = v G v^T with G = X^T X: with G formed once, each ratio costs 2 d_out d_in^2 flops
+ * instead of 2 N d_in d_out, fewer when there are more tokens than input channels. G is
+ * accumulated in float32 by the matrix cores from the bfloat16 activations; both operands of the
+ * quadratic form are float16, each scaled by a power of two into float16's range (exact, removed
+ * exactly from the float64 tile sums). awq_search_scales uses this form by itself where it pays
+ * (awq_search_loss_form). */
+typedef enum { AWQ_LOSS_DIRECT = 0, AWQ_LOSS_GRAM = 1 } awq_loss_form;
+
+/* The loss form awq_search_scales (and awq_search_scales_ex with AWQ_QUANT_INT4_GROUP) uses for
+ * these sizes: AWQ_LOSS_GRAM for bfloat16 activations when forming G plus the n_grid quadratic forms
+ * takes under 0.85 of the direct products' flops (and 256 * ceil(n_tokens / 64) * 64 * 2 < 2^31),
+ * else AWQ_LOSS_DIRECT. Host-only. */
+AWQ_API int awq_search_loss_form(int dtype, int64_t n_tokens, int64_t d_in, int64_t d_out, int n_grid);
+
+/* Workspace bytes of awq_gram: X^T padded to a multiple of 64 tokens (bfloat16) and G in float32.
+ * 0 on invalid sizes. */
+AWQ_API size_t awq_gram_workspace_bytes(int64_t n_tokens, int64_t d_in);
+
+/* G = X^T X for bfloat16 activations, written as float16(G * 2^gram_exp[0]); gram_exp[0] is chosen
+ * so that G's largest entry (on its diagonal) scales to at most 2^14.
+ *   x          device, bfloat16 [n_tokens, ld_x] (the rules of awq_act_stats).
+ *   gram       device, float16 bits [d_in, d_in], 16-byte aligned, written.
+ *   gram_exp   device, int32 [1], written.
+ *   workspace  device, >= awq_gram_workspace_bytes(n_tokens, d_in) bytes, 256-byte aligned.
+ * AWQ_ERR_UNSUPPORTED when 256 rows of the padded X^T exceed 32-bit byte offsets. */
+AWQ_API int awq_gram(const void* x, int64_t ld_x, int64_t n_tokens, int64_t d_in, uint16_t* gram,
+                     int32_t* gram_exp, void* workspace, size_t workspace_bytes, void* stream);
+
+/* awq_quant_delta for bfloat16 weights with delta written as float16(delta * 2^delta_exp[k]). Every
+ * quantizer decision is awq_quant_delta's. delta_exp[k] makes a proven bound on |delta_k|,
+ * (1.5 max|W| max(s_k) + 1e-8) / min(s_k) + max|W|, scale to at most 2^14.
+ *   delta      device, float16 bits [n_cand, d_out, d_in], 16-byte aligned, written.
+ *   delta_exp  device, int32 [n_cand + 1], written (the last entry is scratch: max|W|).
+ *   the other arguments as awq_quant_delta (dtype bfloat16). */
+AWQ_API int awq_quant_delta_f16(const void* const* w_parts, const int64_t* part_rows, int n_parts, int64_t d_in,
+                                int group_size, const double* cand_scales, int n_cand, uint16_t* delta,
+                                int32_t* delta_exp, void* stream);
+
+/* Per-tile shares of candidate j's sum_o delta_j[o] G delta_j[o]^T (float16 operands, float32
+ * accumulation, float64 tile sums, the scales removed), laid out as awq_error_sse's tile_sse so
+ * that awq_loss_argmin gives the losses: candidate j's ceil(d_in/256) * ceil(d_out/256) tile sums
+ * then zeros, awq_error_tiles(n_tokens, d_out) entries per candidate (n_tokens >= d_in, else
+ * AWQ_ERR_SHAPE).
+ *   gram, gram_exp    as written by awq_gram.
+ *   delta, delta_exp  as written by awq_quant_delta_f16.
+ *   tile_sse          device, float64 [n_cand, awq_error_tiles(n_tokens, d_out)], written. */
+AWQ_API int awq_gram_error_sse(const uint16_t* gram, const int32_t* gram_exp, const uint16_t* delta,
+                               const int32_t* delta_exp, int n_cand, int64_t n_tokens, int64_t d_in,
+                               int64_t d_out, double* tile_sse, void* stream);
+
 /* ------------------------------------------------------------------ a5: losses and argmin */
 
 /* losses[k] = (sum of tile_sse[k, :], float64, fixed order) / (n_tokens * d_out): the output
@@ -196,12 +250,14 @@ AWQ_API int awq_loss_argmin(const double* tile_sse, int64_t tiles_per_cand, int 
 
 /* Workspace bytes awq_search_scales needs when it evaluates cand_per_pass candidates per
  * GEMM launch (1 <= cand_per_pass <= n_grid; larger passes fill the GPU better and need a
- * delta buffer of cand_per_pass * d_out * d_in elements). 0 on invalid sizes. */
+ * delta buffer of cand_per_pass * d_out * d_in elements), including the Gram form's buffers
+ * (float16 G, X^T and float32 G) when awq_search_loss_form chooses it. 0 on invalid sizes. */
 AWQ_API size_t awq_search_workspace_bytes(int dtype, int64_t n_tokens, int64_t d_in, int64_t d_out,
                                   int group_size, int n_grid, int cand_per_pass);
 
 /* The whole grid search for one layer (or fused set): a2, then a3 + a4 for every pass of
- * cand_per_pass candidates, then a5 (msModelSlim 缩放因子搜索流程, in that order).
+ * cand_per_pass candidates, then a5 (msModelSlim 缩放因子搜索流程, in that order). a4 is the
+ * direct error GEMM or the Gram form, as awq_search_loss_form says for these sizes.
  *   x, ld_x, w_parts, part_rows, n_parts, dtype: as above.
  *   act_mean    device, float64 [d_in] (from awq_act_stats).
  *   cand_scales device, float64 [n_grid, d_in], 16-byte aligned, written (all candidates).

@@ -66,6 +66,11 @@ _SIGNATURES = {
                                 _vp]),
     "awq_mlp_hidden_ref": (_c_int, [_vp, _c_i64, _vp, _vp, _c_i64, _c_i64, _c_i64, _vp, _vp, _vp]),
     "awq_mlp_hidden_delta": (_c_int, [_vp, _c_i64, _vp, _vp, _vp, _vp, _c_int, _c_i64, _c_i64, _c_i64, _vp, _vp]),
+    "awq_search_loss_form": (_c_int, [_c_int, _c_i64, _c_i64, _c_i64, _c_int]),
+    "awq_gram_workspace_bytes": (_c_size, [_c_i64, _c_i64]),
+    "awq_gram": (_c_int, [_vp, _c_i64, _c_i64, _c_i64, _vp, _vp, _vp, _c_size, _vp]),
+    "awq_quant_delta_f16": (_c_int, [_vp, _vp, _c_int, _c_i64, _c_int, _vp, _c_int, _vp, _vp, _vp]),
+    "awq_gram_error_sse": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_i64, _c_i64, _c_i64, _vp, _vp]),
     "awq_search_workspace_bytes_mlp": (_c_size, [_c_i64, _c_i64, _c_i64, _c_i64, _c_int, _c_int]),
     "awq_search_scales_mlp": (_c_int, [_vp, _c_i64, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64, _c_i64, _vp, _c_int,
                                        _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
@@ -264,6 +269,73 @@ def awq_error_sse(x: torch.Tensor, delta: torch.Tensor, tile_sse=None, stream=No
         tile_sse = torch.empty((n_cand, tiles), dtype=torch.float64, device=x.device)
     pt = _buf(tile_sse, "tile_sse", torch.float64, n_cand * tiles, x.device)
     _check(lib.awq_error_sse(px, ld, pd, _dtype_code(x), n, d, d_out, n_cand, pt, _stream(stream)))
+    return tile_sse
+
+
+AWQ_LOSS_DIRECT, AWQ_LOSS_GRAM = 0, 1
+
+
+def awq_search_loss_form(dtype: int, n_tokens: int, d_in: int, d_out: int, n_grid: int) -> int:
+    """AWQ_LOSS_GRAM when awq_search_scales computes the losses through G = X^T X for these sizes."""
+    return load_library().awq_search_loss_form(dtype, n_tokens, d_in, d_out, n_grid)
+
+
+def awq_gram_workspace_bytes(n_tokens: int, d_in: int) -> int:
+    return load_library().awq_gram_workspace_bytes(n_tokens, d_in)
+
+
+def awq_gram(x: torch.Tensor, gram=None, gram_exp=None, workspace=None, stream=None):
+    """G = X^T X of bfloat16 activations as (float16 [d_in, d_in] holding G * 2^e, int32 [1] = e)."""
+    lib = load_library()
+    px, n, d, ld = _x_args(x)
+    if x.dtype != torch.bfloat16:
+        raise TypeError("awq_gram takes bfloat16 activations")
+    gram = torch.empty((d, d), dtype=torch.float16, device=x.device) if gram is None else gram
+    gram_exp = torch.empty(1, dtype=torch.int32, device=x.device) if gram_exp is None else gram_exp
+    nb = lib.awq_gram_workspace_bytes(n, d)
+    ws = _workspace(nb, x.device, workspace)
+    _check(lib.awq_gram(px, ld, n, d, _buf(gram, "gram", torch.float16, d * d, x.device),
+                        _buf(gram_exp, "gram_exp", torch.int32, 1, x.device), _dev(ws, "workspace"), nb,
+                        _stream(stream)))
+    return gram, gram_exp
+
+
+def awq_quant_delta_f16(w_parts, cand_scales: torch.Tensor, group_size: int = GROUP_SIZE, delta=None,
+                        delta_exp=None, stream=None):
+    """a3 for the Gram form: (float16 [n_cand, d_out, d_in] holding delta * 2^e_k, int32 [n_cand + 1]
+    with e_k first)."""
+    lib = load_library()
+    parts, ptrs, rows, d_out = _parts(w_parts, torch.bfloat16)
+    d_in = parts[0].shape[1]
+    n_cand, pc = _cand_arg(cand_scales, d_in)
+    dev = parts[0].device
+    delta = torch.empty((n_cand, d_out, d_in), dtype=torch.float16, device=dev) if delta is None else delta
+    delta_exp = torch.empty(n_cand + 1, dtype=torch.int32, device=dev) if delta_exp is None else delta_exp
+    _check(lib.awq_quant_delta_f16(ptrs, rows, len(parts), d_in, group_size, pc, n_cand,
+                                   _buf(delta, "delta", torch.float16, n_cand * d_out * d_in, dev),
+                                   _buf(delta_exp, "delta_exp", torch.int32, n_cand + 1, dev), _stream(stream)))
+    return delta, delta_exp
+
+
+def awq_gram_error_sse(gram: torch.Tensor, gram_exp: torch.Tensor, delta: torch.Tensor, delta_exp: torch.Tensor,
+                       n_tokens: int, tile_sse=None, stream=None):
+    """a4 in the Gram form: float64 [n_cand, awq_error_tiles(n_tokens, d_out)] tile shares of each
+    candidate's sum_o delta[o] G delta[o]^T (zeros past its own tiles), for awq_loss_argmin."""
+    lib = load_library()
+    if not isinstance(delta, torch.Tensor) or delta.dim() != 3:
+        raise ValueError("delta must be a [n_cand, d_out, d_in] tensor")
+    n_cand, d_out, d_in = delta.shape
+    dev = delta.device
+    if not isinstance(gram, torch.Tensor) or tuple(gram.shape) != (d_in, d_in):
+        raise ValueError(f"gram must be a [{d_in}, {d_in}] matrix")
+    tiles = lib.awq_error_tiles(n_tokens, d_out)
+    tile_sse = torch.empty((n_cand, tiles), dtype=torch.float64, device=dev) if tile_sse is None else tile_sse
+    _check(lib.awq_gram_error_sse(_buf(gram, "gram", torch.float16, d_in * d_in, dev),
+                                  _buf(gram_exp, "gram_exp", torch.int32, 1, dev),
+                                  _buf(delta, "delta", torch.float16, delta.numel(), dev),
+                                  _buf(delta_exp, "delta_exp", torch.int32, n_cand + 1, dev), n_cand, n_tokens, d_in,
+                                  d_out, _buf(tile_sse, "tile_sse", torch.float64, n_cand * tiles, dev),
+                                  _stream(stream)))
     return tile_sse
 
 

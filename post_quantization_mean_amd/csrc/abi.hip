@@ -141,6 +141,29 @@ int check_quantizer(int quantizer) {
 
 // The search composed from its steps. `ratios` == nullptr selects the msModelSlim grid
 // k / n_grid with the main quantizer; otherwise the variant formula and quantizer.
+// The Gram form of the loss (gram.hip): worth it when forming G = X^T X once plus one d_out x d_in x
+// d_in product per ratio costs well under the direct n_grid N x d_in x d_out products, i.e. with more
+// tokens than input channels. bfloat16 activations only (G's products are exact there); the 32-bit
+// tile offsets bound the padded token count.
+bool gram_form(int dtype, int64_t n_tokens, int64_t d_in, int64_t d_out, int n_grid) {
+  if (dtype != AWQ_DTYPE_BF16 || n_tokens < d_in || d_in <= 0 || d_out <= 0 || n_grid < 1) return false;
+  const int64_t n_pad = awq::gram_n_pad(n_tokens);
+  if ((int64_t)awq::kTileM * n_pad * 2 > 0x7FFFFFFF) return false;
+  const double direct = 2.0 * (double)n_tokens * (double)d_in * (double)d_out * n_grid;
+  const double gram = 2.0 * (double)d_in * (double)d_in * (double)n_pad +
+                      2.0 * (double)d_out * (double)d_in * (double)d_in * n_grid;
+  return gram < 0.85 * direct;
+}
+size_t gram_ws_bytes(int64_t n_tokens, int64_t d_in) {
+  const int64_t n_pad = awq::gram_n_pad(n_tokens);
+  return round_up((size_t)d_in * (size_t)n_pad * 2, 256) + round_up((size_t)d_in * (size_t)d_in * 4, 256);
+}
+// the Gram search's buffers beyond delta and tile_sse: float16 G, the exponents, gram_ws_bytes
+size_t gram_search_extra(int64_t n_tokens, int64_t d_in, int cand_per_pass) {
+  return round_up((size_t)d_in * (size_t)d_in * 2, 256) + 256 + round_up(((size_t)cand_per_pass + 1) * 4, 256) +
+         gram_ws_bytes(n_tokens, d_in);
+}
+
 int run_search(const void* x, int64_t ld_x, const void* const* w_parts, const int64_t* part_rows, int n_parts,
                int dtype, int64_t n_tokens, int64_t d_in, const double* act_mean, const double* w_mean,
                const double* ratios, int formula, int quantizer, int n_grid, int cand_per_pass,
@@ -183,6 +206,38 @@ int run_search(const void* x, int64_t ld_x, const void* const* w_parts, const in
   hipError_t e = ratios ? awq::launch_candidate_scales_ex(act_mean, w_mean, d_in, rl, n_grid, formula, cand_scales, st)
                         : awq::launch_candidate_scales(act_mean, d_in, n_grid, cand_scales, st);
   if (e != hipSuccess) return hip_fail(e, "candidate_scales launch");
+  if (quantizer == AWQ_QUANT_INT4_GROUP && gram_form(dtype, n_tokens, d_in, d_out, n_grid)) {
+    // the loss as the quadratic form of G = X^T X (float16 G and delta, power-of-two scales)
+    char* p = ws + round_up((size_t)cand_per_pass * (size_t)d_out * (size_t)d_in * esize(dtype), 256) +
+              round_up((size_t)n_grid * (size_t)tiles * sizeof(double), 256);
+    uint16_t* g16 = reinterpret_cast<uint16_t*>(p);
+    p += round_up((size_t)d_in * (size_t)d_in * 2, 256);
+    int32_t* gexp = reinterpret_cast<int32_t*>(p);
+    p += 256;
+    int32_t* dexp = reinterpret_cast<int32_t*>(p);
+    p += round_up(((size_t)cand_per_pass + 1) * 4, 256);
+    uint16_t* xt = reinterpret_cast<uint16_t*>(p);
+    p += round_up((size_t)d_in * (size_t)awq::gram_n_pad(n_tokens) * 2, 256);
+    float* g32 = reinterpret_cast<float*>(p);
+    uint16_t* d16 = static_cast<uint16_t*>(delta);
+    e = awq::launch_gram(x, ld_x, n_tokens, d_in, xt, g32, g16, gexp, st);
+    if (e != hipSuccess) return hip_fail(e, "gram launch");
+    for (int k0 = 0; k0 < n_grid; k0 += cand_per_pass) {
+      const int nk = n_grid - k0 < cand_per_pass ? n_grid - k0 : cand_per_pass;
+      const double* cs = cand_scales + (int64_t)k0 * d_in;
+      double* ts = tile_sse + (int64_t)k0 * tiles;
+      if ((e = awq::launch_delta_exp(w, d_in, cs, nk, dexp, st)) != hipSuccess) return hip_fail(e, "delta_exp launch");
+      if ((e = awq::launch_quant_delta_f16(w, d_in, cs, nk, d16, dexp, st)) != hipSuccess)
+        return hip_fail(e, "quant_delta_f16 launch");
+      if ((e = awq::launch_fill_f64(ts, (int64_t)nk * tiles, 0.0, st)) != hipSuccess) return hip_fail(e, "fill launch");
+      if ((e = awq::launch_quad_sse(g16, gexp, d16, dexp, nk, d_in, d_out, tiles, ts, st)) != hipSuccess)
+        return hip_fail(e, "gram_error_sse launch");
+    }
+    e = awq::launch_loss_argmin(tile_sse, tiles, n_grid, n_tokens, d_out, cand_scales, d_in, losses,
+                                best_scales, best_info, st);
+    if (e != hipSuccess) return hip_fail(e, "loss_argmin launch");
+    return ok();
+  }
   for (int k0 = 0; k0 < n_grid; k0 += cand_per_pass) {
     const int nk = n_grid - k0 < cand_per_pass ? n_grid - k0 : cand_per_pass;
     const double* cs = cand_scales + (int64_t)k0 * d_in;
@@ -330,7 +385,84 @@ size_t awq_search_workspace_bytes(int dtype, int64_t n_tokens, int64_t d_in, int
     return 0;
   const size_t delta = round_up((size_t)cand_per_pass * (size_t)d_out * (size_t)d_in * esize(dtype), 256);
   const size_t sse = round_up((size_t)n_grid * (size_t)awq_error_tiles(n_tokens, d_out) * sizeof(double), 256);
-  return delta + sse;
+  const size_t gram = gram_form(dtype, n_tokens, d_in, d_out, n_grid) ? gram_search_extra(n_tokens, d_in, cand_per_pass) : 0;
+  return delta + sse + gram;
+}
+
+int awq_search_loss_form(int dtype, int64_t n_tokens, int64_t d_in, int64_t d_out, int n_grid) {
+  return gram_form(dtype, n_tokens, d_in, d_out, n_grid) ? AWQ_LOSS_GRAM : AWQ_LOSS_DIRECT;
+}
+
+size_t awq_gram_workspace_bytes(int64_t n_tokens, int64_t d_in) {
+  if (n_tokens <= 0 || d_in <= 0 || d_in % AWQ_GROUP_SIZE) return 0;
+  return gram_ws_bytes(n_tokens, d_in);
+}
+
+int awq_gram(const void* x, int64_t ld_x, int64_t n_tokens, int64_t d_in, uint16_t* gram, int32_t* gram_exp,
+             void* workspace, size_t workspace_bytes, void* stream) {
+  TRY(check_group(AWQ_GROUP_SIZE, d_in));
+  TRY(check_d_in_bytes(AWQ_DTYPE_BF16, d_in));
+  TRY(check_x(x, AWQ_DTYPE_BF16, n_tokens, d_in, ld_x));
+  if (!gram || !gram_exp) return fail(AWQ_ERR_NULL, "gram or gram_exp is NULL");
+  if (!aligned(gram, 16) || !aligned(gram_exp, 4)) return fail(AWQ_ERR_UNSUPPORTED, "gram is not 16-byte aligned");
+  if ((int64_t)awq::kTileM * awq::gram_n_pad(n_tokens) * 2 > 0x7FFFFFFF)
+    return fail(AWQ_ERR_UNSUPPORTED, "n_tokens %lld too large for 32-bit tile offsets", (long long)n_tokens);
+  const size_t need = gram_ws_bytes(n_tokens, d_in);
+  if (!workspace || workspace_bytes < need)
+    return fail(AWQ_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace ? workspace_bytes : 0, need);
+  if (!aligned(workspace, 256)) return fail(AWQ_ERR_UNSUPPORTED, "workspace is not 256-byte aligned");
+  uint16_t* xt = static_cast<uint16_t*>(workspace);
+  float* g32 = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                        round_up((size_t)d_in * (size_t)awq::gram_n_pad(n_tokens) * 2, 256));
+  hipError_t e = awq::launch_gram(x, ld_x, n_tokens, d_in, xt, g32, gram, gram_exp, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "gram launch");
+  return ok();
+}
+
+int awq_quant_delta_f16(const void* const* w_parts, const int64_t* part_rows, int n_parts, int64_t d_in,
+                        int group_size, const double* cand_scales, int n_cand, uint16_t* delta, int32_t* delta_exp,
+                        void* stream) {
+  TRY(check_group(group_size, d_in));
+  TRY(check_d_in_bytes(AWQ_DTYPE_BF16, d_in));
+  awq::WParts w;
+  TRY(make_parts(w_parts, part_rows, n_parts, AWQ_DTYPE_BF16, d_in, &w));
+  if (!cand_scales || !delta || !delta_exp) return fail(AWQ_ERR_NULL, "cand_scales, delta or delta_exp is NULL");
+  if (n_cand < 1 || n_cand > 65535) return fail(AWQ_ERR_ARG, "n_cand %d outside [1, 65535]", n_cand);
+  if (!aligned(delta, 16)) return fail(AWQ_ERR_UNSUPPORTED, "delta is not 16-byte aligned");
+  if (!aligned(cand_scales, 16)) return fail(AWQ_ERR_UNSUPPORTED, "cand_scales is not 16-byte aligned");
+  if (!aligned(delta_exp, 4)) return fail(AWQ_ERR_UNSUPPORTED, "delta_exp is not 4-byte aligned");
+  hipError_t e = awq::launch_delta_exp(w, d_in, cand_scales, n_cand, delta_exp, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "delta_exp launch");
+  e = awq::launch_quant_delta_f16(w, d_in, cand_scales, n_cand, delta, delta_exp, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "quant_delta_f16 launch");
+  return ok();
+}
+
+int awq_gram_error_sse(const uint16_t* gram, const int32_t* gram_exp, const uint16_t* delta,
+                       const int32_t* delta_exp, int n_cand, int64_t n_tokens, int64_t d_in, int64_t d_out,
+                       double* tile_sse, void* stream) {
+  TRY(check_group(AWQ_GROUP_SIZE, d_in));
+  TRY(check_d_in_bytes(AWQ_DTYPE_BF16, d_in));
+  if (!gram || !gram_exp || !delta || !delta_exp || !tile_sse) return fail(AWQ_ERR_NULL, "a required pointer is NULL");
+  if (!aligned(gram, 16) || !aligned(delta, 16)) return fail(AWQ_ERR_UNSUPPORTED, "gram or delta is not 16-byte aligned");
+  if (!aligned(gram_exp, 4) || !aligned(delta_exp, 4) || !aligned(tile_sse, 8))
+    return fail(AWQ_ERR_UNSUPPORTED, "gram_exp, delta_exp or tile_sse is misaligned");
+  if (d_out <= 0) return fail(AWQ_ERR_SHAPE, "d_out %lld must be > 0", (long long)d_out);
+  if (n_tokens < d_in)
+    return fail(AWQ_ERR_SHAPE, "n_tokens %lld < d_in %lld: the Gram form's tiles do not fit the loss layout",
+                (long long)n_tokens, (long long)d_in);
+  if (n_cand < 1 || n_cand > 65535) return fail(AWQ_ERR_ARG, "n_cand %d outside [1, 65535]", n_cand);
+  if (d_out > ((int64_t)1 << 40) / d_in) return fail(AWQ_ERR_UNSUPPORTED, "d_out * d_in too large");
+  const int64_t stride = awq_error_tiles(n_tokens, d_out);
+  const int64_t blocks = ((d_in + awq::kTileM - 1) / awq::kTileM) * ((d_out + awq::kTileN - 1) / awq::kTileN) * n_cand;
+  if (blocks > 0x7FFFFFFF || stride * n_cand > 0x7FFFFFFF)
+    return fail(AWQ_ERR_UNSUPPORTED, "%lld tiles exceed one launch", (long long)blocks);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = awq::launch_fill_f64(tile_sse, stride * n_cand, 0.0, st);
+  if (e != hipSuccess) return hip_fail(e, "fill launch");
+  e = awq::launch_quad_sse(gram, gram_exp, delta, delta_exp, n_cand, d_in, d_out, stride, tile_sse, st);
+  if (e != hipSuccess) return hip_fail(e, "gram_error_sse launch");
+  return ok();
 }
 
 int awq_search_scales(const void* x, int64_t ld_x, const void* const* w_parts,

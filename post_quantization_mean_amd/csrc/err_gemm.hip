@@ -26,6 +26,11 @@
 // Tile order: the 256 concurrently running tiles form a 16 x 16 super-block, split 8 x 4 per XCD
 // (tile_of in lds_dma.h), so operand K-slices are shared inside each XCD's L2 and across the XCDs in
 // the memory-side cache.
+//
+// The same data movement serves the Gram form of the loss (gram.hip): with A = B = X^T it stores
+// the float32 tiles of G = X^T X on and above the diagonal (kStore; G is symmetric), and with A = G and B = the candidates' delta, both in
+// float16, it sums each output element T[o, j] = (delta G)[o, j] times delta[o, j] per tile
+// (kQuad), so that a tile holds its share of the quadratic form delta G delta^T.
 #include <algorithm>
 #include <type_traits>
 
@@ -45,10 +50,18 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // One 16-byte fragment pair: a 32 x 32 x (16 bf16 | 8 f32) product into one accumulator; with ZC
 // the accumulator's old value is not read (the matrix core adds to zero), which starts a tile
 // without clearing 256 accumulator registers.
-template <typename T, bool ZC = false>
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// epilogues: the tile's sum of squares, the float32 tile itself, the quadratic-form share
+enum { kSse = 0, kStore = 1, kQuad = 2 };
+
+template <typename T, bool ZC = false, bool F16 = false>
 __device__ __forceinline__ void mma_pair(const uint4& a, const uint4& b, f32x16& c) {
   const f32x16 zero = {};
-  if constexpr (sizeof(T) == 2) {
+  if constexpr (F16) {
+    c = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b),
+                                               ZC ? zero : c, 0, 0, 0);
+  } else if constexpr (sizeof(T) == 2) {
     c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
                                                 ZC ? zero : c, 0, 0, 0);
   } else {
@@ -73,13 +86,29 @@ constexpr int kSplit = 8;
 // candidate's delta, each a raw buffer whose range ends at the last valid row.
 struct TileOps {
   i32x4 ra, rb;
-  int idx;  // tile_sse index
+  int idx;   // tile_sse index
+  int m0, n0, cand;
 };
-template <typename T>
+// Tile G of the upper triangle tm <= tn of a tiles x tiles grid, row by row.
+__device__ __forceinline__ void tri_of(int G, int tiles, int& tm, int& tn) {
+  int r = 0, rem = G;
+  while (rem >= tiles - r) {
+    rem -= tiles - r;
+    ++r;
+  }
+  tm = r;
+  tn = r + rem;
+}
+
+template <typename T, bool TRI = false>
 __device__ __forceinline__ TileOps tile_ops(int G, const T* x, int64_t ld_x, const T* delta, int64_t n_tokens,
-                                            int64_t d_in, int64_t d_out, int tiles_m, int tiles_n, int n_cols) {
+                                            int64_t d_in, int64_t d_out, int tiles_m, int tiles_n, int n_cols,
+                                            int64_t cand_stride) {
   int tm, col;
-  tile_of(G, tiles_m, n_cols, tm, col);
+  if constexpr (TRI)
+    tri_of(G, tiles_m, tm, col);
+  else
+    tile_of(G, tiles_m, n_cols, tm, col);
   const int cand = col / tiles_n;
   const int tn = col % tiles_n;
   const int64_t m0 = (int64_t)tm * BM;
@@ -91,24 +120,39 @@ __device__ __forceinline__ TileOps tile_ops(int G, const T* x, int64_t ld_x, con
   TileOps t;
   t.ra = make_rsrc(x + m0 * ld_x, (rows_a - 1) * lda_bytes + row_bytes);
   t.rb = make_rsrc(delta + ((int64_t)cand * d_out + n0) * d_in, (rows_b - 1) * row_bytes + row_bytes);
-  t.idx = cand * tiles_m * tiles_n + tm * tiles_n + tn;
+  t.idx = (int)(cand * cand_stride + (int64_t)tm * tiles_n + tn);
+  t.m0 = (int)m0;
+  t.n0 = (int)n0;
+  t.cand = cand;
   return t;
 }
+
+// Arguments of the kStore and kQuad epilogues.
+struct Epi {
+  float* c;                     // kStore: the float32 output, row pitch ld_c
+  int64_t ld_c;
+  const int32_t* dexp;          // kQuad: delta of candidate k is scaled by 2^dexp[k] ...
+  const int32_t* gexp;          // ... and G by 2^gexp[0]
+  int64_t cand_stride;          // tile_sse entries per candidate
+};
 
 // Persistent: one workgroup per compute unit walks tiles G = blockIdx.x, + gridDim.x, ... The
 // next tile's first K stage is loaded into the free LDS buffer during the current tile's last K
 // step, so its load latency hides behind that step and the epilogue.
-template <typename T>
+template <typename T, int MODE = kSse>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void error_sse_kernel(const T* __restrict__ x, int64_t ld_x, const T* __restrict__ delta,
                       int64_t n_tokens, int64_t d_in, int64_t d_out, int tiles_m, int tiles_n,
-                      int n_cols, double* __restrict__ tile_sse) {
+                      int n_cols, double* __restrict__ tile_sse, Epi epi) {
   constexpr int FM = 4, FN = 4, NR = 8;
+  constexpr bool F16 = MODE == kQuad;
   __shared__ __attribute__((aligned(1024))) char lds[2 * kStageBytes];
   __shared__ double red[4];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int nblk = tiles_m * n_cols;
+  // kStore (G = X^T X, symmetric): only the tiles with tm <= tn
+  constexpr bool TRI = MODE == kStore;
+  const int nblk = TRI ? tiles_m * (tiles_m + 1) / 2 : tiles_m * n_cols;
 
   const int lda_bytes = (int)(ld_x * (int64_t)sizeof(T));
   const int row_bytes = (int)(d_in * (int64_t)sizeof(T));
@@ -159,12 +203,12 @@ void error_sse_kernel(const T* __restrict__ x, int64_t ld_x, const T* __restrict
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
       const int fm = g >> 1, fn = (g & 1) * 2;
-      mma_pair<T, ZC>(use[fm], use[FM + fn], acc[fm][fn]);
+      mma_pair<T, ZC, F16>(use[fm], use[FM + fn], acc[fm][fn]);
       __builtin_amdgcn_sched_barrier(0);
       if (l0 + g < l1) issue(lt, fstage, l0 + g, kbyte);
       if (reads) nxt[g] = frag(src, sl, g);
       __builtin_amdgcn_sched_barrier(0);
-      mma_pair<T, ZC>(use[fm], use[FM + fn + 1], acc[fm][fn + 1]);
+      mma_pair<T, ZC, F16>(use[fm], use[FM + fn + 1], acc[fm][fn + 1]);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -173,7 +217,8 @@ void error_sse_kernel(const T* __restrict__ x, int64_t ld_x, const T* __restrict
 
   int G = blockIdx.x;
   if (G >= nblk) return;
-  TileOps cur_t = tile_ops<T>(G, x, ld_x, delta, n_tokens, d_in, d_out, tiles_m, tiles_n, n_cols);
+  const int64_t cand_stride = MODE == kQuad ? epi.cand_stride : (int64_t)tiles_m * tiles_n;
+  TileOps cur_t = tile_ops<T, TRI>(G, x, ld_x, delta, n_tokens, d_in, d_out, tiles_m, tiles_n, n_cols, cand_stride);
   int par = 0;  // LDS buffer holding the tile's K stage 0
 #pragma unroll
   for (int i = 0; i < 16; ++i) issue(cur_t, lds_base, i, 0);
@@ -182,7 +227,8 @@ void error_sse_kernel(const T* __restrict__ x, int64_t ld_x, const T* __restrict
     const int Gn = G + (int)gridDim.x;
     const bool has_next = Gn < nblk;
     const TileOps nxt_t =
-        tile_ops<T>(has_next ? Gn : G, x, ld_x, delta, n_tokens, d_in, d_out, tiles_m, tiles_n, n_cols);
+        tile_ops<T, TRI>(has_next ? Gn : G, x, ld_x, delta, n_tokens, d_in, d_out, tiles_m, tiles_n, n_cols,
+                         cand_stride);
     uint4 f0[NR], f1[NR];
     // stage 0 is in flight in buffer par; the first kSplit loads of stage 1 go to the other
     // buffer (free: every wave passed the previous tile's final barrier); wait for stage 0
@@ -238,25 +284,61 @@ void error_sse_kernel(const T* __restrict__ x, int64_t ld_x, const T* __restrict
       par = b ^ 1;
     }
 
-    // sum of squares: each accumulator's 16 values in float32 (relative error below 1e-6), the
-    // 16 accumulators and then lanes, waves in float64
-    double ss = 0.0;
+    // element e of accumulator (i, j) in lane l: row 32 i + 8 (e / 4) + 4 (l / 32) + e % 4 of the
+    // wave's 128 A rows, column 32 j + l % 32 of its 128 B rows
+    const int64_t am = (int64_t)cur_t.m0 + wm * 128 + 4 * fh, bn = (int64_t)cur_t.n0 + wn * 128 + fr;
+    if constexpr (MODE == kStore) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        float s32 = 0.f;
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) s32 = fmaf(acc[i][j][e], acc[i][j][e], s32);
-        ss += (double)s32;
+          for (int e = 0; e < 16; ++e) {
+            const int64_t m = am + 32 * i + 8 * (e >> 2) + (e & 3), n = bn + 32 * j;
+            if (m < n_tokens && n < d_out) epi.c[m * epi.ld_c + n] = acc[i][j][e];
+          }
+      __syncthreads();  // every wave has read the last stage
+    } else {
+      // kSse: sum of squares; kQuad: sum of acc * delta[o, j] (A row j, B row o), four consecutive
+      // j per 8-byte load. Each accumulator's 16 terms in float32, then accumulators, lanes and
+      // waves in float64.
+      double ss = 0.0;
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          float s32 = 0.f;
+          if constexpr (MODE == kSse) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) s32 = fmaf(acc[i][j][e], acc[i][j][e], s32);
+          } else {
+            const int64_t o = bn + 32 * j;  // row of this candidate's delta
+            const _Float16* drow = reinterpret_cast<const _Float16*>(delta) + ((int64_t)cur_t.cand * d_out + o) * d_in;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int64_t m = am + 32 * i + 8 * q;  // K index j of the four terms (d_in % 4 == 0)
+              if (o < d_out && m < n_tokens) {
+                const uint2 u = *reinterpret_cast<const uint2*>(drow + m);
+                const f16x8 h = __builtin_bit_cast(f16x8, make_uint4(u.x, u.y, 0u, 0u));
+#pragma unroll
+                for (int r = 0; r < 4; ++r) s32 = fmaf(acc[i][j][4 * q + r], (float)h[r], s32);
+              }
+            }
+          }
+          ss += (double)s32;
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
-    }
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
-    if (lane == 0) red[wave] = ss;
-    __syncthreads();  // red is complete, and every wave has read the last stage
-    if (threadIdx.x == 0) tile_sse[cur_t.idx] = (red[0] + red[1]) + (red[2] + red[3]);
+      for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
+      if (lane == 0) red[wave] = ss;
+      __syncthreads();  // red is complete, and every wave has read the last stage
+      if (threadIdx.x == 0) {
+        double v = (red[0] + red[1]) + (red[2] + red[3]);
+        if constexpr (MODE == kQuad) v = ldexp(v, -(epi.gexp[0] + 2 * epi.dexp[cur_t.cand]));  // exact
+        tile_sse[cur_t.idx] = v;
+      }
+    }
     if (!has_next) break;
     G = Gn;
     cur_t = nxt_t;
@@ -265,15 +347,10 @@ void error_sse_kernel(const T* __restrict__ x, int64_t ld_x, const T* __restrict
 
 }  // namespace
 
-hipError_t launch_error_sse(const void* x, int64_t ld_x, const void* delta, int dtype,
-                            int64_t n_tokens, int64_t d_in, int64_t d_out, int n_cand,
-                            double* tile_sse, hipStream_t st) {
-  const int tiles_m = (int)((n_tokens + BM - 1) / BM);
-  const int tiles_n = (int)((d_out + BN - 1) / BN);
-  const int n_cols = tiles_n * n_cand;
-  const int64_t nblk = (int64_t)tiles_m * n_cols;
-  // one persistent workgroup per compute unit (the tile order assumes 8 XCDs dealt round-robin)
-  // compute units of the current device, looked up once per device and thread
+namespace {
+// one persistent workgroup per compute unit (the tile order assumes 8 XCDs dealt round-robin);
+// compute units of the current device, looked up once per device and thread
+unsigned persistent_grid(int64_t nblk) {
   static thread_local int cus_of[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
@@ -282,15 +359,55 @@ hipError_t launch_error_sse(const void* x, int64_t ld_x, const void* delta, int 
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
     cus_of[dev] = cus;
   }
-  const unsigned grid = (unsigned)std::min<int64_t>(nblk, cus);
+  return (unsigned)std::min<int64_t>(nblk, cus);
+}
+}  // namespace
+
+hipError_t launch_error_sse(const void* x, int64_t ld_x, const void* delta, int dtype,
+                            int64_t n_tokens, int64_t d_in, int64_t d_out, int n_cand,
+                            double* tile_sse, hipStream_t st) {
+  const int tiles_m = (int)((n_tokens + BM - 1) / BM);
+  const int tiles_n = (int)((d_out + BN - 1) / BN);
+  const int n_cols = tiles_n * n_cand;
+  const unsigned grid = persistent_grid((int64_t)tiles_m * n_cols);
+  const Epi epi = {};
   if (dtype == 1)
     hipLaunchKernelGGL((error_sse_kernel<uint16_t>), dim3(grid), dim3(kThreads), 0, st,
                        static_cast<const uint16_t*>(x), ld_x, static_cast<const uint16_t*>(delta),
-                       n_tokens, d_in, d_out, tiles_m, tiles_n, n_cols, tile_sse);
+                       n_tokens, d_in, d_out, tiles_m, tiles_n, n_cols, tile_sse, epi);
   else
     hipLaunchKernelGGL((error_sse_kernel<float>), dim3(grid), dim3(kThreads), 0, st,
                        static_cast<const float*>(x), ld_x, static_cast<const float*>(delta), n_tokens,
-                       d_in, d_out, tiles_m, tiles_n, n_cols, tile_sse);
+                       d_in, d_out, tiles_m, tiles_n, n_cols, tile_sse, epi);
+  return hipGetLastError();
+}
+
+hipError_t launch_gram_store(const uint16_t* xt, int64_t n_pad, int64_t d_in, float* g, hipStream_t st) {
+  const int tiles = (int)((d_in + BM - 1) / BM);
+  const unsigned grid = persistent_grid((int64_t)tiles * (tiles + 1) / 2);
+  Epi epi = {};
+  epi.c = g;
+  epi.ld_c = d_in;
+  // A = B = X^T ([d_in, n_pad], K = tokens): G[i, j] = sum_t x[t, i] x[t, j]
+  hipLaunchKernelGGL((error_sse_kernel<uint16_t, kStore>), dim3(grid), dim3(kThreads), 0, st, xt, n_pad, xt,
+                     d_in, n_pad, d_in, tiles, tiles, tiles, (double*)nullptr, epi);
+  return hipGetLastError();
+}
+
+hipError_t launch_quad_sse(const uint16_t* g16, const int32_t* gexp, const uint16_t* delta16, const int32_t* dexp,
+                           int n_cand, int64_t d_in, int64_t d_out, int64_t cand_stride, double* tile_sse,
+                           hipStream_t st) {
+  const int tiles_m = (int)((d_in + BM - 1) / BM);
+  const int tiles_n = (int)((d_out + BN - 1) / BN);
+  const int n_cols = tiles_n * n_cand;
+  const unsigned grid = persistent_grid((int64_t)tiles_m * n_cols);
+  Epi epi = {};
+  epi.dexp = dexp;
+  epi.gexp = gexp;
+  epi.cand_stride = cand_stride;
+  // A = G ([d_in, d_in], symmetric: its rows are its columns), B = the candidates' delta
+  hipLaunchKernelGGL((error_sse_kernel<uint16_t, kQuad>), dim3(grid), dim3(kThreads), 0, st, g16, d_in, delta16,
+                     d_in, d_in, d_out, tiles_m, tiles_n, n_cols, tile_sse, epi);
   return hipGetLastError();
 }
 

@@ -50,6 +50,20 @@ hipError_t launch_quant_delta(const WParts& w, int dtype, int64_t d_in, const do
 hipError_t launch_quantize_pack(const WParts& w, int dtype, int64_t d_in, const double* s,
                                 uint8_t* codes, float* qscales, int32_t* zeros,
                                 hipStream_t stream);
+// the same delta in float16, scaled by 2^dexp[k] (bfloat16 weights)
+hipError_t launch_quant_delta_f16(const WParts& w, int64_t d_in, const double* cand_scales, int n_cand,
+                                  uint16_t* delta, const int32_t* dexp, hipStream_t stream);
+
+// ---- the Gram form of the loss (gram.hip)
+int64_t gram_n_pad(int64_t n_tokens);  // tokens of X^T's rows: a multiple of 64
+// X^T into xt ([d_in, gram_n_pad]), G = X^T X into g32 ([d_in, d_in] float32), its scale exponent
+// into gexp[0] and float16(G * 2^gexp) into g16
+hipError_t launch_gram(const void* x, int64_t ld_x, int64_t n_tokens, int64_t d_in, uint16_t* xt, float* g32,
+                       uint16_t* g16, int32_t* gexp, hipStream_t stream);
+// dexp[k] for k < n_cand: the scale exponent of ratio k's delta; dexp[n_cand]: max |W| (scratch)
+hipError_t launch_delta_exp(const WParts& w, int64_t d_in, const double* cand_scales, int n_cand, int32_t* dexp,
+                            hipStream_t stream);
+hipError_t launch_fill_f64(double* p, int64_t n, double v, hipStream_t stream);
 
 // ---- around the search: source fold and deployment form
 hipError_t launch_fold_scales(const void* src, int64_t ld_src, int dtype, int64_t rows, int64_t cols,

@@ -239,6 +239,19 @@ __device__ __forceinline__ void store_pair(float* p, double a, double b) {
   *reinterpret_cast<float2*>(p) = make_float2((float)a, (float)b);
 }
 
+// Float16 output of delta scaled by sc (a power of two, exact) for the Gram form of the loss.
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) | ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
+}
+template <int E>
+__device__ __forceinline__ void storeE_f16(uint16_t* p, const float (&v)[E], float sc) {
+#pragma unroll
+  for (int h = 0; h < E / 8; ++h)
+    *reinterpret_cast<uint4*>(p + 8 * h) =
+        make_uint4(pack_f16x2(v[8 * h] * sc, v[8 * h + 1] * sc), pack_f16x2(v[8 * h + 2] * sc, v[8 * h + 3] * sc),
+                   pack_f16x2(v[8 * h + 4] * sc, v[8 * h + 5] * sc), pack_f16x2(v[8 * h + 6] * sc, v[8 * h + 7] * sc));
+}
+
 // Extends a lane mask to whole groups of 8 lanes: any lane of a group set -> all of them.
 __device__ __forceinline__ uint64_t group_mask(uint64_t b) {
   b |= b >> 1;
@@ -283,8 +296,8 @@ __device__ __forceinline__ void wave_minmax_f64(double& mn, double& mx) {
   mx = fmax(fmax(readlane_f64(mx, 0), readlane_f64(mx, 16)), fmax(readlane_f64(mx, 32), readlane_f64(mx, 48)));
 }
 
-template <typename T>
-__device__ __forceinline__ void exact_group(float wa, float wb, const double* s_lds, T* dst) {
+template <typename T, bool F16 = false>
+__device__ __forceinline__ void exact_group(float wa, float wb, const double* s_lds, T* dst, float sc = 1.f) {
   const double w0 = wa, w1 = wb;
   const double s0 = s_lds[0], s1 = s_lds[1];
   const double y0 = w0 * s0, y1 = w1 * s1;
@@ -293,13 +306,20 @@ __device__ __forceinline__ void exact_group(float wa, float wb, const double* s_
   const double st = group_step(mn, mx);
   const double zero = rint(-mn / st);
   const double q0 = exact_code(y0, st, zero), q1 = exact_code(y1, st, zero);
-  store_pair(dst, (q0 - zero) * st / s0 - w0, (q1 - zero) * st / s1 - w1);
+  const double d0 = (q0 - zero) * st / s0 - w0, d1 = (q1 - zero) * st / s1 - w1;
+  if constexpr (F16)
+    *reinterpret_cast<uint32_t*>(dst) = pack_f16x2((float)d0 * sc, (float)d1 * sc);
+  else
+    store_pair(dst, d0, d1);
 }
 
-template <typename T>
+// With F16 (bfloat16 weights only) delta is written as float16 of delta * 2^dexp[k] instead of in
+// the weights' type.
+template <typename T, bool F16 = false>
 __global__ __launch_bounds__(kThreads) void quant_delta_kernel(WParts w, int64_t d_in, int64_t d_out,
                                                                const double* __restrict__ cand,
-                                                               int n_cand, T* __restrict__ delta) {
+                                                               int n_cand, T* __restrict__ delta,
+                                                               const int32_t* __restrict__ dexp = nullptr) {
   constexpr int E = kChans;
   __shared__ __attribute__((aligned(16))) float sc_s[2][kChansPerBlock];
   __shared__ __attribute__((aligned(16))) float sc_i[2][kChansPerBlock];  // -1/s
@@ -363,6 +383,8 @@ __global__ __launch_bounds__(kThreads) void quant_delta_kernel(WParts w, int64_t
     if (k + 1 < n_cand) stage((k + 1) & 1);
     if (k + 2 < n_cand) fetch(k + 2);
     T* dk = delta + (int64_t)k * d_out * d_in + c0;
+    float sc = 1.f;
+    if constexpr (F16) sc = ldexpf(1.f, dexp[k]);
 #pragma unroll
     for (int i = 0; i < kRows; ++i) {
       float y[E];
@@ -385,7 +407,12 @@ __global__ __launch_bounds__(kThreads) void quant_delta_kernel(WParts w, int64_t
       const bool live = col_ok && o < d_out;
       const bool ok = fg.ok && em <= kHalfGuard32 * step;
       bad[i] = group_mask(__ballot(live && !ok));
-      if (live && !((bad[i] >> lane) & 1)) storeE<T, E>(dk + o * d_in, out);
+      if (live && !((bad[i] >> lane) & 1)) {
+        if constexpr (F16)
+          storeE_f16<E>(dk + o * d_in, out, sc);
+        else
+          storeE<T, E>(dk + o * d_in, out);
+      }
       __builtin_amdgcn_sched_barrier(0);  // one row's temporaries live at a time
     }
     // The flagged groups (rare: near a rounding tie, or unusual ranges), each by the whole wave
@@ -405,8 +432,8 @@ __global__ __launch_bounds__(kThreads) void quant_delta_kernel(WParts w, int64_t
         }
         const float2 wp = *reinterpret_cast<const float2*>(&xpose[wave][2 * lane]);
         const int64_t c = cb + g * kGroup + 2 * lane;
-        exact_group<T>(wp.x, wp.y, &sc_d[k & 1][g * kGroup + 2 * lane],
-                       delta + ((int64_t)k * d_out + row0 + i) * d_in + c);
+        exact_group<T, F16>(wp.x, wp.y, &sc_d[k & 1][g * kGroup + 2 * lane],
+                            delta + ((int64_t)k * d_out + row0 + i) * d_in + c, sc);
       }
     }
   }
@@ -568,6 +595,16 @@ hipError_t launch_quant_delta(const WParts& w, int dtype, int64_t d_in, const do
   else
     hipLaunchKernelGGL(quant_delta_kernel<float>, grid, dim3(kThreads), 0, st, w, d_in, d_out,
                        cand_scales, n_cand, static_cast<float*>(delta));
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_delta_f16(const WParts& w, int64_t d_in, const double* cand_scales, int n_cand,
+                                  uint16_t* delta, const int32_t* dexp, hipStream_t st) {
+  const int64_t d_out = w.row_begin[w.n];
+  dim3 grid((unsigned)((d_in + kChansPerBlock - 1) / kChansPerBlock),
+            (unsigned)((d_out + kRowsPerBlock - 1) / kRowsPerBlock));
+  hipLaunchKernelGGL((quant_delta_kernel<uint16_t, true>), grid, dim3(kThreads), 0, st, w, d_in, d_out,
+                     cand_scales, n_cand, delta, dexp);
   return hipGetLastError();
 }
 

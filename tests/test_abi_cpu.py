@@ -30,11 +30,11 @@ def _declared():
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
     names = _declared()
-    assert len(names) == 29
+    assert len(names) == 34
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(b.exported_symbols()) == names
-    assert lib.awq_abi_version() == 4
+    assert lib.awq_abi_version() == 5
 
 
 def test_status_strings(lib):
@@ -332,3 +332,66 @@ def test_head_tie_validation(lib):
     assert lib.awq_tie_heads(FAKE, 1 << 21, 1, 128, FAKE, None) == 5
     assert lib.awq_head_group_scales(FAKE, 8, 2, 128, None, None) == 1
     assert lib.awq_head_group_scales(FAKE, 6, 4, 128, FAKE, None) == 2
+
+
+def _gram_rule(dtype, n, d_in, d_out, n_grid):
+    """The documented choice of the Gram form: bf16, n >= d_in, 32-bit tile offsets, and G plus the
+    n_grid quadratic forms under 0.85 of the direct products' flops."""
+    if dtype != 1 or n < d_in or d_in <= 0 or d_out <= 0 or n_grid < 1:
+        return 0
+    n_pad = (n + 63) // 64 * 64
+    if 256 * n_pad * 2 > 0x7FFFFFFF:
+        return 0
+    direct = 2.0 * n * d_in * d_out * n_grid
+    gram = 2.0 * d_in * d_in * n_pad + 2.0 * d_out * d_in * d_in * n_grid
+    return int(gram < 0.85 * direct)
+
+
+def test_loss_form_choice(lib):
+    # the four large workloads: the Gram form where tokens outnumber input channels enough
+    assert lib.awq_search_loss_form(1, 65536, 28672, 8192, 40) == 1   # 70B down_proj stress
+    assert lib.awq_search_loss_form(1, 16384, 11008, 4096, 20) == 1   # 7B down_proj
+    assert lib.awq_search_loss_form(1, 4096, 4096, 12288, 20) == 0    # 7B fused QKV
+    assert lib.awq_search_loss_form(1, 8192, 8192, 57344, 20) == 0    # 70B fused gate+up
+    assert lib.awq_search_loss_form(0, 65536, 256, 256, 20) == 0      # float32 activations
+    assert lib.awq_search_loss_form(1, 5000000, 256, 256, 20) == 0    # 32-bit tile offsets
+    import random
+    rng = random.Random(0)
+    for _ in range(500):
+        n, d_in = rng.randint(1, 200000), 128 * rng.randint(1, 200)
+        d_out, g = rng.randint(1, 70000), rng.randint(1, 64)
+        assert lib.awq_search_loss_form(1, n, d_in, d_out, g) == _gram_rule(1, n, d_in, d_out, g), (n, d_in, d_out, g)
+    # the search's workspace includes the Gram form's buffers exactly when it is chosen
+    direct = lib.awq_search_workspace_bytes(1, 4096, 4096, 12288, 128, 20, 20)
+    assert direct == (20 * 12288 * 4096 * 2) + ((20 * 16 * 48 * 8 + 255) // 256 * 256)
+    gram = lib.awq_search_workspace_bytes(1, 65536, 28672, 8192, 128, 40, 40)
+    base = 40 * 8192 * 28672 * 2 + (40 * 256 * 32 * 8 + 255) // 256 * 256
+    assert gram == base + 28672 * 28672 * 2 + 256 + 256 + 28672 * 65536 * 2 + 28672 * 28672 * 4
+    assert lib.awq_gram_workspace_bytes(65536, 28672) == 28672 * 65536 * 2 + 28672 * 28672 * 4
+    assert lib.awq_gram_workspace_bytes(1000, 200) == 0
+
+
+def test_gram_validation(lib):
+    ws = lib.awq_gram_workspace_bytes(1000, 256)
+    assert ws == (256 * 1024 * 2) + (256 * 256 * 4)
+    assert lib.awq_gram(None, 256, 1000, 256, FAKE, FAKE, FAKE, ws, None) == 1
+    assert lib.awq_gram(FAKE, 256, 1000, 200, FAKE, FAKE, FAKE, ws, None) == 2
+    assert lib.awq_gram(FAKE, 256, 1000, 256, None, FAKE, FAKE, ws, None) == 1
+    assert lib.awq_gram(FAKE, 256, 1000, 256, FAKE_ODD, FAKE, FAKE, ws, None) == 5
+    assert lib.awq_gram(FAKE, 256, 1000, 256, FAKE, FAKE, FAKE, ws - 1, None) == 6
+    assert lib.awq_gram(FAKE, 256, 1000, 256, FAKE, FAKE, FAKE_ODD, ws, None) == 5
+    assert lib.awq_gram(FAKE, 256, 5000000, 256, FAKE, FAKE, FAKE, 1 << 40, None) == 5
+    ptrs = (ctypes.c_void_p * 1)(FAKE)
+    rows = (ctypes.c_int64 * 1)(300)
+    assert lib.awq_quant_delta_f16(ptrs, rows, 1, 256, 128, FAKE, 4, FAKE, None, None) == 1
+    assert lib.awq_quant_delta_f16(ptrs, rows, 1, 256, 128, FAKE, 0, FAKE, FAKE, None) == 4
+    assert lib.awq_quant_delta_f16(ptrs, rows, 1, 256, 128, FAKE, 4, FAKE_ODD, FAKE, None) == 5
+    assert lib.awq_quant_delta_f16(ptrs, rows, 1, 256, 128, FAKE_ODD, 4, FAKE, FAKE, None) == 5
+    assert lib.awq_quant_delta_f16(ptrs, rows, 1, 256, 64, FAKE, 4, FAKE, FAKE, None) == 5
+    assert lib.awq_quant_delta_f16(ptrs, rows, 1, 200, 128, FAKE, 4, FAKE, FAKE, None) == 2
+    assert lib.awq_gram_error_sse(FAKE, FAKE, FAKE, FAKE, 4, 100, 256, 300, FAKE, None) == 2   # n_tokens < d_in
+    assert lib.awq_gram_error_sse(None, FAKE, FAKE, FAKE, 4, 1000, 256, 300, FAKE, None) == 1
+    assert lib.awq_gram_error_sse(FAKE, FAKE, FAKE, FAKE, 0, 1000, 256, 300, FAKE, None) == 4
+    assert lib.awq_gram_error_sse(FAKE_ODD, FAKE, FAKE, FAKE, 4, 1000, 256, 300, FAKE, None) == 5
+    assert lib.awq_gram_error_sse(FAKE, FAKE, FAKE, FAKE, 4, 1000, 256, 0, FAKE, None) == 2
+    assert lib.awq_gram_error_sse(FAKE, FAKE, FAKE, FAKE, 4, 1000, 200, 300, FAKE, None) == 2

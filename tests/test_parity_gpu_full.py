@@ -15,7 +15,9 @@ the digests, and then compares:
 * four 256 x 256 tiles of the error matrix against the oracle's sums of squares, and delta on
   sampled rows;
 and the GPU's own outputs must satisfy what holds at any size: each loss is the fixed-order sum
-of its tiles over N * d_out, and k* is the first strict minimum of the losses.
+of its tiles over N * d_out, and k* is the first strict minimum of the losses. Where the search
+takes the Gram form of the loss (more tokens than input channels: the 7B down_proj and the 70B
+stress layer), the whole awq_search_scales run that way is also compared: every loss and k*.
 """
 import hashlib
 import os
@@ -185,6 +187,36 @@ def _check(B, cid):
     print(f"  codes on all {wl.d_out} rows: {tot}, step max rel {step_rel:.2e}", flush=True)
     assert tot["elements"] == wl.d_out * wl.d_in
     assert tot["mismatch"] == 0 and tot["zero_mismatch"] == 0 and step_rel < P.STEP_RTOL
+
+    # where awq_search_scales takes the Gram form of the loss (and the benchmark times it), the
+    # whole search that way, every candidate in one pass: every loss against the oracle's, and k*
+    if B.awq_search_loss_form(B.AWQ_DTYPE_BF16, wl.n_tokens, wl.d_in, wl.d_out, n) == B.AWQ_LOSS_GRAM:
+        _check_gram(B, wl, x_np, w_np, lo, k_or)
+
+
+def _check_gram(B, wl, x_np, w_np, lo, k_or):
+    print(f"  [gram form] {wl.name}: awq_search_scales, {wl.n_grid} candidates in one pass", flush=True)
+    xt = to_torch(x_np, "cuda")
+    wt = to_torch(w_np, "cuda")
+    parts = list(wl.parts) or [wl.d_out]
+    wp, r = [], 0
+    for p in parts:
+        wp.append(wt[r:r + p])
+        r += p
+    act = B.awq_act_stats(xt)
+    res = B.awq_search_scales(xt, wp, act, wl.n_grid)
+    torch.cuda.synchronize()
+    losses = res["losses"].cpu().numpy()
+    info = res["best_info"].cpu().numpy()
+    rels = np.abs(losses - lo) / lo
+    k = int(info[0])
+    print(f"  [gram form] k* gpu {k} oracle {k_or}; loss rel err max {rels.max():.2e} (at k={int(rels.argmax())})",
+          flush=True)
+    assert np.all(rels <= P.LOSS_RTOL)
+    assert int(info[1]) == 0 and P.kstar_ok(k, k_or, lo)
+    assert np.array_equal(res["best_scales"].cpu().numpy(), res["cand_scales"].cpu().numpy()[k])
+    del xt, wt, wp, res
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.timeout(900)

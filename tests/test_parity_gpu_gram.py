@@ -1,0 +1,187 @@
+"""GPU parity of the Gram form of the loss (csrc/gram.hip and the error GEMM's kStore / kQuad
+epilogues) against the float64 oracle, through the C ABI.
+
+The oracle's loss is the definition, mean((X W^T - X What^T)^2); the Gram form reaches the same
+value as sum_o delta[o] (X^T X) delta[o]^T / (N d_out). Checked here:
+* G = X^T X against its float64 definition element by element, and its scale exponent;
+* the float16 delta against the oracle's What - W (float16 rounding instead of bfloat16);
+* every ratio's loss against the oracle's (1e-3) and k* by the pinned rule, on shapes with more
+  tokens than input channels (ragged token counts, ragged 256-tiles in d_in and d_out, fused
+  parts, several passes), both step by step and inside awq_search_scales, which chooses the Gram
+  form for these sizes;
+* non-finite weights: every loss NaN and the ones fallback, as the direct form gives.
+"""
+import numpy as np
+import pytest
+
+from oracle import awq_oracle as O
+from oracle import parity as P
+from workloads import custom_workload, f32_to_bf16_bits, make_w, make_x, to_f32, to_torch
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def B():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from post_quantization_mean_amd import binding
+    binding.load_library()
+    return binding
+
+
+def _parts(wt, parts):
+    out, r = [], 0
+    for p in parts:
+        out.append(wt[r:r + p])
+        r += p
+    return out
+
+
+def _f16_from_bits(t):
+    return t.view(torch.int16).cpu().numpy().view(np.float16).astype(np.float64)
+
+
+@pytest.mark.parametrize("n_tokens,d_in,x_kind", [(1000, 384, "normal"), (2048, 512, "student_t3"),
+                                                   (130, 128, "normal")])
+def test_gram_matrix(B, n_tokens, d_in, x_kind):
+    wl = custom_workload(n_tokens, d_in, 256, "bf16", x_kind=x_kind, outlier_channels=3, config_id=300)
+    x = make_x(wl)
+    print(f"[gpu gram] G of x{x.shape} {x_kind}", flush=True)
+    g16, gexp = B.awq_gram(to_torch(x, "cuda"))
+    torch.cuda.synchronize()
+    X = to_f32(x).astype(np.float64)
+    G = X.T @ X
+    e = int(gexp.cpu()[0])
+    dmax = np.max(np.diag(G))
+    assert 2.0 ** 13 <= dmax * 2.0 ** e < 2.0 ** 14  # the largest entry scales into [2^13, 2^14)
+    got = _f16_from_bits(g16) * 2.0 ** -e
+    A = np.abs(X).T @ np.abs(X)
+    # float16 rounding (2^-11 relative, 2^-25 absolute below the normal range, in scaled units) and
+    # float32 accumulation over the tokens (at most n 2^-24 of the sum of |products|)
+    tol = 2.0 ** -11 * np.abs(G) + 2.0 ** -25 * 2.0 ** -e + n_tokens * 2.0 ** -24 * A
+    assert np.all(np.abs(got - G) <= tol)
+    assert np.all(np.abs(got - got.T) <= 2 * tol)  # both halves of the symmetric product
+
+
+def test_delta_f16_against_oracle(B):
+    wl = custom_workload(700, 384, 600, "bf16", n_grid=4, config_id=301)
+    x, w = make_x(wl), make_w(wl)
+    xt, wt = to_torch(x, "cuda"), to_torch(w, "cuda")
+    wp = _parts(wt, (128, 300, 172))
+    act = B.awq_act_stats(xt)
+    cs = B.awq_candidate_scales(act, 4)
+    d16, dexp = B.awq_quant_delta_f16(wp, cs)
+    torch.cuda.synchronize()
+    X, W = to_f32(x).astype(np.float64), to_f32(w).astype(np.float64)
+    a = O.act_mean(X)
+    ex = dexp.cpu().numpy()
+    for k in range(4):
+        s = O.candidate_scales(a, k / 4)
+        d_or = O.quantize_restore(W, s, 128) - W
+        pk = O.quantize_pack(W, s, 128)
+        em, _ = P.exempt_masks(pk.t, pk.zt)
+        raw = _f16_from_bits(d16[k])
+        assert np.all(np.isfinite(raw)) and np.max(np.abs(raw)) <= 2.0 ** 14
+        got = raw * 2.0 ** -int(ex[k])
+        # the bfloat16 tolerance's terms with float16's rounding: 2^-11 |delta|, plus half of
+        # float16's subnormal spacing in scaled units
+        tol = P.delta_tolerance(d_or, W, pk.qscales, s) - 2.0 ** -8 * np.abs(d_or) + \
+            2.0 ** -11 * np.abs(d_or) + 2.0 ** -25 * 2.0 ** -int(ex[k])
+        bad = ~((np.abs(got - d_or) <= tol) | em)
+        assert not bad.any(), (k, int(bad.sum()))
+        # the scale is not needlessly small: the largest delta uses the upper float16 range
+        assert np.max(np.abs(raw)) >= 2.0 ** 4
+
+
+def _gram_losses(B, xt, wp, n_grid, cpp):
+    n_tokens = xt.shape[0]
+    d_out = sum(p.shape[0] for p in wp)
+    act = B.awq_act_stats(xt)
+    cs = B.awq_candidate_scales(act, n_grid)
+    g16, gexp = B.awq_gram(xt)
+    tiles = B.awq_error_tiles(n_tokens, d_out)
+    sse = torch.empty((n_grid, tiles), dtype=torch.float64, device="cuda")
+    for k0 in range(0, n_grid, cpp):
+        nk = min(cpp, n_grid - k0)
+        d16, dexp = B.awq_quant_delta_f16(wp, cs[k0:k0 + nk])
+        B.awq_gram_error_sse(g16, gexp, d16, dexp, n_tokens, sse[k0:k0 + nk])
+    losses, best, info = B.awq_loss_argmin(sse, n_tokens, d_out, cs)
+    torch.cuda.synchronize()
+    return losses.cpu().numpy(), info.cpu().numpy(), act.cpu().numpy(), sse.cpu().numpy()
+
+
+GRAM_CASES = [
+    # n_tokens, d_in, parts, n_grid, cpp, x_kind
+    (2048, 512, (512,), 20, 20, "normal"),
+    (1000, 384, (300,), 8, 3, "student_t3"),
+    (1500, 256, (128, 256, 96), 12, 12, "normal"),
+    (4096, 256, (256,), 20, 7, "student_t3"),
+]
+
+
+@pytest.mark.parametrize("n_tokens,d_in,parts,n_grid,cpp,x_kind", GRAM_CASES)
+def test_gram_losses_against_oracle(B, n_tokens, d_in, parts, n_grid, cpp, x_kind):
+    d_out = sum(parts)
+    wl = custom_workload(n_tokens, d_in, d_out, "bf16", n_grid=n_grid, x_kind=x_kind, outlier_channels=3,
+                         config_id=302)
+    x, w = make_x(wl), make_w(wl)
+    print(f"[gpu gram] losses x{x.shape} parts={parts} n_grid={n_grid} cpp={cpp} {x_kind}", flush=True)
+    xt, wt = to_torch(x, "cuda"), to_torch(w, "cuda")
+    wp = _parts(wt, parts)
+    losses, info, _, sse = _gram_losses(B, xt, wp, n_grid, cpp)
+    X, W = to_f32(x).astype(np.float64), to_f32(w).astype(np.float64)
+    ref = O.search_scales(X, W, 128, n_grid)
+    rel = P.max_rel(losses, ref.losses)
+    print(f"  losses max rel err {rel:.3e}; k* gpu {info[0]} oracle {ref.best_k}", flush=True)
+    assert rel < P.LOSS_RTOL
+    assert int(info[1]) == 0
+    assert P.kstar_ok(int(info[0]), ref.best_k, ref.losses)
+    # each candidate's own tiles, then zeros up to the direct form's tile count
+    own = ((d_in + 255) // 256) * ((d_out + 255) // 256)
+    assert np.all(sse[:, own:] == 0.0)
+
+
+@pytest.mark.parametrize("cpp", [None, 5])
+def test_search_scales_takes_the_gram_form(B, cpp):
+    n_tokens, d_in, d_out, n_grid = 4096, 256, 512, 20
+    assert B.awq_search_loss_form(B.AWQ_DTYPE_BF16, n_tokens, d_in, d_out, n_grid) == B.AWQ_LOSS_GRAM
+    wl = custom_workload(n_tokens, d_in, d_out, "bf16", n_grid=n_grid, x_kind="student_t3", outlier_channels=4,
+                         config_id=303)
+    x, w = make_x(wl), make_w(wl)
+    print(f"[gpu gram] awq_search_scales x{x.shape} d_out={d_out} cpp={cpp}", flush=True)
+    xt, wt = to_torch(x, "cuda"), to_torch(w, "cuda")
+    wp = _parts(wt, (200, 312))
+    act = B.awq_act_stats(xt)
+    res = B.awq_search_scales(xt, wp, act, n_grid, cand_per_pass=cpp)
+    torch.cuda.synchronize()
+    X, W = to_f32(x).astype(np.float64), to_f32(w).astype(np.float64)
+    ref = O.search_scales(X, W, 128, n_grid)
+    losses = res["losses"].cpu().numpy()
+    info = res["best_info"].cpu().numpy()
+    rel = P.max_rel(losses, ref.losses)
+    print(f"  losses max rel err {rel:.3e}; k* gpu {info[0]} oracle {ref.best_k}", flush=True)
+    assert rel < P.LOSS_RTOL
+    assert int(info[1]) == 0 and P.kstar_ok(int(info[0]), ref.best_k, ref.losses)
+    assert np.array_equal(res["best_scales"].cpu().numpy(), res["cand_scales"].cpu().numpy()[int(info[0])])
+    # the same losses as the step-by-step Gram form (one code path, one rounding)
+    steps, _, _, _ = _gram_losses(B, xt, wp, n_grid, cpp or n_grid)
+    assert np.array_equal(losses, steps)
+
+
+def test_gram_form_with_nonfinite_weights(B):
+    n_tokens, d_in, d_out, n_grid = 4096, 256, 256, 20
+    wl = custom_workload(n_tokens, d_in, d_out, "bf16", n_grid=n_grid, config_id=304)
+    x, w = make_x(wl), make_w(wl)
+    w = w.copy()
+    w[17, 40] = f32_to_bf16_bits(np.array([np.nan], np.float32))[0]
+    print("[gpu gram] NaN weight", flush=True)
+    xt, wt = to_torch(x, "cuda"), to_torch(w, "cuda")
+    act = B.awq_act_stats(xt)
+    res = B.awq_search_scales(xt, [wt], act, n_grid)
+    torch.cuda.synchronize()
+    info = res["best_info"].cpu().numpy()
+    assert np.all(np.isnan(res["losses"].cpu().numpy()))
+    assert int(info[0]) == 0 and int(info[1]) == B.AWQ_INFO_ALL_NONFINITE
+    assert np.all(res["best_scales"].cpu().numpy() == 1.0)
