@@ -298,6 +298,7 @@ def main() -> int:
                        for i in range(args.steps))) / args.steps
     gram_ms = span("gram0", "gram1") / args.steps if gram else None
     n_pad = (wl.n_tokens + 63) // 64 * 64
+    tg = (wl.d_in + 255) // 256  # 256-tiles along G's side
     # algorithmic flops of one launch of the dominant kernel: the error GEMM's products, or in the
     # Gram form the quadratic form's delta G products (G itself is timed apart)
     if gram:
@@ -506,8 +507,9 @@ def main() -> int:
         "kernels_ms": {"act_stats+candidate_scales": act_ms, "quant_delta": quant_ms, "error_sse": gemm_ms,
                        "quantize_pack": pack_ms},
         "gram": None if not gram else {
-            "ms": gram_ms, "note": "X^T, G = X^T X (every 256 x 256 tile, float32), its scale and float16 form",
-            "gram_gemm_tflops": 2.0 * wl.d_in * wl.d_in * n_pad / (gram_ms * 1e-3) / 1e12},
+            "ms": gram_ms, "note": "X^T, G = X^T X (the 256 x 256 tiles on and above the diagonal, float32), its "
+                                   "scale and float16 form; TFLOP/s of those tiles' products over the whole step",
+            "gram_gemm_tflops": 2.0 * n_pad * 256 * 256 * (tg * (tg + 1) // 2) / (gram_ms * 1e-3) / 1e12},
         "hbm_kernels": {"note": "each kernel alone, memory-side cache flushed before every repetition, median of 5; "
                                 "algorithmic bytes / time against 8000 GB/s",
                         "fold_source": src_kind, "ms": iso_ms, "gbps": iso_gbps,
