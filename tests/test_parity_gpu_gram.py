@@ -185,3 +185,58 @@ def test_gram_form_with_nonfinite_weights(B):
     assert np.all(np.isnan(res["losses"].cpu().numpy()))
     assert int(info[0]) == 0 and int(info[1]) == B.AWQ_INFO_ALL_NONFINITE
     assert np.all(res["best_scales"].cpu().numpy() == 1.0)
+
+
+@pytest.mark.parametrize("formula,grid", [("rms", "tenths"), ("duo", "linspace")])
+def test_search_ex_takes_the_gram_form(B, formula, grid):
+    # the variant search with the group INT4 quantizer runs the same loss code: a formula and grid of
+    # the other pages, in the Gram regime, against the variant oracle
+    from oracle import awq_variants as V
+    n_tokens, d_in, d_out = 4096, 256, 384
+    ratios = V.grid_tenths() if grid == "tenths" else V.grid_linspace(16)
+    f_c = B.AWQ_FORMULA_RMS if formula == "rms" else B.AWQ_FORMULA_DUO
+    f_o = V.FORMULA_RMS if formula == "rms" else V.FORMULA_DUO
+    assert B.awq_search_loss_form(B.AWQ_DTYPE_BF16, n_tokens, d_in, d_out, len(ratios)) == B.AWQ_LOSS_GRAM
+    wl = custom_workload(n_tokens, d_in, d_out, "bf16", x_kind="student_t3", outlier_channels=3, config_id=305)
+    x, w = make_x(wl), make_w(wl)
+    print(f"[gpu gram] awq_search_scales_ex {formula} {grid} x{x.shape}", flush=True)
+    xt, wt = to_torch(x, "cuda"), to_torch(w, "cuda")
+    act = B.awq_act_stats(xt)
+    wm = B.awq_weight_mean([wt]) if formula == "duo" else None
+    res = B.awq_search_scales_ex(xt, [wt], act, ratios, f_c, B.AWQ_QUANT_INT4_GROUP, w_mean=wm)
+    torch.cuda.synchronize()
+    X, W = to_f32(x).astype(np.float64), to_f32(w).astype(np.float64)
+    _, ref_losses, ref_k, _ = V.search(X, W, ratios, f_o, V.QUANT_INT4_GROUP)
+    losses = res["losses"].cpu().numpy()
+    info = res["best_info"].cpu().numpy()
+    rel = P.max_rel(losses, ref_losses)
+    print(f"  losses max rel err {rel:.3e}; k* gpu {info[0]} oracle {ref_k}", flush=True)
+    assert rel < P.LOSS_RTOL and P.kstar_ok(int(info[0]), ref_k, ref_losses)
+
+
+def test_gram_search_in_a_hip_graph(B):
+    # the Gram form adds only kernels (transpose, fills, scale choices) to the step: the whole layer
+    # captured once and replayed on new activations equals eager runs bit for bit
+    n_tokens, d_in, d_out, n_grid = 4096, 256, 512, 8
+    assert B.awq_search_loss_form(B.AWQ_DTYPE_BF16, n_tokens, d_in, d_out, n_grid) == B.AWQ_LOSS_GRAM
+    wl = custom_workload(n_tokens, d_in, d_out, "bf16", n_grid=n_grid, outlier_channels=3, config_id=306)
+    x, w = make_x(wl), make_w(wl)
+    print("[gpu gram] HIP graph of the Gram-form layer", flush=True)
+    wt = to_torch(w, "cuda")
+    wp = _parts(wt, (200, 312))
+    x_in = to_torch(x, "cuda").clone()
+    x_variants = [x_in.clone(), (x_in.float() * 0.25).to(torch.bfloat16), x_in.flip(0).contiguous()]
+    B.awq_layer(x_in, wp, n_grid=n_grid)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        captured = B.awq_layer(x_in, wp, n_grid=n_grid)
+    for rep in range(2):
+        for xv in x_variants:
+            want = {k: v.cpu().numpy() for k, v in B.awq_layer(xv, wp, n_grid=n_grid).items()}
+            x_in.copy_(xv)
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            for key in ("losses", "best_info", "best_scales", "codes", "qscales", "zeros"):
+                assert np.array_equal(captured[key].cpu().numpy(), want[key], equal_nan=True), (rep, key)
