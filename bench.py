@@ -300,9 +300,11 @@ def main() -> int:
     n_pad = (wl.n_tokens + 63) // 64 * 64
     tg = (wl.d_in + 255) // 256  # 256-tiles along G's side
     # algorithmic flops of one launch of the dominant kernel: the error GEMM's products, or in the
-    # Gram form the quadratic form's delta G products (G itself is timed apart)
+    # Gram form the quadratic form's delta G products over G's 256-blocks on and right of the
+    # diagonal, which G's symmetry leaves to compute (G itself is timed apart)
     if gram:
-        flops_launch = 2.0 * wl.d_out * wl.d_in * wl.d_in * min(cpp, wl.n_grid)
+        rows_k = sum(min(256, wl.d_in - 256 * i) * (wl.d_in - 256 * i) for i in range(tg))
+        flops_launch = 2.0 * wl.d_out * rows_k * min(cpp, wl.n_grid)
     else:
         flops_launch = 2.0 * wl.n_tokens * wl.d_in * wl.d_out * min(cpp, wl.n_grid)
     peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS

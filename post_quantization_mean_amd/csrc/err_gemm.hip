@@ -28,9 +28,17 @@
 // the memory-side cache.
 //
 // The same data movement serves the Gram form of the loss (gram.hip): with A = B = X^T it stores
-// the float32 tiles of G = X^T X on and above the diagonal (kStore; G is symmetric), and with A = G and B = the candidates' delta, both in
-// float16, it sums each output element T[o, j] = (delta G)[o, j] times delta[o, j] per tile
-// (kQuad), so that a tile holds its share of the quadratic form delta G delta^T.
+// the float32 tiles of G = X^T X on and above the diagonal (kStore; G is symmetric), and with A = G
+// and B = the candidates' delta, both in float16, it sums products T[o, j] delta[o, j] per tile
+// (kQuad), T = delta G over a K range, so that the tiles hold shares of the quadratic form
+// delta G delta^T. With d_in cut into 256-blocks, the form is the sum over block pairs (I, J) of
+// delta_I G_IJ delta_J^T, and G_JI = G_IJ^T makes the (J, I) term equal to the (I, J) one: row tile I
+// runs K over block I alone (weight 1) and, in a tile of its own, over the blocks J > I (weight 2),
+// about half the matrix work of the full K range. The latter tiles' lengths fall with I, so a
+// compute unit takes row tile I and then row tile R - 1 - I of the same column (R rows have blocks
+// right of the diagonal): every pair has the same length, the 256 units stay in step, and their
+// 16 x 16 super-blocks keep sharing operands in L2. The first tile of a pair walks K down from d_in
+// and the second walks it up, so that at any moment the tiles of either kind read the same K slice.
 #include <algorithm>
 #include <type_traits>
 
@@ -88,6 +96,9 @@ struct TileOps {
   i32x4 ra, rb;
   int idx;   // tile_sse index
   int m0, n0, cand;
+  int k_steps;  // K steps of this tile (>= 2)
+  int k_last;   // kQuad: byte offset of the last K step if K is walked downwards, else 0
+  bool dbl;     // kQuad: the tile's sum counts twice
 };
 // Tile G of the upper triangle tm <= tn of a tiles x tiles grid, row by row.
 __device__ __forceinline__ void tri_of(int G, int tiles, int& tm, int& tn) {
@@ -100,15 +111,58 @@ __device__ __forceinline__ void tri_of(int G, int tiles, int& tm, int& tn) {
   tn = r + rem;
 }
 
-template <typename T, bool TRI = false>
+// kQuad work items: first the (tiles_m - 1) x n_cols tiles whose K range is the blocks right of
+// the diagonal, in pairs (see the file comment), then the tiles_m x n_cols diagonal blocks. Item G
+// runs on unit G % grid as that unit's (G / grid)-th tile, so pair p of the top rows is taken by
+// items that are grid apart: chunks of grid items alternate between first and second tiles (the
+// last, partial chunk of pairs lists its first tiles, then their partners).
+__device__ __forceinline__ void quad_off_tile(int G, int R, int n_cols, int grid, int& tm, int& col, bool& down) {
+  const int n_pairs = (R / 2) * n_cols;
+  if (G < 2 * n_pairs) {
+    const int full = n_pairs / grid, rem = n_pairs - full * grid;
+    int p, second;
+    if (G < 2 * full * grid) {
+      const int c = G / grid;
+      p = (c >> 1) * grid + (G - c * grid);
+      second = c & 1;
+    } else {
+      const int g = G - 2 * full * grid;
+      second = g >= rem;
+      p = full * grid + (second ? g - rem : g);
+    }
+    tile_of(p, R / 2, n_cols, tm, col);
+    if (second) tm = R - 1 - tm;
+    down = !second;
+  } else {  // R odd: the middle row, its tiles all of one length
+    tm = R / 2;
+    col = G - 2 * n_pairs;
+    down = false;
+  }
+}
+
+template <typename T, int MODE>
 __device__ __forceinline__ TileOps tile_ops(int G, const T* x, int64_t ld_x, const T* delta, int64_t n_tokens,
                                             int64_t d_in, int64_t d_out, int tiles_m, int tiles_n, int n_cols,
                                             int64_t cand_stride) {
   int tm, col;
-  if constexpr (TRI)
+  int64_t k0 = 0, k1 = d_in;  // K range [k0, k1) in elements
+  bool dbl = false, down = false;
+  if constexpr (MODE == kStore) {
     tri_of(G, tiles_m, tm, col);
-  else
+  } else if constexpr (MODE == kQuad) {
+    const int n_off = (tiles_m - 1) * n_cols;
+    if (G < n_off) {
+      quad_off_tile(G, tiles_m - 1, n_cols, (int)gridDim.x, tm, col, down);
+      k0 = (int64_t)(tm + 1) * BM;
+      dbl = true;
+    } else {
+      tile_of(G - n_off, tiles_m, n_cols, tm, col);
+      k0 = (int64_t)tm * BM;
+      k1 = min(d_in, k0 + BM);
+    }
+  } else {
     tile_of(G, tiles_m, n_cols, tm, col);
+  }
   const int cand = col / tiles_n;
   const int tn = col % tiles_n;
   const int64_t m0 = (int64_t)tm * BM;
@@ -117,13 +171,17 @@ __device__ __forceinline__ TileOps tile_ops(int G, const T* x, int64_t ld_x, con
   const int rows_b = (int)min((int64_t)BN, d_out - n0);
   const int lda_bytes = (int)(ld_x * (int64_t)sizeof(T));
   const int row_bytes = (int)(d_in * (int64_t)sizeof(T));
+  const int kb0 = (int)(k0 * (int64_t)sizeof(T));  // both bases start at K element k0
   TileOps t;
-  t.ra = make_rsrc(x + m0 * ld_x, (rows_a - 1) * lda_bytes + row_bytes);
-  t.rb = make_rsrc(delta + ((int64_t)cand * d_out + n0) * d_in, (rows_b - 1) * row_bytes + row_bytes);
+  t.ra = make_rsrc(x + m0 * ld_x + k0, (rows_a - 1) * lda_bytes + row_bytes - kb0);
+  t.rb = make_rsrc(delta + ((int64_t)cand * d_out + n0) * d_in + k0, (rows_b - 1) * row_bytes + row_bytes - kb0);
   t.idx = (int)(cand * cand_stride + (int64_t)tm * tiles_n + tn);
   t.m0 = (int)m0;
   t.n0 = (int)n0;
   t.cand = cand;
+  t.k_steps = (int)((k1 - k0) * (int64_t)sizeof(T) / KB);
+  t.k_last = down ? (t.k_steps - 1) * KB : 0;
+  t.dbl = dbl;
   return t;
 }
 
@@ -150,9 +208,11 @@ void error_sse_kernel(const T* __restrict__ x, int64_t ld_x, const T* __restrict
   __shared__ double red[4];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // kStore (G = X^T X, symmetric): only the tiles with tm <= tn
-  constexpr bool TRI = MODE == kStore;
-  const int nblk = TRI ? tiles_m * (tiles_m + 1) / 2 : tiles_m * n_cols;
+  // kStore (G = X^T X, symmetric): only the tiles with tm <= tn; kQuad: the blocks right of the
+  // diagonal, then the diagonal ones
+  const int nblk = MODE == kStore  ? tiles_m * (tiles_m + 1) / 2
+                   : MODE == kQuad ? (2 * tiles_m - 1) * n_cols
+                                   : tiles_m * n_cols;
 
   const int lda_bytes = (int)(ld_x * (int64_t)sizeof(T));
   const int row_bytes = (int)(d_in * (int64_t)sizeof(T));
@@ -169,6 +229,7 @@ void error_sse_kernel(const T* __restrict__ x, int64_t ld_x, const T* __restrict
   const uint32_t lds_base = __builtin_amdgcn_readfirstlane(lds_address(lds));
   // load i of 16 (8 of A, then 8 of B) of the stage at LDS address `stage`, K offset kbyte
   auto issue = [&](const TileOps& t, uint32_t stage, int i, int kbyte) {
+    if constexpr (MODE == kQuad) kbyte = t.k_last ? t.k_last - kbyte : kbyte;  // K step order
     if (i < 8)
       dma_load16(t.ra, __builtin_amdgcn_readfirstlane(stage + (4 * i + wave) * 8 * KB), voff_a[i], kbyte);
     else
@@ -184,7 +245,6 @@ void error_sse_kernel(const T* __restrict__ x, int64_t ld_x, const T* __restrict
   int slot[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) slot[q] = ((2 * q + fh) ^ swz(fr)) << 4;
-  const int k_steps = row_bytes / KB;  // >= 2: d_in is a positive multiple of 128
 
   f32x16 acc[FM][FN];
   auto frag = [&](const char* stage, int sl, int r) -> uint4 {
@@ -214,11 +274,33 @@ void error_sse_kernel(const T* __restrict__ x, int64_t ld_x, const T* __restrict
   };
   const std::false_type acc_in{};
   const std::true_type acc_zero{};
+  // kQuad: the epilogue's delta[o, j] (four consecutive j per 8 bytes), loaded while the tile's last
+  // K steps run; element e of accumulator (i, j) in lane l is row 32 i + 8 (e / 4) + 4 (l / 32) +
+  // e % 4 of the wave's 128 A rows and column 32 j + l % 32 of its 128 B rows. Here n_tokens = d_in
+  // is a multiple of 128, so a wave's A rows are all inside or all outside G; loads outside either
+  // matrix read a clamped address, and the epilogue skips their terms.
+  uint2 dq[FM][FN][4];
+  auto load_dq = [&](const TileOps& t) {
+    if constexpr (MODE == kQuad) {
+      const int64_t am = (int64_t)t.m0 + wm * 128 < n_tokens ? (int64_t)t.m0 + wm * 128 + 4 * fh : 0;
+      const int64_t bn = (int64_t)t.n0 + wn * 128 + fr;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int64_t o = min(bn + 32 * j, d_out - 1);  // row of this candidate's delta
+        const uint2* drow =
+            reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(delta) + ((int64_t)t.cand * d_out + o) * d_in + am);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) dq[i][j][q] = drow[8 * i + 2 * q];  // j index am + 32 i + 8 q
+      }
+    }
+  };
 
   int G = blockIdx.x;
   if (G >= nblk) return;
   const int64_t cand_stride = MODE == kQuad ? epi.cand_stride : (int64_t)tiles_m * tiles_n;
-  TileOps cur_t = tile_ops<T, TRI>(G, x, ld_x, delta, n_tokens, d_in, d_out, tiles_m, tiles_n, n_cols, cand_stride);
+  TileOps cur_t = tile_ops<T, MODE>(G, x, ld_x, delta, n_tokens, d_in, d_out, tiles_m, tiles_n, n_cols, cand_stride);
   int par = 0;  // LDS buffer holding the tile's K stage 0
 #pragma unroll
   for (int i = 0; i < 16; ++i) issue(cur_t, lds_base, i, 0);
@@ -227,8 +309,9 @@ void error_sse_kernel(const T* __restrict__ x, int64_t ld_x, const T* __restrict
     const int Gn = G + (int)gridDim.x;
     const bool has_next = Gn < nblk;
     const TileOps nxt_t =
-        tile_ops<T, TRI>(has_next ? Gn : G, x, ld_x, delta, n_tokens, d_in, d_out, tiles_m, tiles_n, n_cols,
-                         cand_stride);
+        tile_ops<T, MODE>(has_next ? Gn : G, x, ld_x, delta, n_tokens, d_in, d_out, tiles_m, tiles_n, n_cols,
+                          cand_stride);
+    const int k_steps = cur_t.k_steps;  // >= 2: K ranges are positive multiples of 128 elements
     uint4 f0[NR], f1[NR];
     // stage 0 is in flight in buffer par; the first kSplit loads of stage 1 go to the other
     // buffer (free: every wave passed the previous tile's final barrier); wait for stage 0
@@ -269,6 +352,7 @@ void error_sse_kernel(const T* __restrict__ x, int64_t ld_x, const T* __restrict
       substep(acc_in, f0, f1, cur, slot[3], true, cur_t, 0, 0, 0, 0);
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       __syncthreads();  // every wave has read all of stage k_steps-2: its buffer is free
+      load_dq(cur_t);
       substep(acc_in, f1, f0, nxt, slot[0], true, cur_t, 0, 0, 0, 0);
       substep(acc_in, f0, f1, nxt, slot[1], true, nxt_t, fre, 0, 0, min(nl, 8));
       ++kt;
@@ -299,10 +383,11 @@ void error_sse_kernel(const T* __restrict__ x, int64_t ld_x, const T* __restrict
           }
       __syncthreads();  // every wave has read the last stage
     } else {
-      // kSse: sum of squares; kQuad: sum of acc * delta[o, j] (A row j, B row o), four consecutive
-      // j per 8-byte load. Each accumulator's 16 terms in float32, then accumulators, lanes and
-      // waves in float64.
+      // kSse: sum of squares; kQuad: sum of acc * delta[o, j] (A row j, B row o; zero outside the
+      // matrices). Each accumulator's 16 terms in float32, then accumulators, lanes and waves in
+      // float64.
       double ss = 0.0;
+      const bool rows_in = MODE != kQuad || am - 4 * fh < n_tokens;  // kQuad: wave-uniform
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -311,18 +396,12 @@ void error_sse_kernel(const T* __restrict__ x, int64_t ld_x, const T* __restrict
           if constexpr (MODE == kSse) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) s32 = fmaf(acc[i][j][e], acc[i][j][e], s32);
-          } else {
-            const int64_t o = bn + 32 * j;  // row of this candidate's delta
-            const _Float16* drow = reinterpret_cast<const _Float16*>(delta) + ((int64_t)cur_t.cand * d_out + o) * d_in;
+          } else if (rows_in && bn + 32 * j < d_out) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              const int64_t m = am + 32 * i + 8 * q;  // K index j of the four terms (d_in % 4 == 0)
-              if (o < d_out && m < n_tokens) {
-                const uint2 u = *reinterpret_cast<const uint2*>(drow + m);
-                const f16x8 h = __builtin_bit_cast(f16x8, make_uint4(u.x, u.y, 0u, 0u));
+              const f16x8 h = __builtin_bit_cast(f16x8, make_uint4(dq[i][j][q].x, dq[i][j][q].y, 0u, 0u));
 #pragma unroll
-                for (int r = 0; r < 4; ++r) s32 = fmaf(acc[i][j][4 * q + r], (float)h[r], s32);
-              }
+              for (int r = 0; r < 4; ++r) s32 = fmaf(acc[i][j][4 * q + r], (float)h[r], s32);
             }
           }
           ss += (double)s32;
@@ -335,8 +414,15 @@ void error_sse_kernel(const T* __restrict__ x, int64_t ld_x, const T* __restrict
       __syncthreads();  // red is complete, and every wave has read the last stage
       if (threadIdx.x == 0) {
         double v = (red[0] + red[1]) + (red[2] + red[3]);
-        if constexpr (MODE == kQuad) v = ldexp(v, -(epi.gexp[0] + 2 * epi.dexp[cur_t.cand]));  // exact
-        tile_sse[cur_t.idx] = v;
+        if constexpr (MODE == kQuad) {
+          // exact unscaling; the two items of a tile_sse entry (diagonal block, blocks right of
+          // it) add onto the zero the caller wrote: 0 + a + b equals 0 + b + a, so the sum is
+          // independent of their order
+          v = ldexp(v, (cur_t.dbl ? 1 : 0) - (epi.gexp[0] + 2 * epi.dexp[cur_t.cand]));
+          atomicAdd(&tile_sse[cur_t.idx], v);
+        } else {
+          tile_sse[cur_t.idx] = v;
+        }
       }
     }
     if (!has_next) break;
@@ -400,7 +486,7 @@ hipError_t launch_quad_sse(const uint16_t* g16, const int32_t* gexp, const uint1
   const int tiles_m = (int)((d_in + BM - 1) / BM);
   const int tiles_n = (int)((d_out + BN - 1) / BN);
   const int n_cols = tiles_n * n_cand;
-  const unsigned grid = persistent_grid((int64_t)tiles_m * n_cols);
+  const unsigned grid = persistent_grid((int64_t)(2 * tiles_m - 1) * n_cols);
   Epi epi = {};
   epi.dexp = dexp;
   epi.gexp = gexp;

@@ -52,8 +52,10 @@ __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1
 
 // Tile order of the persistent 256 x 256 GEMMs: the hardware deals workgroups round-robin to the
 // 8 XCDs, so the 256 tiles processed together form a 16 x 16 super-block of (token tile, column)
-// pairs, each XCD taking an 8 x 4 sub-block; edge super-blocks go column-major. Tile of linear
-// index G: token tile tm, column col.
+// pairs, each XCD taking an 8 x 4 sub-block. In the last super-block row, h < 16 tiles high, each
+// XCD takes all h rows of 2 adjacent columns, so that every column's panel is still read by one
+// XCD's L2; super-blocks cut by the last column go column-major. Tile of linear index G: token
+// tile tm, column col.
 constexpr int kSuper = 16;
 constexpr int kXcds = 8;
 __device__ __forceinline__ void tile_of(int G, int tiles_m, int n_cols, int& tm, int& col) {
@@ -68,6 +70,10 @@ __device__ __forceinline__ void tile_of(int G, int tiles_m, int n_cols, int& tm,
     const int x = G2 % kXcds, q = G2 / kXcds;
     tm = kSuper * r + (x / 4) * 8 + q % 8;
     col = kSuper * c + (x % 4) * 4 + q / 8;
+  } else if (w == kSuper) {
+    const int x = G2 % kXcds, q = G2 / kXcds;  // q < 2 h
+    tm = kSuper * r + q % h;
+    col = kSuper * c + 2 * x + q / h;
   } else {
     tm = kSuper * r + G2 % h;
     col = kSuper * c + G2 / h;

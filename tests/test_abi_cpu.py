@@ -121,7 +121,7 @@ def test_gemm_and_argmin_validation(lib):
 
 
 def test_search_workspace_and_validation(lib):
-    need = lib.awq_search_workspace_bytes(1, 4096, 4096, 12288, 128, 20, 20)
+    need = lib.awq_search_workspace_bytes(1, 4095, 4096, 12288, 128, 20, 20)  # the direct form
     delta = 20 * 12288 * 4096 * 2
     sse = 20 * 16 * 48 * 8
     assert need == delta + ((sse + 255) // 256) * 256
@@ -335,24 +335,31 @@ def test_head_tie_validation(lib):
 
 
 def _gram_rule(dtype, n, d_in, d_out, n_grid):
-    """The documented choice of the Gram form: bf16, n >= d_in, 32-bit tile offsets, and G plus the
-    n_grid quadratic forms under 0.85 of the direct products' flops."""
+    """The documented choice of the Gram form: bf16, n >= d_in, 32-bit tile offsets, at most 2^31 - 1
+    work items in the quadratic form's launch, and G's upper tiles plus the n_grid quadratic forms over
+    G's upper blocks (d_in (d_in + 256) flops per token and per output row) under 0.85 of the direct
+    products' flops."""
     if dtype != 1 or n < d_in or d_in <= 0 or d_out <= 0 or n_grid < 1:
         return 0
     n_pad = (n + 63) // 64 * 64
     if 256 * n_pad * 2 > 0x7FFFFFFF:
         return 0
+    tiles_m, tiles_n = -(-d_in // 256), -(-d_out // 256)
+    if (2 * tiles_m - 1) * tiles_n * n_grid > 0x7FFFFFFF:
+        return 0
     direct = 2.0 * n * d_in * d_out * n_grid
-    gram = 2.0 * d_in * d_in * n_pad + 2.0 * d_out * d_in * d_in * n_grid
+    gram = d_in * (d_in + 256.0) * (n_pad + d_out * n_grid)
     return int(gram < 0.85 * direct)
 
 
 def test_loss_form_choice(lib):
-    # the four large workloads: the Gram form where tokens outnumber input channels enough
+    # the four large workloads have at least as many tokens as input channels: all take the Gram form
     assert lib.awq_search_loss_form(1, 65536, 28672, 8192, 40) == 1   # 70B down_proj stress
     assert lib.awq_search_loss_form(1, 16384, 11008, 4096, 20) == 1   # 7B down_proj
-    assert lib.awq_search_loss_form(1, 4096, 4096, 12288, 20) == 0    # 7B fused QKV
-    assert lib.awq_search_loss_form(1, 8192, 8192, 57344, 20) == 0    # 70B fused gate+up
+    assert lib.awq_search_loss_form(1, 4096, 4096, 12288, 20) == 1    # 7B fused QKV
+    assert lib.awq_search_loss_form(1, 8192, 8192, 57344, 20) == 1    # 70B fused gate+up
+    assert lib.awq_search_loss_form(1, 4095, 4096, 12288, 20) == 0    # fewer tokens than channels
+    assert lib.awq_search_loss_form(1, 2048, 256, 256, 1) == 0        # G costs more than one product
     assert lib.awq_search_loss_form(0, 65536, 256, 256, 20) == 0      # float32 activations
     assert lib.awq_search_loss_form(1, 5000000, 256, 256, 20) == 0    # 32-bit tile offsets
     import random
@@ -362,7 +369,7 @@ def test_loss_form_choice(lib):
         d_out, g = rng.randint(1, 70000), rng.randint(1, 64)
         assert lib.awq_search_loss_form(1, n, d_in, d_out, g) == _gram_rule(1, n, d_in, d_out, g), (n, d_in, d_out, g)
     # the search's workspace includes the Gram form's buffers exactly when it is chosen
-    direct = lib.awq_search_workspace_bytes(1, 4096, 4096, 12288, 128, 20, 20)
+    direct = lib.awq_search_workspace_bytes(1, 4095, 4096, 12288, 128, 20, 20)  # the direct form
     assert direct == (20 * 12288 * 4096 * 2) + ((20 * 16 * 48 * 8 + 255) // 256 * 256)
     gram = lib.awq_search_workspace_bytes(1, 65536, 28672, 8192, 128, 40, 40)
     base = 40 * 8192 * 28672 * 2 + (40 * 256 * 32 * 8 + 255) // 256 * 256

@@ -118,6 +118,9 @@ GRAM_CASES = [
     (1000, 384, (300,), 8, 3, "student_t3"),
     (1500, 256, (128, 256, 96), 12, 12, "normal"),
     (4096, 256, (256,), 20, 7, "student_t3"),
+    # 34 row tiles of G, the last 128 wide: two full super-block rows of the quadratic form's tile
+    # order (the second in reverse) and a partial one
+    (8600, 8576, (200,), 2, 2, "normal"),
 ]
 
 
