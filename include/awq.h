@@ -181,8 +181,9 @@ AWQ_API int awq_error_sse(const void* x, int64_t ld_x, const void* delta, int dt
 
 /* The same losses through the Gram matrix of the activations. By linearity the loss of a ratio is
  * sum_o ||X delta[o]^T||^2 / (N d_out) (gsyq section 二 target_out - actual_out; bjdmk L(s)), and
- * ||X v||^2 = v G v^T with G = X^T X: with G formed once, each ratio costs 2 d_out d_in^2 flops
- * instead of 2 N d_in d_out, fewer when there are more tokens than input channels. G is
+ * ||X v||^2 = v G v^T with G = X^T X: with G formed once, and G's symmetry leaving only its
+ * 256-blocks on and above the diagonal to multiply, each ratio costs about d_out d_in (d_in + 256)
+ * flops instead of 2 N d_in d_out, about half when tokens and input channels are as many. G is
  * accumulated in float32 by the matrix cores from the bfloat16 activations; both operands of the
  * quadratic form are float16, each scaled by a power of two into float16's range (exact, removed
  * exactly from the float64 tile sums). awq_search_scales uses this form by itself where it pays
@@ -190,9 +191,11 @@ AWQ_API int awq_error_sse(const void* x, int64_t ld_x, const void* delta, int dt
 typedef enum { AWQ_LOSS_DIRECT = 0, AWQ_LOSS_GRAM = 1 } awq_loss_form;
 
 /* The loss form awq_search_scales (and awq_search_scales_ex with AWQ_QUANT_INT4_GROUP) uses for
- * these sizes: AWQ_LOSS_GRAM for bfloat16 activations when forming G plus the n_grid quadratic forms
- * takes under 0.85 of the direct products' flops (and 256 * ceil(n_tokens / 64) * 64 * 2 < 2^31),
- * else AWQ_LOSS_DIRECT. Host-only. */
+ * these sizes: AWQ_LOSS_GRAM for bfloat16 activations with n_tokens >= d_in when G's upper tiles
+ * plus the n_grid quadratic forms, d_in (d_in + 256) (n_pad + n_grid d_out) flops with n_pad =
+ * ceil(n_tokens / 64) * 64, take under 0.85 of the direct products' 2 n_tokens d_in d_out n_grid
+ * (and 256 * n_pad * 2 < 2^31, and (2 ceil(d_in / 256) - 1) ceil(d_out / 256) n_grid < 2^31), else
+ * AWQ_LOSS_DIRECT. Host-only. */
 AWQ_API int awq_search_loss_form(int dtype, int64_t n_tokens, int64_t d_in, int64_t d_out, int n_grid);
 
 /* Workspace bytes of awq_gram: X^T padded to a multiple of 64 tokens (bfloat16) and G in float32.
@@ -223,7 +226,9 @@ AWQ_API int awq_quant_delta_f16(const void* const* w_parts, const int64_t* part_
  * accumulation, float64 tile sums, the scales removed), laid out as awq_error_sse's tile_sse so
  * that awq_loss_argmin gives the losses: candidate j's ceil(d_in/256) * ceil(d_out/256) tile sums
  * then zeros, awq_error_tiles(n_tokens, d_out) entries per candidate (n_tokens >= d_in, else
- * AWQ_ERR_SHAPE).
+ * AWQ_ERR_SHAPE). Tile (I, t) holds, over output rows t, delta_I G_II delta_I^T + 2 sum_{J>I}
+ * delta_I G_IJ delta_J^T for the 256-blocks I, J of d_in: only G's blocks on and above the diagonal
+ * are read. Each entry is the float64 sum of its two parts, independent of their order.
  *   gram, gram_exp    as written by awq_gram.
  *   delta, delta_exp  as written by awq_quant_delta_f16.
  *   tile_sse          device, float64 [n_cand, awq_error_tiles(n_tokens, d_out)], written. */
