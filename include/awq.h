@@ -194,8 +194,7 @@ typedef enum { AWQ_LOSS_DIRECT = 0, AWQ_LOSS_GRAM = 1 } awq_loss_form;
  * these sizes: AWQ_LOSS_GRAM for bfloat16 activations with n_tokens >= d_in when G's upper tiles
  * plus the n_grid quadratic forms, d_in (d_in + 256) (n_pad + n_grid d_out) flops with n_pad =
  * ceil(n_tokens / 64) * 64, take under 0.85 of the direct products' 2 n_tokens d_in d_out n_grid
- * (and 256 * n_pad * 2 < 2^31, and (2 ceil(d_in / 256) - 1) ceil(d_out / 256) n_grid < 2^31), else
- * AWQ_LOSS_DIRECT. Host-only. */
+ * (and 256 * n_pad * 2 < 2^31), else AWQ_LOSS_DIRECT. Host-only. */
 AWQ_API int awq_search_loss_form(int dtype, int64_t n_tokens, int64_t d_in, int64_t d_out, int n_grid);
 
 /* Workspace bytes of awq_gram: X^T padded to a multiple of 64 tokens (bfloat16) and G in float32.
@@ -228,7 +227,8 @@ AWQ_API int awq_quant_delta_f16(const void* const* w_parts, const int64_t* part_
  * then zeros, awq_error_tiles(n_tokens, d_out) entries per candidate (n_tokens >= d_in, else
  * AWQ_ERR_SHAPE). Tile (I, t) holds, over output rows t, delta_I G_II delta_I^T + 2 sum_{J>I}
  * delta_I G_IJ delta_J^T for the 256-blocks I, J of d_in: only G's blocks on and above the diagonal
- * are read. Each entry is the float64 sum of its two parts, independent of their order.
+ * are read. G's diagonal block enters halved and the tile's sum doubled; the halving is exact but for
+ * float16 values that fall below float16's normal range, under 2^-26 of G's largest entry.
  *   gram, gram_exp    as written by awq_gram.
  *   delta, delta_exp  as written by awq_quant_delta_f16.
  *   tile_sse          device, float64 [n_cand, awq_error_tiles(n_tokens, d_out)], written. */

@@ -1,7 +1,6 @@
 // Host side of the C ABI declared in include/awq.h: argument checks (all before any HIP call),
 // workspace sizing, and the composition of the search from its steps. No allocation happens
 // here; every buffer belongs to the caller.
-#include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -152,9 +151,6 @@ bool gram_form(int dtype, int64_t n_tokens, int64_t d_in, int64_t d_out, int n_g
   if (dtype != AWQ_DTYPE_BF16 || n_tokens < d_in || d_in <= 0 || d_out <= 0 || n_grid < 1) return false;
   const int64_t n_pad = awq::gram_n_pad(n_tokens);
   if ((int64_t)awq::kTileM * n_pad * 2 > 0x7FFFFFFF) return false;
-  const double tiles_m = (double)((d_in + awq::kTileM - 1) / awq::kTileM);
-  const double tiles_n = ceil((double)d_out / awq::kTileN);
-  if ((2.0 * tiles_m - 1.0) * tiles_n * n_grid > 2147483647.0) return false;  // the quadratic form's work items
   const double direct = 2.0 * (double)n_tokens * (double)d_in * (double)d_out * n_grid;
   const double gram = (double)d_in * ((double)d_in + awq::kTileM) * ((double)n_pad + (double)d_out * n_grid);
   return gram < 0.85 * direct;
@@ -459,8 +455,7 @@ int awq_gram_error_sse(const uint16_t* gram, const int32_t* gram_exp, const uint
   if (n_cand < 1 || n_cand > 65535) return fail(AWQ_ERR_ARG, "n_cand %d outside [1, 65535]", n_cand);
   if (d_out > ((int64_t)1 << 40) / d_in) return fail(AWQ_ERR_UNSUPPORTED, "d_out * d_in too large");
   const int64_t stride = awq_error_tiles(n_tokens, d_out);
-  const int64_t blocks =
-      (2 * ((d_in + awq::kTileM - 1) / awq::kTileM) - 1) * ((d_out + awq::kTileN - 1) / awq::kTileN) * n_cand;
+  const int64_t blocks = ((d_in + awq::kTileM - 1) / awq::kTileM) * ((d_out + awq::kTileN - 1) / awq::kTileN) * n_cand;
   if (blocks > 0x7FFFFFFF || stride * n_cand > 0x7FFFFFFF)
     return fail(AWQ_ERR_UNSUPPORTED, "%lld tiles exceed one launch", (long long)blocks);
   hipStream_t st = (hipStream_t)stream;

@@ -32,13 +32,14 @@
 // and B = the candidates' delta, both in float16, it sums products T[o, j] delta[o, j] per tile
 // (kQuad), T = delta G over a K range, so that the tiles hold shares of the quadratic form
 // delta G delta^T. With d_in cut into 256-blocks, the form is the sum over block pairs (I, J) of
-// delta_I G_IJ delta_J^T, and G_JI = G_IJ^T makes the (J, I) term equal to the (I, J) one: row tile I
-// runs K over block I alone (weight 1) and, in a tile of its own, over the blocks J > I (weight 2),
-// about half the matrix work of the full K range. The latter tiles' lengths fall with I, so a
-// compute unit takes row tile I and then row tile R - 1 - I of the same column (R rows have blocks
-// right of the diagonal): every pair has the same length, the 256 units stay in step, and their
-// 16 x 16 super-blocks keep sharing operands in L2. The first tile of a pair walks K down from d_in
-// and the second walks it up, so that at any moment the tiles of either kind read the same K slice.
+// delta_I G_IJ delta_J^T, and G_JI = G_IJ^T makes the (J, I) term equal to the (I, J) one, so the
+// form is sum_I (delta_I G_II delta_I^T + 2 sum_{J>I} delta_I G_IJ delta_J^T): row tile I runs K over
+// the blocks J >= I, about half the matrix work of the full K range, with G's fragments halved
+// while K is in block I and the tile's sum doubled. The tiles' lengths fall with I, so a compute
+// unit takes row tile I and then row tile T - 1 - I of the same column: every pair has the same
+// length, the 256 units stay in step, and their 16 x 16 super-blocks keep sharing operands in L2.
+// The first tile of a pair walks K down from d_in and the second walks it up, so that at any
+// moment the tiles of either kind read the same K slice.
 #include <algorithm>
 #include <type_traits>
 
@@ -82,6 +83,19 @@ __device__ __forceinline__ void mma_pair(const uint4& a, const uint4& b, f32x16&
   }
 }
 
+// A fragment of eight float16 values times f, a pair of equal float16 values (exact for a power
+// of two down to float16's normal range).
+__device__ __forceinline__ uint4 scale_f16x8(uint4 a, uint32_t f) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const h2 m = __builtin_bit_cast(h2, f);
+  a.x = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, a.x) * m);
+  a.y = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, a.y) * m);
+  a.z = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, a.z) * m);
+  a.w = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, a.w) * m);
+  return a;
+}
+constexpr uint32_t kF16One = 0x3C003C00u, kF16Half = 0x38003800u;
+
 constexpr int KB = 128;
 constexpr int kStageBytes = (BM + BN) * KB;  // 64 KiB
 constexpr int kThreads = 256;
@@ -98,7 +112,7 @@ struct TileOps {
   int m0, n0, cand;
   int k_steps;  // K steps of this tile (>= 2)
   int k_last;   // kQuad: byte offset of the last K step if K is walked downwards, else 0
-  bool dbl;     // kQuad: the tile's sum counts twice
+  int d0, d1;   // kQuad: the K steps [d0, d1) (in walk order) lie in the diagonal block
 };
 // Tile G of the upper triangle tm <= tn of a tiles x tiles grid, row by row.
 __device__ __forceinline__ void tri_of(int G, int tiles, int& tm, int& tn) {
@@ -111,12 +125,12 @@ __device__ __forceinline__ void tri_of(int G, int tiles, int& tm, int& tn) {
   tn = r + rem;
 }
 
-// kQuad work items: first the (tiles_m - 1) x n_cols tiles whose K range is the blocks right of
-// the diagonal, in pairs (see the file comment), then the tiles_m x n_cols diagonal blocks. Item G
-// runs on unit G % grid as that unit's (G / grid)-th tile, so pair p of the top rows is taken by
-// items that are grid apart: chunks of grid items alternate between first and second tiles (the
-// last, partial chunk of pairs lists its first tiles, then their partners).
-__device__ __forceinline__ void quad_off_tile(int G, int R, int n_cols, int grid, int& tm, int& col, bool& down) {
+// kQuad work items: the R x n_cols tiles (R = tiles_m) in pairs of rows (I, R - 1 - I), see the
+// file comment; with R odd the middle row comes last. Item G runs on unit G % grid as that unit's
+// (G / grid)-th tile, so pair p of the top rows is taken by items that are grid apart: chunks of
+// grid items alternate between first and second tiles (the last, partial chunk of pairs lists its
+// first tiles, then their partners).
+__device__ __forceinline__ void quad_tile(int G, int R, int n_cols, int grid, int& tm, int& col, bool& down) {
   const int n_pairs = (R / 2) * n_cols;
   if (G < 2 * n_pairs) {
     const int full = n_pairs / grid, rem = n_pairs - full * grid;
@@ -145,21 +159,13 @@ __device__ __forceinline__ TileOps tile_ops(int G, const T* x, int64_t ld_x, con
                                             int64_t d_in, int64_t d_out, int tiles_m, int tiles_n, int n_cols,
                                             int64_t cand_stride) {
   int tm, col;
-  int64_t k0 = 0, k1 = d_in;  // K range [k0, k1) in elements
-  bool dbl = false, down = false;
+  int64_t k0 = 0;  // K range [k0, d_in) in elements
+  bool down = false;
   if constexpr (MODE == kStore) {
     tri_of(G, tiles_m, tm, col);
   } else if constexpr (MODE == kQuad) {
-    const int n_off = (tiles_m - 1) * n_cols;
-    if (G < n_off) {
-      quad_off_tile(G, tiles_m - 1, n_cols, (int)gridDim.x, tm, col, down);
-      k0 = (int64_t)(tm + 1) * BM;
-      dbl = true;
-    } else {
-      tile_of(G - n_off, tiles_m, n_cols, tm, col);
-      k0 = (int64_t)tm * BM;
-      k1 = min(d_in, k0 + BM);
-    }
+    quad_tile(G, tiles_m, n_cols, (int)gridDim.x, tm, col, down);
+    k0 = (int64_t)tm * BM;
   } else {
     tile_of(G, tiles_m, n_cols, tm, col);
   }
@@ -179,9 +185,11 @@ __device__ __forceinline__ TileOps tile_ops(int G, const T* x, int64_t ld_x, con
   t.m0 = (int)m0;
   t.n0 = (int)n0;
   t.cand = cand;
-  t.k_steps = (int)((k1 - k0) * (int64_t)sizeof(T) / KB);
+  t.k_steps = (int)((d_in - k0) * (int64_t)sizeof(T) / KB);
   t.k_last = down ? (t.k_steps - 1) * KB : 0;
-  t.dbl = dbl;
+  const int nd = (int)(min((int64_t)BM, d_in - k0) * (int64_t)sizeof(T) / KB);  // the diagonal block's steps
+  t.d0 = MODE != kQuad ? 0 : down ? t.k_steps - nd : 0;
+  t.d1 = MODE != kQuad ? 0 : down ? t.k_steps : nd;
   return t;
 }
 
@@ -208,11 +216,8 @@ void error_sse_kernel(const T* __restrict__ x, int64_t ld_x, const T* __restrict
   __shared__ double red[4];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // kStore (G = X^T X, symmetric): only the tiles with tm <= tn; kQuad: the blocks right of the
-  // diagonal, then the diagonal ones
-  const int nblk = MODE == kStore  ? tiles_m * (tiles_m + 1) / 2
-                   : MODE == kQuad ? (2 * tiles_m - 1) * n_cols
-                                   : tiles_m * n_cols;
+  // kStore (G = X^T X, symmetric): only the tiles with tm <= tn
+  const int nblk = MODE == kStore ? tiles_m * (tiles_m + 1) / 2 : tiles_m * n_cols;
 
   const int lda_bytes = (int)(ld_x * (int64_t)sizeof(T));
   const int row_bytes = (int)(d_in * (int64_t)sizeof(T));
@@ -256,13 +261,17 @@ void error_sse_kernel(const T* __restrict__ x, int64_t ld_x, const T* __restrict
   // next sub-step's fragment reads (if `reads`). A load holds up the wave's issue for about as
   // long as the texture unit takes to accept its 64 addresses, so one per MFMA keeps the matrix
   // core fed (two back to back left it idle for ~10 % of the cycles).
-  // (zc: the tile's first sub-step, which writes every accumulator once from zero)
-  auto substep = [&](auto zc, const uint4 (&use)[NR], uint4 (&nxt)[NR], const char* src, int sl, bool reads,
+  // (zc: the tile's first sub-step, which writes every accumulator once from zero; kQuad: hf is the
+  // float16 pair that scales the A fragments of `use`'s K step, one half in the diagonal block)
+  auto substep = [&](auto zc, uint32_t hf, uint4 (&use)[NR], uint4 (&nxt)[NR], const char* src, int sl, bool reads,
                      const TileOps& lt, uint32_t fstage, int kbyte, int l0, int l1) {
     constexpr bool ZC = decltype(zc)::value;
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
       const int fm = g >> 1, fn = (g & 1) * 2;
+      if constexpr (MODE == kQuad) {
+        if ((g & 1) == 0) use[fm] = scale_f16x8(use[fm], hf);
+      }
       mma_pair<T, ZC, F16>(use[fm], use[FM + fn], acc[fm][fn]);
       __builtin_amdgcn_sched_barrier(0);
       if (l0 + g < l1) issue(lt, fstage, l0 + g, kbyte);
@@ -274,6 +283,10 @@ void error_sse_kernel(const T* __restrict__ x, int64_t ld_x, const T* __restrict
   };
   const std::false_type acc_in{};
   const std::true_type acc_zero{};
+  // kQuad: the factor of K step kt's A fragments in tile t
+  auto hf_of = [&](const TileOps& t, int kt) -> uint32_t {
+    return (unsigned)(kt - t.d0) < (unsigned)(t.d1 - t.d0) ? kF16Half : kF16One;
+  };
   // kQuad: the epilogue's delta[o, j] (four consecutive j per 8 bytes), loaded while the tile's last
   // K steps run; element e of accumulator (i, j) in lane l is row 32 i + 8 (e / 4) + 4 (l / 32) +
   // e % 4 of the wave's 128 A rows and column 32 j + l % 32 of its 128 B rows. Here n_tokens = d_in
@@ -326,7 +339,8 @@ void error_sse_kernel(const T* __restrict__ x, int64_t ld_x, const T* __restrict
     // one's fragments); the loop runs B C | barrier | D A', so that K step 0's A, which starts
     // the accumulators, stays outside it. Loads: the rest of stage kt+1 in A(kt), the first
     // kSplit of stage kt+2 in D(kt) into the buffer the barrier of step kt freed.
-    substep(acc_zero, f0, f1, lds + par * kStageBytes, slot[1], true, cur_t, lds_base + (par ^ 1) * kStageBytes, KB,
+    substep(acc_zero, hf_of(cur_t, 0), f0, f1, lds + par * kStageBytes, slot[1], true, cur_t,
+            lds_base + (par ^ 1) * kStageBytes, KB,
             kSplit, 16);
     int kt = 0;
     for (; kt + 2 < k_steps; ++kt) {
@@ -334,12 +348,13 @@ void error_sse_kernel(const T* __restrict__ x, int64_t ld_x, const T* __restrict
       char* cur = lds + b * kStageBytes;
       char* nxt = lds + (b ^ 1) * kStageBytes;
       const uint32_t fre = lds_base + b * kStageBytes;  // stage kt's buffer, refilled with stage kt+2
-      substep(acc_in, f1, f0, cur, slot[2], true, cur_t, 0, 0, 0, 0);
-      substep(acc_in, f0, f1, cur, slot[3], true, cur_t, 0, 0, 0, 0);
+      const uint32_t hf = hf_of(cur_t, kt);
+      substep(acc_in, hf, f1, f0, cur, slot[2], true, cur_t, 0, 0, 0, 0);
+      substep(acc_in, hf, f0, f1, cur, slot[3], true, cur_t, 0, 0, 0, 0);
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // stage kt+1 has landed
       __syncthreads();                           // and every wave has read all of stage kt
-      substep(acc_in, f1, f0, nxt, slot[0], true, cur_t, fre, (kt + 2) * KB, 0, kSplit);
-      substep(acc_in, f0, f1, nxt, slot[1], true, cur_t, fre, (kt + 2) * KB, kSplit, 16);
+      substep(acc_in, hf, f1, f0, nxt, slot[0], true, cur_t, fre, (kt + 2) * KB, 0, kSplit);
+      substep(acc_in, hf_of(cur_t, kt + 1), f0, f1, nxt, slot[1], true, cur_t, fre, (kt + 2) * KB, kSplit, 16);
     }
     {  // K step k_steps-2 (B C D), then A of the last step, which starts the next tile's stage 0
       // in the buffer this step's barrier freed
@@ -348,13 +363,14 @@ void error_sse_kernel(const T* __restrict__ x, int64_t ld_x, const T* __restrict
       char* nxt = lds + (b ^ 1) * kStageBytes;
       const uint32_t fre = lds_base + b * kStageBytes;
       const int nl = has_next ? 16 : 0;
-      substep(acc_in, f1, f0, cur, slot[2], true, cur_t, 0, 0, 0, 0);
-      substep(acc_in, f0, f1, cur, slot[3], true, cur_t, 0, 0, 0, 0);
+      const uint32_t hf = hf_of(cur_t, kt);
+      substep(acc_in, hf, f1, f0, cur, slot[2], true, cur_t, 0, 0, 0, 0);
+      substep(acc_in, hf, f0, f1, cur, slot[3], true, cur_t, 0, 0, 0, 0);
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       __syncthreads();  // every wave has read all of stage k_steps-2: its buffer is free
       load_dq(cur_t);
-      substep(acc_in, f1, f0, nxt, slot[0], true, cur_t, 0, 0, 0, 0);
-      substep(acc_in, f0, f1, nxt, slot[1], true, nxt_t, fre, 0, 0, min(nl, 8));
+      substep(acc_in, hf, f1, f0, nxt, slot[0], true, cur_t, 0, 0, 0, 0);
+      substep(acc_in, hf_of(cur_t, kt + 1), f0, f1, nxt, slot[1], true, nxt_t, fre, 0, 0, min(nl, 8));
       ++kt;
     }
     {  // K step k_steps-1: B C D
@@ -362,9 +378,10 @@ void error_sse_kernel(const T* __restrict__ x, int64_t ld_x, const T* __restrict
       char* cur = lds + b * kStageBytes;
       const uint32_t fre = lds_base + (b ^ 1) * kStageBytes;
       const int nl = has_next ? 16 : 0;
-      substep(acc_in, f1, f0, cur, slot[2], true, nxt_t, fre, 0, 8, nl);
-      substep(acc_in, f0, f1, cur, slot[3], true, nxt_t, 0, 0, 0, 0);
-      substep(acc_in, f1, f0, cur, slot[0], false, nxt_t, 0, 0, 0, 0);
+      const uint32_t hf = hf_of(cur_t, kt);
+      substep(acc_in, hf, f1, f0, cur, slot[2], true, nxt_t, fre, 0, 8, nl);
+      substep(acc_in, hf, f0, f1, cur, slot[3], true, nxt_t, 0, 0, 0, 0);
+      substep(acc_in, hf, f1, f0, cur, slot[0], false, nxt_t, 0, 0, 0, 0);
       par = b ^ 1;
     }
 
@@ -414,15 +431,9 @@ void error_sse_kernel(const T* __restrict__ x, int64_t ld_x, const T* __restrict
       __syncthreads();  // red is complete, and every wave has read the last stage
       if (threadIdx.x == 0) {
         double v = (red[0] + red[1]) + (red[2] + red[3]);
-        if constexpr (MODE == kQuad) {
-          // exact unscaling; the two items of a tile_sse entry (diagonal block, blocks right of
-          // it) add onto the zero the caller wrote: 0 + a + b equals 0 + b + a, so the sum is
-          // independent of their order
-          v = ldexp(v, (cur_t.dbl ? 1 : 0) - (epi.gexp[0] + 2 * epi.dexp[cur_t.cand]));
-          atomicAdd(&tile_sse[cur_t.idx], v);
-        } else {
-          tile_sse[cur_t.idx] = v;
-        }
+        // kQuad: doubled and unscaled, exactly
+        if constexpr (MODE == kQuad) v = ldexp(v, 1 - (epi.gexp[0] + 2 * epi.dexp[cur_t.cand]));
+        tile_sse[cur_t.idx] = v;
       }
     }
     if (!has_next) break;
@@ -486,7 +497,7 @@ hipError_t launch_quad_sse(const uint16_t* g16, const int32_t* gexp, const uint1
   const int tiles_m = (int)((d_in + BM - 1) / BM);
   const int tiles_n = (int)((d_out + BN - 1) / BN);
   const int n_cols = tiles_n * n_cand;
-  const unsigned grid = persistent_grid((int64_t)(2 * tiles_m - 1) * n_cols);
+  const unsigned grid = persistent_grid((int64_t)tiles_m * n_cols);
   Epi epi = {};
   epi.dexp = dexp;
   epi.gexp = gexp;

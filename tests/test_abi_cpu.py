@@ -335,17 +335,13 @@ def test_head_tie_validation(lib):
 
 
 def _gram_rule(dtype, n, d_in, d_out, n_grid):
-    """The documented choice of the Gram form: bf16, n >= d_in, 32-bit tile offsets, at most 2^31 - 1
-    work items in the quadratic form's launch, and G's upper tiles plus the n_grid quadratic forms over
-    G's upper blocks (d_in (d_in + 256) flops per token and per output row) under 0.85 of the direct
-    products' flops."""
+    """The documented choice of the Gram form: bf16, n >= d_in, 32-bit tile offsets, and G's upper
+    tiles plus the n_grid quadratic forms over G's upper blocks (d_in (d_in + 256) flops per token and
+    per output row) under 0.85 of the direct products' flops."""
     if dtype != 1 or n < d_in or d_in <= 0 or d_out <= 0 or n_grid < 1:
         return 0
     n_pad = (n + 63) // 64 * 64
     if 256 * n_pad * 2 > 0x7FFFFFFF:
-        return 0
-    tiles_m, tiles_n = -(-d_in // 256), -(-d_out // 256)
-    if (2 * tiles_m - 1) * tiles_n * n_grid > 0x7FFFFFFF:
         return 0
     direct = 2.0 * n * d_in * d_out * n_grid
     gram = d_in * (d_in + 256.0) * (n_pad + d_out * n_grid)
