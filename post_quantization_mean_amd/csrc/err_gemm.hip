@@ -124,6 +124,30 @@ __device__ __forceinline__ void tri_of(int G, int tiles, int& tm, int& tn) {
   tm = r;
   tn = r + rem;
 }
+// The same triangle in super-block rows of 16 tile rows: each row's h(h+1)/2 tiles on the diagonal
+// (row by row), then its h x (tiles - 16 R - h) tiles right of them in tile_of's order, so that the
+// tiles running together share operand panels inside each XCD's L2.
+__device__ __forceinline__ void tri_tile(int G, int tiles, int& tm, int& tn) {
+  int r0 = 0, rem = G;
+  for (;;) {
+    const int h = min(kSuper, tiles - r0), n_diag = h * (h + 1) / 2, n_right = h * (tiles - r0 - h);
+    if (rem < n_diag) {
+      tri_of(rem, h, tm, tn);
+      tm += r0;
+      tn += r0;
+      return;
+    }
+    rem -= n_diag;
+    if (rem < n_right) {
+      tile_of(rem, h, tiles - r0 - h, tm, tn);
+      tm += r0;
+      tn += r0 + h;
+      return;
+    }
+    rem -= n_right;
+    r0 += kSuper;
+  }
+}
 
 // kQuad work items: the R x n_cols tiles (R = tiles_m) in pairs of rows (I, R - 1 - I), see the
 // file comment; with R odd the middle row comes last. Item G runs on unit G % grid as that unit's
@@ -162,7 +186,7 @@ __device__ __forceinline__ TileOps tile_ops(int G, const T* x, int64_t ld_x, con
   int64_t k0 = 0;  // K range [k0, d_in) in elements
   bool down = false;
   if constexpr (MODE == kStore) {
-    tri_of(G, tiles_m, tm, col);
+    tri_tile(G, tiles_m, tm, col);
   } else if constexpr (MODE == kQuad) {
     quad_tile(G, tiles_m, n_cols, (int)gridDim.x, tm, col, down);
     k0 = (int64_t)tm * BM;
