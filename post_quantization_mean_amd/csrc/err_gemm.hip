@@ -290,12 +290,15 @@ void error_sse_kernel(const T* __restrict__ x, int64_t ld_x, const T* __restrict
   auto substep = [&](auto zc, uint32_t hf, uint4 (&use)[NR], uint4 (&nxt)[NR], const char* src, int sl, bool reads,
                      const TileOps& lt, uint32_t fstage, int kbyte, int l0, int l1) {
     constexpr bool ZC = decltype(zc)::value;
+    if constexpr (MODE == kQuad) {
+      if (hf != kF16One) {  // wave-uniform: only the diagonal block's K steps pay for the products
+#pragma unroll
+        for (int f = 0; f < FM; ++f) use[f] = scale_f16x8(use[f], hf);
+      }
+    }
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
       const int fm = g >> 1, fn = (g & 1) * 2;
-      if constexpr (MODE == kQuad) {
-        if ((g & 1) == 0) use[fm] = scale_f16x8(use[fm], hf);
-      }
       mma_pair<T, ZC, F16>(use[fm], use[FM + fn], acc[fm][fn]);
       __builtin_amdgcn_sched_barrier(0);
       if (l0 + g < l1) issue(lt, fstage, l0 + g, kbyte);
