@@ -118,9 +118,13 @@ GRAM_CASES = [
     (1000, 384, (300,), 8, 3, "student_t3"),
     (1500, 256, (128, 256, 96), 12, 12, "normal"),
     (4096, 256, (256,), 20, 7, "student_t3"),
-    # 34 row tiles of G, the last 128 wide: two full super-block rows of the quadratic form's tile
-    # order (the second in reverse) and a partial one
+    # 34 row tiles of G, the last 128 wide: 17 pairs of row tiles in the quadratic form
     (8600, 8576, (200,), 2, 2, "normal"),
+    # 3 row tiles, the last 128 wide: one pair and the middle row
+    (1200, 640, (300, 212), 6, 3, "student_t3"),
+    # 4 row tiles x 200 columns: 400 pairs over 256 compute units, one full chunk of first tiles and
+    # partners, then a partial one
+    (1100, 1024, (2560,), 20, 20, "normal"),
 ]
 
 
