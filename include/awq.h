@@ -190,7 +190,7 @@ AWQ_API int awq_error_sse(const void* x, int64_t ld_x, const void* delta, int dt
  * (awq_search_loss_form). */
 typedef enum { AWQ_LOSS_DIRECT = 0, AWQ_LOSS_GRAM = 1 } awq_loss_form;
 
-/* The loss form awq_search_scales (and awq_search_scales_ex with AWQ_QUANT_INT4_GROUP) uses for
+/* The loss form awq_search_scales (and awq_search_scales_ex, with any quantizer) uses for
  * these sizes: AWQ_LOSS_GRAM for bfloat16 activations with n_tokens >= d_in when G's upper tiles
  * plus the n_grid quadratic forms, d_in (d_in + 256) (n_pad + n_grid d_out) flops with n_pad =
  * ceil(n_tokens / 64) * 64, take under 0.85 of the direct products' 2 n_tokens d_in d_out n_grid
@@ -407,7 +407,10 @@ AWQ_API int awq_quant_delta_ex(const void* const* w_parts, const int64_t* part_r
 
 /* awq_search_scales over an explicit ratio list with a scale formula and a quantizer:
  * awq_candidate_scales_ex, then awq_quant_delta_ex + the error GEMM per pass of cand_per_pass
- * candidates, then awq_loss_argmin (k* indexes the list).
+ * candidates, then awq_loss_argmin (k* indexes the list). Where awq_search_loss_form says so, the
+ * loss takes the Gram form as in awq_search_scales, each quantizer's delta written in float16 with
+ * a power-of-two scale from a proven bound on |delta| (the symmetric INT8 quantizer's step floor
+ * widens that bound by 1.27e-6 / min(s_k)).
  *   w_mean     device, float64 [d_in]; read only by AWQ_FORMULA_DUO, may be NULL otherwise.
  *   ratios, n_ratios, formula: as awq_candidate_scales_ex.  quantizer: as awq_quant_delta_ex.
  *   workspace  device, >= awq_search_workspace_bytes(dtype, n_tokens, d_in, d_out, 128, n_ratios,

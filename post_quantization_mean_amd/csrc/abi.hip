@@ -207,8 +207,9 @@ int run_search(const void* x, int64_t ld_x, const void* const* w_parts, const in
   hipError_t e = ratios ? awq::launch_candidate_scales_ex(act_mean, w_mean, d_in, rl, n_grid, formula, cand_scales, st)
                         : awq::launch_candidate_scales(act_mean, d_in, n_grid, cand_scales, st);
   if (e != hipSuccess) return hip_fail(e, "candidate_scales launch");
-  if (quantizer == AWQ_QUANT_INT4_GROUP && gram_form(dtype, n_tokens, d_in, d_out, n_grid)) {
+  if (gram_form(dtype, n_tokens, d_in, d_out, n_grid)) {
     // the loss as the quadratic form of G = X^T X (float16 G and delta, power-of-two scales)
+    const double bound_b = quantizer == AWQ_QUANT_INT8_ROW_SYM ? 1.27e-6 : 1e-8;  // |delta|'s bound
     char* p = ws + round_up((size_t)cand_per_pass * (size_t)d_out * (size_t)d_in * esize(dtype), 256) +
               round_up((size_t)n_grid * (size_t)tiles * sizeof(double), 256);
     uint16_t* g16 = reinterpret_cast<uint16_t*>(p);
@@ -227,9 +228,11 @@ int run_search(const void* x, int64_t ld_x, const void* const* w_parts, const in
       const int nk = n_grid - k0 < cand_per_pass ? n_grid - k0 : cand_per_pass;
       const double* cs = cand_scales + (int64_t)k0 * d_in;
       double* ts = tile_sse + (int64_t)k0 * tiles;
-      if ((e = awq::launch_delta_exp(w, d_in, cs, nk, dexp, st)) != hipSuccess) return hip_fail(e, "delta_exp launch");
-      if ((e = awq::launch_quant_delta_f16(w, d_in, cs, nk, d16, dexp, st)) != hipSuccess)
-        return hip_fail(e, "quant_delta_f16 launch");
+      if ((e = awq::launch_delta_exp(w, d_in, cs, nk, bound_b, dexp, st)) != hipSuccess)
+        return hip_fail(e, "delta_exp launch");
+      e = quantizer == AWQ_QUANT_INT4_GROUP ? awq::launch_quant_delta_f16(w, d_in, cs, nk, d16, dexp, st)
+                                            : awq::launch_quant_delta_row_f16(w, d_in, quantizer, cs, nk, d16, dexp, st);
+      if (e != hipSuccess) return hip_fail(e, "quant_delta_f16 launch");
       if ((e = awq::launch_fill_f64(ts, (int64_t)nk * tiles, 0.0, st)) != hipSuccess) return hip_fail(e, "fill launch");
       if ((e = awq::launch_quad_sse(g16, gexp, d16, dexp, nk, d_in, d_out, tiles, ts, st)) != hipSuccess)
         return hip_fail(e, "gram_error_sse launch");
@@ -432,7 +435,7 @@ int awq_quant_delta_f16(const void* const* w_parts, const int64_t* part_rows, in
   if (!aligned(delta, 16)) return fail(AWQ_ERR_UNSUPPORTED, "delta is not 16-byte aligned");
   if (!aligned(cand_scales, 16)) return fail(AWQ_ERR_UNSUPPORTED, "cand_scales is not 16-byte aligned");
   if (!aligned(delta_exp, 4)) return fail(AWQ_ERR_UNSUPPORTED, "delta_exp is not 4-byte aligned");
-  hipError_t e = awq::launch_delta_exp(w, d_in, cand_scales, n_cand, delta_exp, (hipStream_t)stream);
+  hipError_t e = awq::launch_delta_exp(w, d_in, cand_scales, n_cand, 1e-8, delta_exp, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "delta_exp launch");
   e = awq::launch_quant_delta_f16(w, d_in, cand_scales, n_cand, delta, delta_exp, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "quant_delta_f16 launch");

@@ -167,13 +167,17 @@ __global__ __launch_bounds__(kThreads) void absmax_kernel(WParts w, int64_t d_in
   }
 }
 
-// The scale of ratio k's delta, from a bound on |delta|. A reconstructed value is (q - zero) step / s,
-// and the codes span the group's range to within half a step, so |(q - zero) step| <= max|y| +
-// step / 2 with step = max((max y - min y) / 15, 1e-8) <= max(2 max|y| / 15, 1e-8): at most
-// 1.5 max|y| + 1e-8. With |y| <= max|W| max(s_k), |What| <= (1.5 max|W| max(s_k) + 1e-8) / min(s_k),
-// and |W| adds at most max|W|. One block per ratio; dexp[n_cand] holds max|W| (absmax_kernel).
+// The scale of ratio k's delta, from a bound on |delta| = |What - W| <= |What| + max|W|, with
+// |What| <= (1.5 max|W| max(s_k) + b) / min(s_k) since |y| <= max|W| max(s_k):
+// * group INT4: a reconstructed value is (q - zero) step / s, and the codes span the group's range to
+//   within half a step, so |(q - zero) step| <= max|y| + step / 2 with step = max((max y - min y) /
+//   15, 1e-8) <= max(2 max|y| / 15, 1e-8): at most 1.5 max|y| + 1e-8 (b = 1e-8);
+// * row INT4: q = round(y / (step + 1e-6)), |q step| <= |y| + step / 2 <= (1 + 1/15) max|y| (b = 1e-8);
+// * row INT8 symmetric: |q| <= 127 and step = max(max|y| / 127, 1e-8), |q step| <= max(max|y|, 1.27e-6)
+//   (b = 1.27e-6).
+// One block per ratio; dexp[n_cand] holds max|W| (absmax_kernel).
 __global__ __launch_bounds__(kThreads) void delta_exp_kernel(const double* __restrict__ cand, int64_t d_in,
-                                                             int n_cand, int32_t* __restrict__ dexp) {
+                                                             int n_cand, double b, int32_t* __restrict__ dexp) {
   __shared__ double rmx[kThreads / 64], rmn[kThreads / 64];
   const int k = blockIdx.x;
   const double* s = cand + (int64_t)k * d_in;
@@ -200,7 +204,7 @@ __global__ __launch_bounds__(kThreads) void delta_exp_kernel(const double* __res
     mx = fmax(mx, rmx[0]);
     mn = fmin(mn, rmn[0]);
     const double wmax = (double)__uint_as_float(reinterpret_cast<const uint32_t*>(dexp)[n_cand]);
-    dexp[k] = scale_exp((1.5 * wmax * mx + 1e-8) / mn + wmax);
+    dexp[k] = scale_exp((1.5 * wmax * mx + b) / mn + wmax);
   }
 }
 
@@ -229,8 +233,8 @@ hipError_t launch_gram(const void* x, int64_t ld_x, int64_t n_tokens, int64_t d_
   return hipGetLastError();
 }
 
-hipError_t launch_delta_exp(const WParts& w, int64_t d_in, const double* cand_scales, int n_cand, int32_t* dexp,
-                            hipStream_t st) {
+hipError_t launch_delta_exp(const WParts& w, int64_t d_in, const double* cand_scales, int n_cand, double b,
+                            int32_t* dexp, hipStream_t st) {
   const int64_t d_out = w.row_begin[w.n];
   uint32_t* slot = reinterpret_cast<uint32_t*>(dexp + n_cand);
   hipLaunchKernelGGL(set_u32_kernel, dim3(1), dim3(64), 0, st, slot, 0u);
@@ -239,7 +243,7 @@ hipError_t launch_delta_exp(const WParts& w, int64_t d_in, const double* cand_sc
   hipLaunchKernelGGL(absmax_kernel, dim3((unsigned)std::min<int64_t>(d_out, 1024)), dim3(kThreads), 0, st, w, d_in,
                      d_out, slot);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(delta_exp_kernel, dim3((unsigned)n_cand), dim3(kThreads), 0, st, cand_scales, d_in, n_cand,
+  hipLaunchKernelGGL(delta_exp_kernel, dim3((unsigned)n_cand), dim3(kThreads), 0, st, cand_scales, d_in, n_cand, b,
                      dexp);
   return hipGetLastError();
 }

@@ -60,9 +60,11 @@ int64_t gram_n_pad(int64_t n_tokens);  // tokens of X^T's rows: a multiple of 64
 // into gexp[0] and float16(G * 2^gexp) into g16
 hipError_t launch_gram(const void* x, int64_t ld_x, int64_t n_tokens, int64_t d_in, uint16_t* xt, float* g32,
                        uint16_t* g16, int32_t* gexp, hipStream_t stream);
-// dexp[k] for k < n_cand: the scale exponent of ratio k's delta; dexp[n_cand]: max |W| (scratch)
-hipError_t launch_delta_exp(const WParts& w, int64_t d_in, const double* cand_scales, int n_cand, int32_t* dexp,
-                            hipStream_t stream);
+// dexp[k] for k < n_cand: the scale exponent of ratio k's delta, from the bound
+// (1.5 max|W| max(s_k) + b) / min(s_k) + max|W| (b: 1e-8 for the INT4 quantizers, 1.27e-6 for the
+// symmetric INT8 one); dexp[n_cand]: max |W| (scratch)
+hipError_t launch_delta_exp(const WParts& w, int64_t d_in, const double* cand_scales, int n_cand, double b,
+                            int32_t* dexp, hipStream_t stream);
 hipError_t launch_fill_f64(double* p, int64_t n, double v, hipStream_t stream);
 
 // ---- around the search: source fold and deployment form

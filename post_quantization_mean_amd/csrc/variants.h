@@ -22,6 +22,9 @@ hipError_t launch_candidate_scales_ex(const double* act_mean, const double* w_me
                                       hipStream_t stream);
 hipError_t launch_quant_delta_row(const WParts& w, int dtype, int64_t d_in, int quantizer, const double* cand_scales,
                                   int n_cand, void* delta, hipStream_t stream);
+// the per-row quantizers for the Gram form: bfloat16 weights, delta as float16 of delta * 2^dexp[k]
+hipError_t launch_quant_delta_row_f16(const WParts& w, int64_t d_in, int quantizer, const double* cand_scales,
+                                      int n_cand, uint16_t* delta, const int32_t* dexp, hipStream_t stream);
 hipError_t launch_fill(double* p, int64_t n, double v, hipStream_t stream);
 
 }  // namespace awq

@@ -177,13 +177,24 @@ __device__ __forceinline__ double div_by(double a, double s, double rs) {
 // weights come from HBM once and from the caches after that. Per candidate a first pass over each row
 // finds its extremes; the second goes through the row in 512-channel slices (lane l: channels 8l ..
 // 8l+7 of the slice), forms each channel's reciprocal scale once for the wave's rows, and writes the
-// rows' deltas.
+// rows' deltas: in the weights' type, or with F16 (bfloat16 weights, the Gram form of the loss) as
+// float16 of delta * 2^dexp[k].
 constexpr int kRowsPerWave = 4;
 
-template <typename T, int Q>
+__device__ __forceinline__ void store8_f16(uint16_t* p, const float (&v)[8], float sc) {
+  uint32_t h[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    h[j] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(v[2 * j] * sc)) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(v[2 * j + 1] * sc)) << 16);
+  *reinterpret_cast<uint4*>(p) = make_uint4(h[0], h[1], h[2], h[3]);
+}
+
+template <typename T, int Q, bool F16 = false>
 __global__ __launch_bounds__(kThreads) void quant_delta_row_kernel(WParts w, int64_t d_in, int d_out,
                                                                   const double* __restrict__ cand, int n_cand,
-                                                                  T* __restrict__ delta) {
+                                                                  T* __restrict__ delta,
+                                                                  const int32_t* __restrict__ dexp = nullptr) {
   constexpr int R = kRowsPerWave;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -194,6 +205,7 @@ __global__ __launch_bounds__(kThreads) void quant_delta_row_kernel(WParts w, int
   for (int r = 0; r < R; ++r) wr[r] = part_row<T>(w, min(o0 + r, d_out - 1), d_in);
   for (int k = 0; k < n_cand; ++k) {
     const double* s = cand + (int64_t)k * d_in;
+    const float sc = F16 ? ldexpf(1.f, dexp[k]) : 1.f;
     double mx[R], mn[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -251,7 +263,10 @@ __global__ __launch_bounds__(kThreads) void quant_delta_row_kernel(WParts w, int
           if constexpr (Q == kQuantInt8RowSym) q = q < -127.0 ? -127.0 : (q > 127.0 ? 127.0 : q);
           out[j] = (float)(div_by(q * step[r], sv[j], rs[j]) - wv[j]);
         }
-        store8(delta + ((int64_t)k * d_out + o0 + r) * d_in + c, out);
+        if constexpr (F16)
+          store8_f16(delta + ((int64_t)k * d_out + o0 + r) * d_in + c, out, sc);
+        else
+          store8(delta + ((int64_t)k * d_out + o0 + r) * d_in + c, out);
       }
     }
   }
@@ -298,6 +313,19 @@ hipError_t launch_quant_delta_row(const WParts& w, int dtype, int64_t d_in, int 
       hipLaunchKernelGGL((quant_delta_row_kernel<float, kQuantInt4Row>), grid, dim3(kThreads), 0, st, w, d_in,
                          d_out, cand_scales, n_cand, static_cast<float*>(delta));
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_delta_row_f16(const WParts& w, int64_t d_in, int quantizer, const double* cand_scales,
+                                      int n_cand, uint16_t* delta, const int32_t* dexp, hipStream_t st) {
+  const int d_out = (int)w.row_begin[w.n];
+  const dim3 grid((unsigned)((d_out + kRowWaves * kRowsPerWave - 1) / (kRowWaves * kRowsPerWave)));
+  if (quantizer == kQuantInt8RowSym)
+    hipLaunchKernelGGL((quant_delta_row_kernel<uint16_t, kQuantInt8RowSym, true>), grid, dim3(kThreads), 0, st, w,
+                       d_in, d_out, cand_scales, n_cand, delta, dexp);
+  else
+    hipLaunchKernelGGL((quant_delta_row_kernel<uint16_t, kQuantInt4Row, true>), grid, dim3(kThreads), 0, st, w,
+                       d_in, d_out, cand_scales, n_cand, delta, dexp);
   return hipGetLastError();
 }
 

@@ -177,16 +177,22 @@ def test_search_scales_takes_the_gram_form(B, cpp):
     assert np.array_equal(losses, steps)
 
 
-def test_gram_form_with_nonfinite_weights(B):
+@pytest.mark.parametrize("quant", [None, "int4_row", "int8_row_sym"])
+def test_gram_form_with_nonfinite_weights(B, quant):
     n_tokens, d_in, d_out, n_grid = 4096, 256, 256, 20
     wl = custom_workload(n_tokens, d_in, d_out, "bf16", n_grid=n_grid, config_id=304)
     x, w = make_x(wl), make_w(wl)
     w = w.copy()
     w[17, 40] = f32_to_bf16_bits(np.array([np.nan], np.float32))[0]
-    print("[gpu gram] NaN weight", flush=True)
+    print(f"[gpu gram] NaN weight, quantizer {quant or 'int4_group'}", flush=True)
     xt, wt = to_torch(x, "cuda"), to_torch(w, "cuda")
     act = B.awq_act_stats(xt)
-    res = B.awq_search_scales(xt, [wt], act, n_grid)
+    if quant is None:
+        res = B.awq_search_scales(xt, [wt], act, n_grid)
+    else:
+        q_c = B.AWQ_QUANT_INT4_ROW if quant == "int4_row" else B.AWQ_QUANT_INT8_ROW_SYM
+        res = B.awq_search_scales_ex(xt, [wt], act, [k / n_grid for k in range(n_grid)],
+                                     B.AWQ_FORMULA_MSMODELSLIM, q_c)
     torch.cuda.synchronize()
     info = res["best_info"].cpu().numpy()
     assert np.all(np.isnan(res["losses"].cpu().numpy()))
@@ -194,26 +200,32 @@ def test_gram_form_with_nonfinite_weights(B):
     assert np.all(res["best_scales"].cpu().numpy() == 1.0)
 
 
-@pytest.mark.parametrize("formula,grid", [("rms", "tenths"), ("duo", "linspace")])
-def test_search_ex_takes_the_gram_form(B, formula, grid):
-    # the variant search with the group INT4 quantizer runs the same loss code: a formula and grid of
-    # the other pages, in the Gram regime, against the variant oracle
+@pytest.mark.parametrize("formula,grid,quant", [("rms", "tenths", "int4_group"), ("duo", "linspace", "int4_group"),
+                                                ("duo", "linspace", "int4_row"), ("ms", "ms", "int8_row_sym"),
+                                                ("ms", "tenths", "int4_row")])
+def test_search_ex_takes_the_gram_form(B, formula, grid, quant):
+    # the variant search runs the same loss code with every quantizer (its delta in float16 with a
+    # power-of-two scale): a formula, grid and quantizer of the pages, in the Gram regime, against the
+    # variant oracle
     from oracle import awq_variants as V
     n_tokens, d_in, d_out = 4096, 256, 384
-    ratios = V.grid_tenths() if grid == "tenths" else V.grid_linspace(16)
-    f_c = B.AWQ_FORMULA_RMS if formula == "rms" else B.AWQ_FORMULA_DUO
-    f_o = V.FORMULA_RMS if formula == "rms" else V.FORMULA_DUO
+    ratios = {"tenths": V.grid_tenths(), "linspace": V.grid_linspace(16), "ms": V.grid_ms(20)}[grid]
+    f_c = {"rms": B.AWQ_FORMULA_RMS, "duo": B.AWQ_FORMULA_DUO, "ms": B.AWQ_FORMULA_MSMODELSLIM}[formula]
+    f_o = {"rms": V.FORMULA_RMS, "duo": V.FORMULA_DUO, "ms": V.FORMULA_MSMODELSLIM}[formula]
+    q_c = {"int4_group": B.AWQ_QUANT_INT4_GROUP, "int4_row": B.AWQ_QUANT_INT4_ROW,
+           "int8_row_sym": B.AWQ_QUANT_INT8_ROW_SYM}[quant]
+    q_o = {"int4_group": V.QUANT_INT4_GROUP, "int4_row": V.QUANT_INT4_ROW, "int8_row_sym": V.QUANT_INT8_ROW_SYM}[quant]
     assert B.awq_search_loss_form(B.AWQ_DTYPE_BF16, n_tokens, d_in, d_out, len(ratios)) == B.AWQ_LOSS_GRAM
     wl = custom_workload(n_tokens, d_in, d_out, "bf16", x_kind="student_t3", outlier_channels=3, config_id=305)
     x, w = make_x(wl), make_w(wl)
-    print(f"[gpu gram] awq_search_scales_ex {formula} {grid} x{x.shape}", flush=True)
+    print(f"[gpu gram] awq_search_scales_ex {formula} {grid} {quant} x{x.shape}", flush=True)
     xt, wt = to_torch(x, "cuda"), to_torch(w, "cuda")
     act = B.awq_act_stats(xt)
     wm = B.awq_weight_mean([wt]) if formula == "duo" else None
-    res = B.awq_search_scales_ex(xt, [wt], act, ratios, f_c, B.AWQ_QUANT_INT4_GROUP, w_mean=wm)
+    res = B.awq_search_scales_ex(xt, [wt], act, ratios, f_c, q_c, w_mean=wm)
     torch.cuda.synchronize()
     X, W = to_f32(x).astype(np.float64), to_f32(w).astype(np.float64)
-    _, ref_losses, ref_k, _ = V.search(X, W, ratios, f_o, V.QUANT_INT4_GROUP)
+    _, ref_losses, ref_k, _ = V.search(X, W, ratios, f_o, q_o)
     losses = res["losses"].cpu().numpy()
     info = res["best_info"].cpu().numpy()
     rel = P.max_rel(losses, ref_losses)
