@@ -243,13 +243,20 @@ __device__ __forceinline__ void store_pair(float* p, double a, double b) {
 __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) | ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
 }
+// E float32 values as float16 (round to nearest even; one v_cvt_pk_f16_f32 per pair)
 template <int E>
-__device__ __forceinline__ void storeE_f16(uint16_t* p, const float (&v)[E], float sc) {
+__device__ __forceinline__ void storeE_f16(uint16_t* p, const float (&v)[E]) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  uint32_t u[E / 2];
+#pragma unroll
+  for (int j = 0; j < E / 2; ++j) {
+    const f2 pair = {v[2 * j], v[2 * j + 1]};
+    u[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pair, h2));
+  }
 #pragma unroll
   for (int h = 0; h < E / 8; ++h)
-    *reinterpret_cast<uint4*>(p + 8 * h) =
-        make_uint4(pack_f16x2(v[8 * h] * sc, v[8 * h + 1] * sc), pack_f16x2(v[8 * h + 2] * sc, v[8 * h + 3] * sc),
-                   pack_f16x2(v[8 * h + 4] * sc, v[8 * h + 5] * sc), pack_f16x2(v[8 * h + 6] * sc, v[8 * h + 7] * sc));
+    *reinterpret_cast<uint4*>(p + 8 * h) = make_uint4(u[4 * h], u[4 * h + 1], u[4 * h + 2], u[4 * h + 3]);
 }
 
 // Extends a lane mask to whole groups of 8 lanes: any lane of a group set -> all of them.
@@ -322,7 +329,7 @@ __global__ __launch_bounds__(kThreads) void quant_delta_kernel(WParts w, int64_t
                                                                const int32_t* __restrict__ dexp = nullptr) {
   constexpr int E = kChans;
   __shared__ __attribute__((aligned(16))) float sc_s[2][kChansPerBlock];
-  __shared__ __attribute__((aligned(16))) float sc_i[2][kChansPerBlock];  // -1/s
+  __shared__ __attribute__((aligned(16))) float sc_i[2][kChansPerBlock];  // -1/s (F16: times 2^dexp[k])
   __shared__ __attribute__((aligned(16))) double sc_d[2][kChansPerBlock];  // for the exact path
   __shared__ __attribute__((aligned(16))) float xpose[4][kGroup];  // per wave: one group's weights
   const int tid = threadIdx.x;
@@ -356,17 +363,20 @@ __global__ __launch_bounds__(kThreads) void quant_delta_kernel(WParts w, int64_t
       p1 = p[1];
     }
   };
-  auto stage = [&](int buf) {
+  // F16: -1/s is stored times the candidate's 2^dexp, which scales every fast-path delta exactly
+  // (a power of two, far from float32's limits)
+  auto stage = [&](int buf, int kk) {
     const f32x4 sv = {(float)p0.x, (float)p0.y, (float)p1.x, (float)p1.y};
-    const f32x4 iv = {-__builtin_amdgcn_rcpf(sv.x), -__builtin_amdgcn_rcpf(sv.y), -__builtin_amdgcn_rcpf(sv.z),
-                      -__builtin_amdgcn_rcpf(sv.w)};
+    const float m = F16 ? -ldexpf(1.f, dexp[kk]) : -1.f;
+    const f32x4 iv = {m * __builtin_amdgcn_rcpf(sv.x), m * __builtin_amdgcn_rcpf(sv.y), m * __builtin_amdgcn_rcpf(sv.z),
+                      m * __builtin_amdgcn_rcpf(sv.w)};
     *reinterpret_cast<f32x4*>(&sc_s[buf][4 * tid]) = sv;
     *reinterpret_cast<f32x4*>(&sc_i[buf][4 * tid]) = iv;
     *reinterpret_cast<double2*>(&sc_d[buf][4 * tid]) = p0;
     *reinterpret_cast<double2*>(&sc_d[buf][4 * tid + 2]) = p1;
   };
   fetch(0);
-  stage(0);
+  stage(0, 0);
   if (n_cand > 1) fetch(1);
 
   uint64_t bad[kRows];  // per row: the lanes of the flagged groups (wave-uniform)
@@ -380,7 +390,7 @@ __global__ __launch_bounds__(kThreads) void quant_delta_kernel(WParts w, int64_t
       s[4 * h] = a.x; s[4 * h + 1] = a.y; s[4 * h + 2] = a.z; s[4 * h + 3] = a.w;
       nis[4 * h] = b.x; nis[4 * h + 1] = b.y; nis[4 * h + 2] = b.z; nis[4 * h + 3] = b.w;
     }
-    if (k + 1 < n_cand) stage((k + 1) & 1);
+    if (k + 1 < n_cand) stage((k + 1) & 1, k + 1);
     if (k + 2 < n_cand) fetch(k + 2);
     T* dk = delta + (int64_t)k * d_out * d_in + c0;
     float sc = 1.f;
@@ -393,6 +403,7 @@ __global__ __launch_bounds__(kThreads) void quant_delta_kernel(WParts w, int64_t
       const FastGroup fg = fast_group<E>(y);
       const float step = fg.step, inv = fg.inv;
       // r = round(y / step); e = y - r step (one rounding); delta = (r step - y) / s = e * (-1/s)
+      // (F16: delta * 2^dexp[k])
       float em = 0.f;
       float out[E];
 #pragma unroll
@@ -409,7 +420,7 @@ __global__ __launch_bounds__(kThreads) void quant_delta_kernel(WParts w, int64_t
       bad[i] = group_mask(__ballot(live && !ok));
       if (live && !((bad[i] >> lane) & 1)) {
         if constexpr (F16)
-          storeE_f16<E>(dk + o * d_in, out, sc);
+          storeE_f16<E>(dk + o * d_in, out);
         else
           storeE<T, E>(dk + o * d_in, out);
       }

@@ -181,12 +181,16 @@ __device__ __forceinline__ double div_by(double a, double s, double rs) {
 // float16 of delta * 2^dexp[k].
 constexpr int kRowsPerWave = 4;
 
+// v * sc (sc a power of two: exact) as float16, round to nearest even, one v_cvt_pk_f16_f32 per pair
 __device__ __forceinline__ void store8_f16(uint16_t* p, const float (&v)[8], float sc) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
   uint32_t h[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    h[j] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(v[2 * j] * sc)) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(v[2 * j + 1] * sc)) << 16);
+  for (int j = 0; j < 4; ++j) {
+    const f2 pair = {v[2 * j] * sc, v[2 * j + 1] * sc};
+    h[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pair, h2));
+  }
   *reinterpret_cast<uint4*>(p) = make_uint4(h[0], h[1], h[2], h[3]);
 }
 
