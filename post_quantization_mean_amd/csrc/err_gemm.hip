@@ -36,8 +36,9 @@
 // form is sum_I (delta_I G_II delta_I^T + 2 sum_{J>I} delta_I G_IJ delta_J^T): row tile I runs K over
 // the blocks J >= I, about half the matrix work of the full K range, with G's fragments halved
 // while K is in block I and the tile's sum doubled. The tiles' lengths fall with I, so a compute
-// unit takes row tile I and then row tile T - 1 - I of the same column: every pair has the same
-// length, the 256 units stay in step, and their 16 x 16 super-blocks keep sharing operands in L2.
+// unit takes row tile I and then row tile R - 1 - I of the same column (R = ceil(d_in / 256) row
+// tiles): every pair has the same length, the 256 units stay in step, and their 16 x 16
+// super-blocks keep sharing operands in L2.
 // The first tile of a pair walks K down from d_in and the second walks it up, so that at any
 // moment the tiles of either kind read the same K slice.
 #include <algorithm>
@@ -104,8 +105,9 @@ constexpr int kThreads = 256;
 // of the next step, so the texture unit sees no burst.
 constexpr int kSplit = 8;
 
-// Operand descriptors of one tile: A = its 256 token rows of X, B = its 256 rows of the
-// candidate's delta, each a raw buffer whose range ends at the last valid row.
+// Operand descriptors of one tile: A = its 256 rows of the first operand (tokens of X; in the Gram
+// form rows of X^T or of G), B = its 256 rows of the second (a candidate's delta; X^T), each a raw
+// buffer that starts at the tile's first K element and whose range ends at the last valid row.
 struct TileOps {
   i32x4 ra, rb;
   int idx;   // tile_sse index
@@ -124,9 +126,10 @@ __device__ __forceinline__ void tri_of(int G, int tiles, int& tm, int& tn) {
   tm = r;
   tn = r + rem;
 }
-// The same triangle in super-block rows of 16 tile rows: each row's h(h+1)/2 tiles on the diagonal
-// (row by row), then its h x (tiles - 16 R - h) tiles right of them in tile_of's order, so that the
-// tiles running together share operand panels inside each XCD's L2.
+// The same triangle in super-block rows of 16 tile rows: for the super-block row starting at tile
+// row r0, its h(h+1)/2 tiles on the diagonal (row by row), then its h x (tiles - r0 - h) tiles right
+// of them in tile_of's order, so that the tiles running together share operand panels inside each
+// XCD's L2.
 __device__ __forceinline__ void tri_tile(int G, int tiles, int& tm, int& tn) {
   int r0 = 0, rem = G;
   for (;;) {
