@@ -233,6 +233,36 @@ def test_search_ex_takes_the_gram_form(B, formula, grid, quant):
     assert rel < P.LOSS_RTOL and P.kstar_ok(int(info[0]), ref_k, ref_losses)
 
 
+@pytest.mark.parametrize("quant", ["int4_group", "int4_row", "int8_row_sym"])
+def test_gram_form_with_tiny_weights(B, quant):
+    # weights around 1e-8: the quantizers' step floor (1e-8) decides, so most codes are 0 or +-1 and
+    # delta is about as large as the weights; the float16 delta's scale comes from the bound's
+    # additive constant, which must still keep every value finite and in range
+    from oracle import awq_variants as V
+    n_tokens, d_in, d_out, n_grid = 4096, 256, 384, 10
+    wl = custom_workload(n_tokens, d_in, d_out, "bf16", n_grid=n_grid, outlier_channels=3, config_id=307)
+    x, w = make_x(wl), make_w(wl)
+    w = f32_to_bf16_bits((to_f32(w) * 1e-6).astype(np.float32))
+    ratios = V.grid_ms(n_grid)
+    q_c = {"int4_group": B.AWQ_QUANT_INT4_GROUP, "int4_row": B.AWQ_QUANT_INT4_ROW,
+           "int8_row_sym": B.AWQ_QUANT_INT8_ROW_SYM}[quant]
+    q_o = {"int4_group": V.QUANT_INT4_GROUP, "int4_row": V.QUANT_INT4_ROW, "int8_row_sym": V.QUANT_INT8_ROW_SYM}[quant]
+    assert B.awq_search_loss_form(B.AWQ_DTYPE_BF16, n_tokens, d_in, d_out, n_grid) == B.AWQ_LOSS_GRAM
+    print(f"[gpu gram] tiny weights, quantizer {quant}", flush=True)
+    xt, wt = to_torch(x, "cuda"), to_torch(w, "cuda")
+    act = B.awq_act_stats(xt)
+    res = B.awq_search_scales_ex(xt, [wt], act, ratios, B.AWQ_FORMULA_MSMODELSLIM, q_c)
+    torch.cuda.synchronize()
+    X, W = to_f32(x).astype(np.float64), to_f32(w).astype(np.float64)
+    _, ref_losses, ref_k, _ = V.search(X, W, ratios, V.FORMULA_MSMODELSLIM, q_o)
+    losses = res["losses"].cpu().numpy()
+    info = res["best_info"].cpu().numpy()
+    assert np.all(np.isfinite(losses)) and np.all(ref_losses > 0)
+    rel = P.max_rel(losses, ref_losses)
+    print(f"  losses max rel err {rel:.3e}; k* gpu {info[0]} oracle {ref_k}", flush=True)
+    assert rel < P.LOSS_RTOL and P.kstar_ok(int(info[0]), ref_k, ref_losses)
+
+
 def test_gram_search_in_a_hip_graph(B):
     # the Gram form adds only kernels (transpose, fills, scale choices) to the step: the whole layer
     # captured once and replayed on new activations equals eager runs bit for bit
