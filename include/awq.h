@@ -442,9 +442,11 @@ AWQ_API int awq_search_scales_ex(const void* x, int64_t ld_x, const void* const*
  *   zeros_u4  device, uint8 [d_out, ceil(d_in / 256)], groups 2i / 2i+1 in the low / high 4 bits.
  *   y         device, [n_tokens, ld_y] of y_dtype (AWQ_DTYPE_F32, or x_dtype: rounded to nearest
  *             even), ld_y >= d_out; written.
- * d_in must be a multiple of 128. n_tokens == 0 returns AWQ_ERR_NO_TOKENS. Up to 32 tokens use a
- * kernel that streams the weights once per 16 tokens; more use one that stages activations in LDS
- * (16 output rows per wave up to 512 tokens, 64 beyond). */
+ * d_in must be a multiple of 128. n_tokens == 0 returns AWQ_ERR_NO_TOKENS. One token (d_in up to
+ * 32768) uses a kernel whose waves stream whole weight rows; up to 32 tokens one that streams the
+ * weights once per 16 tokens; more use kernels that stage activations in LDS (16 output rows per
+ * wave up to 512 tokens, 64 up to 1023, 256 x 256 tiles from 1024); the order of the float32
+ * additions differs between these kernels. */
 AWQ_API int awq_w4a16_gemm(const void* x, int64_t ld_x, int x_dtype, const uint8_t* codes,
                    const uint16_t* steps_f16, const uint8_t* zeros_u4, int64_t n_tokens, int64_t d_in,
                    int64_t d_out, void* y, int64_t ld_y, int y_dtype, void* stream);

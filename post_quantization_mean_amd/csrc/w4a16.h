@@ -6,8 +6,10 @@
 
 namespace awq {
 
-// Launches with at most this many tokens use the few-token kernel (weights streamed once per 16
-// tokens); larger ones the many-token kernel (activations staged in LDS per block).
+// A single token with d_in <= 32768 uses the one-token kernel (each wave streams whole rows in 1 KiB
+// windows); launches with at most this many tokens otherwise use the few-token kernel (weights
+// streamed once per 16 tokens); larger ones the many-token kernels (activations staged in LDS per
+// block).
 constexpr int64_t kW4a16SmallMaxTokens = 32;
 
 bool w4a16_uses_big_kernel(int64_t n_tokens);

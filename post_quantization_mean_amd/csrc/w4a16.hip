@@ -191,6 +191,158 @@ __global__ __launch_bounds__(64 * kSmallWaves) void w4a16_small_kernel(const uin
   }
 }
 
+// One token (decode): the weights stream through in contiguous 1 KiB windows, one output row at a
+// time per wave. Lane l of a window holds the row's codes 32 l .. 32 l + 31 (one 16-byte load, all in
+// group l / 4 of the window's 16), so each wave load reads 1 KiB of consecutive bytes. The token's
+// activations sit in LDS, chunk t (8 values) of lane l's 32 at t KiB + 16 l of the window's 4 KiB, so
+// that the four reads of a window are conflict-free. Products use v_mfma_f32_16x16x32 with the lane's
+// activations as A and its dequantized weights as B: the diagonal C[i][i] collects the products of
+// the lanes i, i + 16, i + 32, i + 48, so the sum of the diagonal over all windows is the row's dot
+// product (the off-diagonal entries are discarded). Dequantization per 8 codes: (q, q') pairs of
+// nibbles e and e + 4 are placed in the mantissas of two float16 values 1024 + q (one and-or), and
+// fma(1024 + q, step, -(1024 + zero) * step) = (q - zero) * step exactly in float32 (both products
+// need at most 22 bits), rounded once to the operand type: the same values the other kernels form.
+constexpr int kGemvWaves = 8;
+constexpr int kGemvDepth = 8;         // windows in flight per wave
+constexpr int kGemvMaxIn = 32768;     // the LDS copy of the activations (64 KiB)
+constexpr int kGemvBlocks = 512;      // two blocks per compute unit
+
+// (h & mask) | magic in one instruction: VOP3 takes no literal operand on this architecture, so the
+// mask comes in a scalar register and the float16 exponent pattern in a vector register.
+__device__ __forceinline__ uint32_t and_or(uint32_t h, uint32_t mask, uint32_t magic) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(h), "s"(mask), "v"(magic));
+  return r;
+}
+
+// Per-lane constants of a group: fma(1024 + q, st, c0) and fma(1024 + 16 q, st16, c16) both give
+// (q - zero) * step exactly.
+struct MixParams {
+  float st, c0, st16, c16;
+};
+
+template <int KIND>
+__device__ __forceinline__ uint4 dequant8_mix(uint32_t w, const MixParams& p, uint32_t magic) {
+  const uint32_t w8 = w >> 8;
+  const f16x2_t h0 = __builtin_bit_cast(f16x2_t, and_or(w, 0x000F000Fu, magic));   // nibbles 0, 4
+  const f16x2_t h1 = __builtin_bit_cast(f16x2_t, and_or(w, 0x00F000F0u, magic));   // 1, 5 (times 16)
+  const f16x2_t h2 = __builtin_bit_cast(f16x2_t, and_or(w8, 0x000F000Fu, magic));  // 2, 6
+  const f16x2_t h3 = __builtin_bit_cast(f16x2_t, and_or(w8, 0x00F000F0u, magic));  // 3, 7 (times 16)
+  const float v0 = fmaf((float)h0.x, p.st, p.c0), v4 = fmaf((float)h0.y, p.st, p.c0);
+  const float v1 = fmaf((float)h1.x, p.st16, p.c16), v5 = fmaf((float)h1.y, p.st16, p.c16);
+  const float v2 = fmaf((float)h2.x, p.st, p.c0), v6 = fmaf((float)h2.y, p.st, p.c0);
+  const float v3 = fmaf((float)h3.x, p.st16, p.c16), v7 = fmaf((float)h3.y, p.st16, p.c16);
+  return make_uint4(pack2(v0, v1, KIND), pack2(v2, v3, KIND), pack2(v4, v5, KIND), pack2(v6, v7, KIND));
+}
+
+template <int KIND, typename OutT>
+__global__ __launch_bounds__(64 * kGemvWaves) void w4a16_gemv_kernel(const uint16_t* __restrict__ x,
+                                                                     const uint8_t* __restrict__ codes,
+                                                                     const uint16_t* __restrict__ steps,
+                                                                     const uint8_t* __restrict__ zeros, int d_in,
+                                                                     int d_out, int rows_per_wave,
+                                                                     OutT* __restrict__ y) {
+  extern __shared__ uint4 xs[];  // windows x 4 KiB
+  constexpr int D = kGemvDepth;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int G = d_in / kGroup, GZ = (G + 1) / 2, W = (G + 15) / 16;
+  const int r0 = (blockIdx.x * kGemvWaves + wave) * rows_per_wave;
+  const int r1 = min(r0 + rows_per_wave, d_out);
+  const int n_items = r1 > r0 ? (r1 - r0) * W : 0;
+  const int lg = lane >> 2;  // the lane's group within a window
+
+  uint4 cw[D];
+  // the narrow loads stay in their own types: a zero extension at the loop's back edge would wait for
+  // every load in flight
+  uint16_t sr[D];
+  uint8_t zr[D];
+  int lrow = r0, lwin = 0, lcount = 0;  // next item to load
+  // items past the wave's last re-load its last one (the same cache lines; never used); a wave
+  // without rows has r1 = d_out and re-reads the last row
+  auto load_item = [&](int u) {
+    const bool in = lcount < n_items;
+    const int64_t o = in ? lrow : r1 - 1;
+    const int g = min((in ? lwin : W - 1) * 16 + lg, G - 1);  // lanes past the row's last group re-read it
+    cw[u] = *reinterpret_cast<const uint4*>(codes + o * (d_in / 2) + (int64_t)g * (kGroup / 2) + (lane & 3) * 16);
+    sr[u] = steps[o * G + g];
+    zr[u] = zeros[o * GZ + (g >> 1)];
+    ++lcount;
+    if (++lwin == W) lwin = 0, ++lrow;
+    // keep the slots' loads in slot order, as the waits assume
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // the activations into LDS, window by window, chunk c of a window (8 values, c = 4 l + t) at
+  // t KiB + 16 l, past d_in zeros. Their loads go out first, then the ring's first loads, so that the
+  // stores wait only for the activations.
+  {
+    constexpr int kIters = kGemvMaxIn / 8 / (64 * kGemvWaves);
+    uint4 v[kIters];
+#pragma unroll
+    for (int i = 0; i < kIters; ++i) {  // every load issued before the first store
+      const int c = threadIdx.x + i * 64 * kGemvWaves;
+      v[i] = make_uint4(0, 0, 0, 0);
+      if (c * 8 < d_in) v[i] = *reinterpret_cast<const uint4*>(x + (int64_t)c * 8);
+    }
+    // unconditional, so that the count of loads in flight is the same in every wave
+#pragma unroll
+    for (int u = 0; u < D; ++u) load_item(u);
+#pragma unroll
+    for (int i = 0; i < kIters; ++i) {
+      const int c = threadIdx.x + i * 64 * kGemvWaves, cc = c & 255;
+      if (c < W * 256) xs[(c >> 8) * 256 + (cc & 3) * 64 + (cc >> 2)] = v[i];
+    }
+  }
+  __syncthreads();
+
+  const uint32_t magic = 0x64006400u;  // float16 1024 in both halves
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  int crow = r0, cwin = 0;  // next item to consume
+  auto consume = [&](int u) {
+    const int g = cwin * 16 + lg;
+    const float s = (float)__builtin_bit_cast(_Float16, sr[u]);
+    const int z = __builtin_amdgcn_ubfe(zr[u], (lg & 1) * 4, 4);
+    MixParams p;
+    p.st = s;
+    p.c0 = -(float)(1024 + z) * s;  // exact: 11-bit integer times an 11-bit mantissa
+    p.st16 = s * 0.0625f;
+    p.c16 = -(float)(64 + z) * s;
+    if (g >= G) p.st = p.c0 = p.st16 = p.c16 = 0.f;  // past the row's end: weight 0 (the LDS holds zeros there)
+    const uint4* xw = xs + cwin * 256 + lane;
+    const uint32_t wt[4] = {cw[u].x, cw[u].y, cw[u].z, cw[u].w};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc = mma<KIND>(xw[64 * t], dequant8_mix<KIND>(wt[t], p, magic), acc);
+    if (++cwin == W) {
+      // the diagonal: lane l holds C[4 (l / 16) + i][l mod 16] in acc[i]
+      const int i = (lane & 15) - 4 * (lane >> 4);
+      float d = (i == 0) ? acc.x : (i == 1) ? acc.y : (i == 2) ? acc.z : (i == 3) ? acc.w : 0.f;
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) d += __shfl_xor(d, m);
+      if (lane == 0) y[crow] = to_out<OutT>(d, KIND);
+      acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      cwin = 0;
+      ++crow;
+    }
+  };
+  // a slot is consumed, then refilled with the item D places later; the loads are unconditional so
+  // that every wait counts a fixed number of loads in flight, except in the last round, which loads
+  // nothing
+  for (int base = 0; base < n_items; base += D) {
+    if (base + D < n_items) {
+#pragma unroll
+      for (int u = 0; u < D; ++u) {
+        if (base + u < n_items) consume(u);  // wave-uniform
+        load_item(u);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < D; ++u)
+        if (base + u < n_items) consume(u);
+    }
+  }
+}
+
 // Many tokens (prefill): a block computes 128 tokens x 64 NJ output rows, each wave 128 tokens x
 // 16 NJ rows (NJ = 4 for prefill, 1 up to a few hundred tokens). Per group the block's activations (128 tokens x 128 inputs, 32 KiB) go global -> LDS by
 // DMA, 16-byte chunks of a token row XOR-swizzled by the token so that the 16 lanes of a fragment
@@ -644,6 +796,13 @@ hipError_t launch_kind(const void* x, int64_t ld_x, const uint8_t* codes, const 
     else
       hipLaunchKernelGGL((w4a16_big_kernel<KIND, OutT, kMidNJ>), dim3((unsigned)((d_out + 64 * kMidNJ - 1) / (64 * kMidNJ)), gy),
                          dim3(kThreads), 0, st, xp, ld_x, codes, steps, zeros, n_tokens, d_in, d_out, yp, ld_y);
+  } else if (n_tokens == 1 && d_in <= kGemvMaxIn) {
+    // about kGemvBlocks blocks of kGemvWaves waves, each wave a run of whole rows
+    const int W = (d_in / kGroup + 15) / 16;
+    const int rpw = (d_out + kGemvWaves * kGemvBlocks - 1) / (kGemvWaves * kGemvBlocks);
+    const unsigned blocks = (unsigned)((d_out + kGemvWaves * rpw - 1) / (kGemvWaves * rpw));
+    hipLaunchKernelGGL((w4a16_gemv_kernel<KIND, OutT>), dim3(blocks), dim3(64 * kGemvWaves), W * 4096, st, xp, codes,
+                       steps, zeros, d_in, d_out, rpw, yp);
   } else {
     const dim3 grid((unsigned)((d_out + 16 * kSmallNT - 1) / (16 * kSmallNT)), (unsigned)((n_tokens + 15) / 16));
     hipLaunchKernelGGL((w4a16_small_kernel<KIND, OutT>), grid, dim3(64 * kSmallWaves), 0, st, xp, ld_x, codes, steps, zeros,

@@ -156,3 +156,112 @@ def _check_tile(n_tokens, d_in, d_out, ld_x):
     (4096, 4096, 12288, 4096), (1024, 11008, 4096, 11008)])
 def test_tile_kernel_loads_stay_inside(n_tokens, d_in, d_out, ld_x):
     assert _check_tile(n_tokens, d_in, d_out, ld_x) == 0
+
+
+# ------------------------------------------------------------------ the one-token kernel
+
+GEMV_WAVES, GEMV_DEPTH, GEMV_BLOCKS, GEMV_MAX_IN = 8, 8, 512, 32768
+
+
+def _gemv_launch(d_in, d_out):
+    W = (d_in // 128 + 15) // 16
+    rpw = (d_out + GEMV_WAVES * GEMV_BLOCKS - 1) // (GEMV_WAVES * GEMV_BLOCKS)
+    return W, rpw, (d_out + GEMV_WAVES * rpw - 1) // (GEMV_WAVES * rpw)
+
+
+def _check_gemv(d_in, d_out):
+    """Every wave's prefetch ring (D windows ahead, loads past the wave's last window clamped to it),
+    its consumption order, the activation staging and the LDS reads. Returns how often each (row,
+    window) was consumed and each row written."""
+    G, GZ = d_in // 128, (d_in // 128 + 1) // 2
+    W, rpw, blocks = _gemv_launch(d_in, d_out)
+    assert W * 4096 <= 65536
+    lane = np.arange(64)
+    lg = lane >> 2
+    consumed = np.zeros((d_out, W), int)
+    written = np.zeros(d_out, int)
+    code_bytes, n_steps, n_zeros = d_out * d_in // 2, d_out * G, d_out * GZ
+    c = np.arange(GEMV_MAX_IN // 8)  # staging: chunk c -> LDS slot, only chunks below W 256 stored
+    cc = c & 255
+    slot = (c >> 8) * 256 + (cc & 3) * 64 + (cc >> 2)
+    stored = c < W * 256
+    assert np.all(slot[stored] < W * 256) and len(set(slot[stored])) == W * 256
+    assert np.all((c[stored] * 8 >= d_in) | (c[stored] * 8 + 8 <= d_in))  # a chunk is wholly in x or past it
+    for b in range(blocks):
+        for wave in range(GEMV_WAVES):
+            r0 = (b * GEMV_WAVES + wave) * rpw
+            r1 = min(r0 + rpw, d_out)
+            n_items = (r1 - r0) * W if r1 > r0 else 0
+            ld = {"row": r0, "win": 0, "count": 0}
+
+            def load():
+                inside = ld["count"] < n_items
+                o = ld["row"] if inside else r1 - 1
+                g = np.minimum((ld["win"] if inside else W - 1) * 16 + lg, G - 1)
+                a = o * (d_in // 2) + g * 64 + (lane & 3) * 16
+                assert o >= 0 and np.all(a >= 0) and np.all(a + 16 <= code_bytes)
+                assert np.all(o * G + g < n_steps) and np.all(o * GZ + (g >> 1) < n_zeros)
+                ld["count"] += 1
+                ld["win"] += 1
+                if ld["win"] == W:
+                    ld["win"], ld["row"] = 0, ld["row"] + 1
+
+            for _ in range(GEMV_DEPTH):  # unconditional: a wave without rows re-reads the last row
+                load()
+            crow, cwin = r0, 0
+            for base in range(0, n_items, GEMV_DEPTH):
+                for u in range(GEMV_DEPTH):
+                    if base + u < n_items:
+                        consumed[crow, cwin] += 1
+                        assert np.all(cwin * 256 + lane + 64 * 3 < W * 256)
+                        cwin += 1
+                        if cwin == W:
+                            written[crow] += 1
+                            cwin, crow = 0, crow + 1
+                    if base + GEMV_DEPTH < n_items:
+                        load()
+    return consumed, written
+
+
+@pytest.mark.parametrize("d_in,d_out", [(128, 1), (128, 17), (2176, 300), (640, 1), (1920, 8193), (4224, 4097),
+                                        (32768, 40), (4096, 12288), (28672, 8192), (11008, 4096), (256, 40000)])
+def test_one_token_kernel_loads_and_coverage(d_in, d_out):
+    consumed, written = _check_gemv(d_in, d_out)
+    assert np.all(consumed == 1) and np.all(written == 1)
+
+
+def test_one_token_diagonal_lanes():
+    # the 16x16 accumulator's diagonal sits in lanes 20 q + i (q, i < 4), element i, one per lane
+    lane = np.arange(64)
+    i = (lane & 15) - 4 * (lane >> 4)
+    diag = (i >= 0) & (i < 4)
+    rows, cols = 4 * (lane[diag] >> 4) + i[diag], lane[diag] & 15
+    assert np.array_equal(rows, cols) and sorted(rows) == list(range(16))
+
+
+def test_one_token_dequant_identity():
+    # the nibble pairs placed in float16 mantissas and the two fused multiply-adds reproduce
+    # (q - zero) * step exactly in float32, for every code, zero point and a spread of float16 steps
+    # (subnormal, smallest normal, 1, largest); float64 evaluates the fma exactly
+    steps = np.array([2.0 ** -24, 2.0 ** -14, 0.00123, 1.0, 3.5, 65504.0], np.float16).astype(np.float64)
+    q = np.arange(16)
+    for w in [0x76543210, 0xFEDCBA98, 0x0F0F0F0F, 0xF0F0F0F0]:
+        nib = [(w >> (4 * e)) & 15 for e in range(8)]
+        w8 = w >> 8
+        h = [(w & 0x000F000F) | 0x64006400, (w & 0x00F000F0) | 0x64006400,
+             (w8 & 0x000F000F) | 0x64006400, (w8 & 0x00F000F0) | 0x64006400]
+        halves = np.array([[x & 0xFFFF, x >> 16] for x in h], np.uint16).view(np.float16).astype(np.float64)
+        # h0 = (1024 + q0, 1024 + q4), h1 = (1024 + 16 q1, 1024 + 16 q5), h2 / h3 likewise for 2, 6 / 3, 7
+        assert np.array_equal(halves[0], 1024 + np.array([nib[0], nib[4]]))
+        assert np.array_equal(halves[1], 1024 + 16 * np.array([nib[1], nib[5]]))
+        assert np.array_equal(halves[2], 1024 + np.array([nib[2], nib[6]]))
+        assert np.array_equal(halves[3], 1024 + 16 * np.array([nib[3], nib[7]]))
+    for s in steps:
+        for z in range(16):
+            c0 = np.float32(-(1024 + z) * s)
+            c16 = np.float32(-(64 + z) * s)
+            assert c0 == -(1024 + z) * s and c16 == -(64 + z) * s  # the constants are exact in float32
+            v0 = np.float32((1024 + q) * np.float64(np.float32(s)) + np.float64(c0))
+            v1 = np.float32((1024 + 16 * q) * np.float64(np.float32(s * 0.0625)) + np.float64(c16))
+            want = (q - z) * s
+            assert np.array_equal(v0.astype(np.float64), want) and np.array_equal(v1.astype(np.float64), want)
