@@ -25,12 +25,14 @@ namespace awq {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBatch = 4;   // small-M kernel: groups whose codes a wave loads at once
-constexpr int kXSub = 4;    // small-M kernel: groups whose activations are loaded at once
+constexpr int kBatch = 2;   // small-M kernel: groups whose codes a wave loads at once
+constexpr int kXSub = 2;    // small-M kernel: groups whose activations are loaded at once
 constexpr int kSmallWaves = 8;  // small-M kernel: waves per block, each 1/8 of the groups (a 4096-input
                                 // layer's codes then fit one batch per wave)
-constexpr int kSmallNT = 1; // small-M kernel: 16-row tiles per wave (more cut the activations' L2
-                            // re-reads but leave too few blocks for layers of 4096 rows)
+// small-M kernel: layers with at least this many rows take two 16-row tiles per wave (each
+// activation fragment then feeds both, halving the activation loads, whose scattered cache lines
+// limit the kernel at 16 tokens); smaller layers take one, which keeps at least 256 blocks
+constexpr int kSmallWideRows = 8192;
 constexpr int kBigTokens = 128;    // large-M kernel: tokens per block (8 tiles of 16)
 // many-token kernel: NJ tiles of 16 output rows per wave (4 for prefill; 1 for a few hundred tokens,
 // where 4 would leave too few blocks to fill the chip)
@@ -84,21 +86,20 @@ __device__ __forceinline__ void group_params(uint32_t step_bits, uint32_t zbyte,
   nzs = -(float)z * s;  // exact: 4-bit integer times an 11-bit mantissa
 }
 
-// Few tokens (decode): a block computes 16 tokens x (16 kSmallNT) output rows; its eight waves take
+// Few tokens (decode): a block computes 16 tokens x (16 NT) output rows; its eight waves take
 // eight contiguous ranges of the groups and their partial products are added in wave order. The
 // weights, read once per 16 tokens, dominate the HBM traffic; each activation fragment is used for
-// kSmallNT row tiles, which divides the activations' re-reads from L2. Loads are unconditional
+// NT row tiles, which divides the activations' re-reads from L2. Loads are unconditional
 // (rows and tokens past the end read the last valid one, whose results are never stored) so that a
 // batch's loads all go out back to back; the codes of the next batch are in flight while the
 // current one is multiplied.
-template <int KIND, typename OutT>
+template <int KIND, typename OutT, int NT>
 __global__ __launch_bounds__(64 * kSmallWaves) void w4a16_small_kernel(const uint16_t* __restrict__ x, int64_t ld_x,
                                                               const uint8_t* __restrict__ codes,
                                                               const uint16_t* __restrict__ steps,
                                                               const uint8_t* __restrict__ zeros, int n_tokens,
                                                               int d_in, int d_out, OutT* __restrict__ y,
                                                               int64_t ld_y) {
-  constexpr int NT = kSmallNT;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, kq = lane >> 4;
@@ -803,10 +804,14 @@ hipError_t launch_kind(const void* x, int64_t ld_x, const uint8_t* codes, const 
     const unsigned blocks = (unsigned)((d_out + kGemvWaves * rpw - 1) / (kGemvWaves * rpw));
     hipLaunchKernelGGL((w4a16_gemv_kernel<KIND, OutT>), dim3(blocks), dim3(64 * kGemvWaves), W * 4096, st, xp, codes,
                        steps, zeros, d_in, d_out, rpw, yp);
+  } else if (d_out >= kSmallWideRows) {
+    const dim3 grid((unsigned)((d_out + 31) / 32), (unsigned)((n_tokens + 15) / 16));
+    hipLaunchKernelGGL((w4a16_small_kernel<KIND, OutT, 2>), grid, dim3(64 * kSmallWaves), 0, st, xp, ld_x, codes, steps,
+                       zeros, n_tokens, d_in, d_out, yp, ld_y);
   } else {
-    const dim3 grid((unsigned)((d_out + 16 * kSmallNT - 1) / (16 * kSmallNT)), (unsigned)((n_tokens + 15) / 16));
-    hipLaunchKernelGGL((w4a16_small_kernel<KIND, OutT>), grid, dim3(64 * kSmallWaves), 0, st, xp, ld_x, codes, steps, zeros,
-                       n_tokens, d_in, d_out, yp, ld_y);
+    const dim3 grid((unsigned)((d_out + 15) / 16), (unsigned)((n_tokens + 15) / 16));
+    hipLaunchKernelGGL((w4a16_small_kernel<KIND, OutT, 1>), grid, dim3(64 * kSmallWaves), 0, st, xp, ld_x, codes, steps,
+                       zeros, n_tokens, d_in, d_out, yp, ld_y);
   }
   return hipGetLastError();
 }

@@ -79,7 +79,8 @@ def _want_bits(yref, out, operand):
     (1, 128, 16), (1, 2176, 300), (1, 640, 1), (1, 1920, 8193), (1, 4224, 4097),  # one-token kernel: ragged
     (1, 32768, 40),                                                                # windows and row runs, LDS full
     (1, 32896, 24),                                                                # d_in past its LDS: few-token kernel
-    (5, 384, 300), (16, 1152, 272), (17, 256, 40), (32, 640, 33),                  # few-token kernel
+    (5, 384, 300), (16, 1152, 272), (17, 256, 40), (32, 640, 33),                  # few-token kernel,
+    (5, 256, 8209), (16, 384, 8192), (32, 128, 8200), (2, 640, 12289),            # two row tiles per wave
     (33, 384, 300), (128, 256, 256), (300, 1152, 520), (129, 128, 17),            # many-token kernel,
     (600, 384, 300), (513, 128, 520),                                              # 16 or 64 rows per wave
     (1024, 256, 300), (1300, 384, 520), (2049, 128, 17),                           # several token blocks
@@ -190,27 +191,28 @@ def test_full_size_7b_qkv(B, n_tokens):
     assert np.all(err <= tol)
 
 
-@pytest.mark.parametrize("operand", ["bf16", "f16"])
-def test_one_token_70b_down_proj_shape(B, operand):
-    # decode on the 70B down_proj's shape (8192 rows x 28672 inputs, 224 groups = 14 windows per row):
-    # every output against the accumulation bound on 96 sampled rows, all rows finite
-    rng = np.random.default_rng(11)
+@pytest.mark.parametrize("operand,n_tokens", [("bf16", 1), ("f16", 1), ("bf16", 16), ("f16", 7)])
+def test_decode_70b_down_proj_shape(B, operand, n_tokens):
+    # decode on the 70B down_proj's shape (8192 rows x 28672 inputs, 224 groups = 14 windows per row),
+    # one token (whole-row windows) and several (two row tiles per wave): every output against the
+    # accumulation bound on 96 sampled rows, all outputs finite
+    rng = np.random.default_rng(11 + n_tokens)
     d_in, d_out = 28672, 8192
     g = d_in // 128
     codes = rng.integers(0, 256, (d_out, d_in // 2), dtype=np.uint8)
     sb = (np.abs(rng.normal(0.002, 0.0005, (d_out, g))) + 1e-4).astype(np.float16).view(np.uint16)
     zp = rng.integers(0, 256, (d_out, g // 2)).astype(np.uint8)
-    x = rng.standard_normal((1, d_in)).astype(np.float32)
+    x = rng.standard_normal((n_tokens, d_in)).astype(np.float32)
     xt = _x_torch(x, operand)
-    print(f"[gpu w4a16] one token, 8192 x 28672, {operand}", flush=True)
+    print(f"[gpu w4a16] {n_tokens} tokens, 8192 x 28672, {operand}", flush=True)
     y = B.awq_w4a16_gemm(xt, *_dev(codes, sb, zp), out_dtype=torch.float32)
     torch.cuda.synchronize()
-    got = y.cpu().numpy().astype(np.float64)[0]
+    got = y.cpu().numpy().astype(np.float64)
     assert np.all(np.isfinite(got))
     rows = np.unique(np.concatenate([[0, 1, d_out - 1], rng.integers(0, d_out, 93)]))
     xq = xt.float().cpu().numpy().astype(np.float64)
-    yref = Q.w4a16_matmul(xq, codes[rows], sb[rows], zp[rows], operand)[0]
-    tol = d_in * 2.0 ** -24 * Q.abs_product_sums(xq, codes[rows], sb[rows], zp[rows], operand)[0]
-    err = np.abs(got[rows] - yref)
+    yref = Q.w4a16_matmul(xq, codes[rows], sb[rows], zp[rows], operand)
+    tol = d_in * 2.0 ** -24 * Q.abs_product_sums(xq, codes[rows], sb[rows], zp[rows], operand)
+    err = np.abs(got[:, rows] - yref)
     print(f"  max err / bound {(err / tol).max():.3e}", flush=True)
     assert np.all(err <= tol)
