@@ -86,14 +86,15 @@ __device__ __forceinline__ void group_params(uint32_t step_bits, uint32_t zbyte,
   nzs = -(float)z * s;  // exact: 4-bit integer times an 11-bit mantissa
 }
 
-// Few tokens (decode): a block computes 16 tokens x (16 NT) output rows; its eight waves take
-// eight contiguous ranges of the groups and their partial products are added in wave order. The
-// weights, read once per 16 tokens, dominate the HBM traffic; each activation fragment is used for
-// NT row tiles, which divides the activations' re-reads from L2. Loads are unconditional
+// Few tokens (decode): a block computes 16 MT tokens x 16 NT output rows (MT = 2 for 17-32 tokens,
+// so that each dequantized weight fragment feeds both token tiles and the weights are read once);
+// its eight waves take eight contiguous ranges of the groups and their partial products are added
+// in wave order. The weights dominate the HBM traffic; each activation fragment is used for NT row
+// tiles, which divides the activations' re-reads from L2. Loads are unconditional
 // (rows and tokens past the end read the last valid one, whose results are never stored) so that a
 // batch's loads all go out back to back; the codes of the next batch are in flight while the
 // current one is multiplied.
-template <int KIND, typename OutT, int NT>
+template <int KIND, typename OutT, int NT, int MT>
 __global__ __launch_bounds__(64 * kSmallWaves) void w4a16_small_kernel(const uint16_t* __restrict__ x, int64_t ld_x,
                                                               const uint8_t* __restrict__ codes,
                                                               const uint16_t* __restrict__ steps,
@@ -103,7 +104,6 @@ __global__ __launch_bounds__(64 * kSmallWaves) void w4a16_small_kernel(const uin
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, kq = lane >> 4;
-  const int tok = min(blockIdx.y * 16 + n, n_tokens - 1);
   const int G = d_in / kGroup, GZ = (G + 1) / 2;
   const int g_begin = (G * wave) / kSmallWaves, g_end = (G * (wave + 1)) / kSmallWaves;
   const uint8_t* crow[NT];
@@ -116,10 +116,15 @@ __global__ __launch_bounds__(64 * kSmallWaves) void w4a16_small_kernel(const uin
     srow[j] = steps + (int64_t)row * G;
     zrow[j] = zeros + (int64_t)row * GZ;
   }
-  const uint16_t* xrow = x + (int64_t)tok * ld_x + kq * 32;
-  f32x4 acc[NT];
+  const uint16_t* xrow[MT];
 #pragma unroll
-  for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int m = 0; m < MT; ++m)
+    xrow[m] = x + (int64_t)min(blockIdx.y * (16 * MT) + 16 * m + n, n_tokens - 1) * ld_x + kq * 32;
+  f32x4 acc[MT][NT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   uint4 cw[kBatch][NT];
   uint32_t sr[kBatch][NT], zr[kBatch][NT];
@@ -150,12 +155,14 @@ __global__ __launch_bounds__(64 * kSmallWaves) void w4a16_small_kernel(const uin
 #pragma unroll
     for (int h = 0; h < kBatch; h += kXSub) {
       if (gb + h < g_end) {  // wave-uniform
-        uint4 a[kXSub][4];
+        uint4 a[MT][kXSub][4];
 #pragma unroll
         for (int i = 0; i < kXSub; ++i) {
           const int g = min(gb + h + i, g_end - 1);
 #pragma unroll
-          for (int t = 0; t < 4; ++t) a[i][t] = *reinterpret_cast<const uint4*>(xrow + g * kGroup + t * 8);
+          for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) a[m][i][t] = *reinterpret_cast<const uint4*>(xrow[m] + g * kGroup + t * 8);
         }
 #pragma unroll
         for (int i = 0; i < kXSub; ++i) {
@@ -164,29 +171,34 @@ __global__ __launch_bounds__(64 * kSmallWaves) void w4a16_small_kernel(const uin
             for (int j = 0; j < NT; ++j) {
               const uint32_t wt[4] = {cur[h + i][j].x, cur[h + i][j].y, cur[h + i][j].z, cur[h + i][j].w};
 #pragma unroll
-              for (int t = 0; t < 4; ++t)
-                acc[j] = mma<KIND>(a[i][t], dequant8<KIND>(wt[t], st[h + i][j], nzs[h + i][j]), acc[j]);
+              for (int t = 0; t < 4; ++t) {
+                const uint4 b = dequant8<KIND>(wt[t], st[h + i][j], nzs[h + i][j]);
+#pragma unroll
+                for (int m = 0; m < MT; ++m) acc[m][j] = mma<KIND>(a[m][i][t], b, acc[m][j]);
+              }
             }
           }
         }
       }
     }
   }
-  __shared__ f32x4 red[kSmallWaves][NT][64];
+  __shared__ f32x4 red[kSmallWaves][MT * NT][64];
 #pragma unroll
-  for (int j = 0; j < NT; ++j) red[wave][j][lane] = acc[j];
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) red[wave][m * NT + j][lane] = acc[m][j];
   __syncthreads();
-  if (wave < NT) {
-    const int j = wave;
-    f32x4 s = red[0][j][lane];
+  if (wave < MT * NT) {  // wave m NT + j adds the partials of token tile m, row tile j
+    const int m = wave / NT, j = wave % NT;
+    f32x4 s = red[0][wave][lane];
 #pragma unroll
-    for (int w = 1; w < kSmallWaves; ++w) s += red[w][j][lane];
+    for (int w = 1; w < kSmallWaves; ++w) s += red[w][wave][lane];
     // C layout of the 16x16 result: lane l holds rows 4 (l / 16) .. +3 of column l mod 16
     const int orow = blockIdx.x * (16 * NT) + 16 * j + (lane & 15);
     const float sv[4] = {s.x, s.y, s.z, s.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int t2 = blockIdx.y * 16 + 4 * (lane >> 4) + i;
+      const int t2 = blockIdx.y * (16 * MT) + 16 * m + 4 * (lane >> 4) + i;
       if (orow < d_out && t2 < n_tokens) y[(int64_t)t2 * ld_y + orow] = to_out<OutT>(sv[i], KIND);
     }
   }
@@ -804,14 +816,22 @@ hipError_t launch_kind(const void* x, int64_t ld_x, const uint8_t* codes, const 
     const unsigned blocks = (unsigned)((d_out + kGemvWaves * rpw - 1) / (kGemvWaves * rpw));
     hipLaunchKernelGGL((w4a16_gemv_kernel<KIND, OutT>), dim3(blocks), dim3(64 * kGemvWaves), W * 4096, st, xp, codes,
                        steps, zeros, d_in, d_out, rpw, yp);
-  } else if (d_out >= kSmallWideRows) {
-    const dim3 grid((unsigned)((d_out + 31) / 32), (unsigned)((n_tokens + 15) / 16));
-    hipLaunchKernelGGL((w4a16_small_kernel<KIND, OutT, 2>), grid, dim3(64 * kSmallWaves), 0, st, xp, ld_x, codes, steps,
-                       zeros, n_tokens, d_in, d_out, yp, ld_y);
   } else {
-    const dim3 grid((unsigned)((d_out + 15) / 16), (unsigned)((n_tokens + 15) / 16));
-    hipLaunchKernelGGL((w4a16_small_kernel<KIND, OutT, 1>), grid, dim3(64 * kSmallWaves), 0, st, xp, ld_x, codes, steps,
-                       zeros, n_tokens, d_in, d_out, yp, ld_y);
+    // 17-32 tokens: both 16-token tiles in one block, so each weight fragment is dequantized once
+    const bool wide = d_out >= kSmallWideRows, two = n_tokens > 16;
+    const dim3 grid((unsigned)((d_out + (wide ? 31 : 15)) / (wide ? 32 : 16)), 1);
+    if (wide && two)
+      hipLaunchKernelGGL((w4a16_small_kernel<KIND, OutT, 2, 2>), grid, dim3(64 * kSmallWaves), 0, st, xp, ld_x, codes,
+                         steps, zeros, n_tokens, d_in, d_out, yp, ld_y);
+    else if (wide)
+      hipLaunchKernelGGL((w4a16_small_kernel<KIND, OutT, 2, 1>), grid, dim3(64 * kSmallWaves), 0, st, xp, ld_x, codes,
+                         steps, zeros, n_tokens, d_in, d_out, yp, ld_y);
+    else if (two)
+      hipLaunchKernelGGL((w4a16_small_kernel<KIND, OutT, 1, 2>), grid, dim3(64 * kSmallWaves), 0, st, xp, ld_x, codes,
+                         steps, zeros, n_tokens, d_in, d_out, yp, ld_y);
+    else
+      hipLaunchKernelGGL((w4a16_small_kernel<KIND, OutT, 1, 1>), grid, dim3(64 * kSmallWaves), 0, st, xp, ld_x, codes,
+                         steps, zeros, n_tokens, d_in, d_out, yp, ld_y);
   }
   return hipGetLastError();
 }

@@ -80,7 +80,8 @@ def _want_bits(yref, out, operand):
     (1, 32768, 40),                                                                # windows and row runs, LDS full
     (1, 32896, 24),                                                                # d_in past its LDS: few-token kernel
     (5, 384, 300), (16, 1152, 272), (17, 256, 40), (32, 640, 33),                  # few-token kernel,
-    (5, 256, 8209), (16, 384, 8192), (32, 128, 8200), (2, 640, 12289),            # two row tiles per wave
+    (5, 256, 8209), (16, 384, 8192), (32, 128, 8200), (2, 640, 12289),            # two row tiles per wave,
+    (20, 256, 8209),                                                               # and two token tiles
     (33, 384, 300), (128, 256, 256), (300, 1152, 520), (129, 128, 17),            # many-token kernel,
     (600, 384, 300), (513, 128, 520),                                              # 16 or 64 rows per wave
     (1024, 256, 300), (1300, 384, 520), (2049, 128, 17),                           # several token blocks
@@ -191,11 +192,11 @@ def test_full_size_7b_qkv(B, n_tokens):
     assert np.all(err <= tol)
 
 
-@pytest.mark.parametrize("operand,n_tokens", [("bf16", 1), ("f16", 1), ("bf16", 16), ("f16", 7)])
+@pytest.mark.parametrize("operand,n_tokens", [("bf16", 1), ("f16", 1), ("bf16", 16), ("f16", 7), ("bf16", 27)])
 def test_decode_70b_down_proj_shape(B, operand, n_tokens):
     # decode on the 70B down_proj's shape (8192 rows x 28672 inputs, 224 groups = 14 windows per row),
-    # one token (whole-row windows) and several (two row tiles per wave): every output against the
-    # accumulation bound on 96 sampled rows, all outputs finite
+    # one token (whole-row windows) and several (two row tiles per wave; 27 tokens: two token tiles per
+    # block): every output against the accumulation bound on 96 sampled rows, all outputs finite
     rng = np.random.default_rng(11 + n_tokens)
     d_in, d_out = 28672, 8192
     g = d_in // 128
