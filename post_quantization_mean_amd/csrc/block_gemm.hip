@@ -225,10 +225,11 @@ void mlp_hidden_kernel(const uint16_t* __restrict__ x, int64_t ld_x, const uint1
                              acc[i][2 + jj][4 * q + 3]};
             *reinterpret_cast<f32x4*>(give + (((i * 2 + jj) * 4 + q) * 64 + lane) * 4) = w;
           }
-      __syncthreads();
       const bool is_gate = wn == 0;
-      // the reference values of accumulator group n + 1 are in flight while group n is computed
-      float gv[2][16], uv[2][16];
+      // the reference values of four accumulator groups are in flight (one or two exposed the loads'
+      // latency group by group); the first four go out before the exchange's barrier
+      constexpr int D = 4;
+      float gv[D][16], uv[D][16];
       auto load_ref = [&](int n, int b) {
         const int i = n >> 1, jj = n & 1;
         const int64_t fc = min(f_w + 32 * (jj + 2 * wn) + fr, fmax);
@@ -239,16 +240,17 @@ void mlp_hidden_kernel(const uint16_t* __restrict__ x, int64_t ld_x, const uint1
           uv[b][e] = u_io[t * d_ff + fc];
         }
       };
-      load_ref(0, 0);
+#pragma unroll
+      for (int n = 0; n < D; ++n) load_ref(n, n);
+      __syncthreads();
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
           const int n = i * 2 + jj;
-          if (n + 1 < FM * 2) load_ref(n + 1, (n + 1) & 1);
           const int64_t f = f_w + 32 * (jj + 2 * wn) + fr;
-          const float (&gn)[16] = gv[n & 1];
-          const float (&un)[16] = uv[n & 1];
+          const float (&gn)[16] = gv[n % D];
+          const float (&un)[16] = uv[n % D];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const f32x4 oth = *reinterpret_cast<const f32x4*>(take + ((n * 4 + q) * 64 + lane) * 4);
@@ -263,6 +265,7 @@ void mlp_hidden_kernel(const uint16_t* __restrict__ x, int64_t ld_x, const uint1
               if (t < n_tokens && f < d_ff) dh[t * d_ff + f] = (uint16_t)(pack_bf16x2(d, 0.f) & 0xFFFFu);
             }
           }
+          if (n + D < FM * 2) load_ref(n + D, n % D);
           __builtin_amdgcn_sched_barrier(0);
         }
     }
