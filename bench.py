@@ -428,10 +428,12 @@ def main() -> int:
             e1.synchronize()
             ts.append(e0.elapsed_time(e1))
         g_ref, u_ref = B.awq_mlp_hidden_ref(x, wg_b, wu_b)
-        dwg = torch.zeros_like(wg_b)
+        # a candidate pass reads two distinct delta matrices (gate and up), as in the search
+        dwg = (torch.randn((d_ff, 4096), generator=gen_b, device=dev) * 0.001).to(torch.bfloat16)
+        dwu = (torch.randn((d_ff, 4096), generator=gen_b, device=dev) * 0.001).to(torch.bfloat16)
         dh_b = torch.empty((wl.n_tokens, d_ff), dtype=torch.bfloat16, device=dev)
         t_ref = isolated(lambda: B.awq_mlp_hidden_ref(x, wg_b, wu_b, g_ref, u_ref))
-        t_dh = isolated(lambda: B.awq_mlp_hidden_delta(x, dwg, dwg, g_ref, u_ref, B.AWQ_ACT_SILU, dh_b))
+        t_dh = isolated(lambda: B.awq_mlp_hidden_delta(x, dwg, dwu, g_ref, u_ref, B.AWQ_ACT_SILU, dh_b))
         sse_b = torch.empty((1, B.awq_error_tiles(wl.n_tokens, d_model)), dtype=torch.float64, device=dev)
         t_dn = isolated(lambda: B.awq_error_sse(dh_b, wd_b.view(1, d_model, d_ff), sse_b))
         f_gu = 2.0 * 2 * wl.n_tokens * 4096 * d_ff
@@ -443,7 +445,7 @@ def main() -> int:
                "ms": {"mlp_hidden_ref": t_ref, "mlp_hidden_delta": t_dh, "error_sse_down": t_dn},
                "tflops": {"mlp_hidden_ref": f_gu / (t_ref * 1e-3) / 1e12, "mlp_hidden_delta": f_gu / (t_dh * 1e-3) / 1e12,
                           "error_sse_down": f_dn / (t_dn * 1e-3) / 1e12}}
-        del ws_b, g_ref, u_ref, dh_b, wg_b, wu_b, wd_b, dwg
+        del ws_b, g_ref, u_ref, dh_b, wg_b, wu_b, wd_b, dwg, dwu
     del flush
     var_gbps = {"weight_mean": (wl.d_out * wl.d_in * esz + wl.d_in * 8) / (var_ms["weight_mean"] * 1e-3) / 1e9,
                 "quant_delta_int4_row": q_bytes / (var_ms["quant_delta_int4_row"] * 1e-3) / 1e9,
