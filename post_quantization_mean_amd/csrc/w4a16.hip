@@ -260,8 +260,10 @@ __global__ __launch_bounds__(64 * kGemvWaves) void w4a16_gemv_kernel(const uint1
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = d_in / kGroup, GZ = (G + 1) / 2, W = (G + 15) / 16;
-  const int r0 = (blockIdx.x * kGemvWaves + wave) * rows_per_wave;
-  const int r1 = min(r0 + rows_per_wave, d_out);
+  // 64-bit until clamped: near the largest d_out the last wave's row range ends past 2^31
+  const int64_t r0l = ((int64_t)blockIdx.x * kGemvWaves + wave) * rows_per_wave;
+  const int r0 = (int)min(r0l, (int64_t)d_out);
+  const int r1 = (int)min(r0l + rows_per_wave, (int64_t)d_out);
   const int n_items = r1 > r0 ? (r1 - r0) * W : 0;
   const int lg = lane >> 2;  // the lane's group within a window
 
@@ -812,8 +814,9 @@ hipError_t launch_kind(const void* x, int64_t ld_x, const uint8_t* codes, const 
   } else if (n_tokens == 1 && d_in <= kGemvMaxIn) {
     // about kGemvBlocks blocks of kGemvWaves waves, each wave a run of whole rows
     const int W = (d_in / kGroup + 15) / 16;
-    const int rpw = (d_out + kGemvWaves * kGemvBlocks - 1) / (kGemvWaves * kGemvBlocks);
-    const unsigned blocks = (unsigned)((d_out + kGemvWaves * rpw - 1) / (kGemvWaves * rpw));
+    const int64_t per = (int64_t)kGemvWaves * kGemvBlocks;
+    const int rpw = (int)(((int64_t)d_out + per - 1) / per);
+    const unsigned blocks = (unsigned)(((int64_t)d_out + (int64_t)kGemvWaves * rpw - 1) / ((int64_t)kGemvWaves * rpw));
     hipLaunchKernelGGL((w4a16_gemv_kernel<KIND, OutT>), dim3(blocks), dim3(64 * kGemvWaves), W * 4096, st, xp, codes,
                        steps, zeros, d_in, d_out, rpw, yp);
   } else {

@@ -265,3 +265,23 @@ def test_one_token_dequant_identity():
             v1 = np.float32((1024 + 16 * q) * np.float64(np.float32(s * 0.0625)) + np.float64(c16))
             want = (q - z) * s
             assert np.array_equal(v0.astype(np.float64), want) and np.array_equal(v1.astype(np.float64), want)
+
+
+def test_one_token_row_ranges_at_the_largest_d_out():
+    # the ABI admits d_out up to 2^31 - 257; there the last wave's row range would end at 2^31, so the
+    # kernel forms it in 64 bits and clamps to d_out: every wave's [r0, r1) stays inside [0, d_out],
+    # the ranges tile the rows, and the host's grid arithmetic needs 64 bits as well
+    d_out = 0x7FFFFFFF - 256
+    per = GEMV_WAVES * GEMV_BLOCKS
+    assert d_out + per - 1 > 2**31 - 1  # the host's rounding up overflows 32 bits
+    W, rpw, blocks = _gemv_launch(128, d_out)
+    assert blocks * GEMV_WAVES * rpw >= d_out and (blocks - 1) * GEMV_WAVES * rpw < d_out
+    ends = []
+    for wv in range(blocks * GEMV_WAVES):
+        r0l = wv * rpw
+        r0, r1 = min(r0l, d_out), min(r0l + rpw, d_out)
+        assert 0 <= r0 <= r1 <= d_out <= 2**31 - 1
+        ends.append((r0, r1))
+    assert max(wv * rpw + rpw for wv in range(blocks * GEMV_WAVES)) > 2**31 - 1  # why 64 bits
+    assert ends[0][0] == 0 and ends[-1][1] == d_out
+    assert all(a[1] == b[0] for a, b in zip(ends, ends[1:]))
