@@ -217,3 +217,28 @@ def test_decode_70b_down_proj_shape(B, operand, n_tokens):
     err = np.abs(got[:, rows] - yref)
     print(f"  max err / bound {(err / tol).max():.3e}", flush=True)
     assert np.all(err <= tol)
+
+
+@pytest.mark.parametrize("n_tokens,d_in,d_out", [(1, 640, 300), (5, 384, 8200), (1100, 256, 300)])
+def test_nonfinite_activations(B, n_tokens, d_in, d_out):
+    # a NaN, +inf and -inf at one input each of three tokens (one token: the -inf alone): those
+    # tokens' outputs are NaN or +-inf
+    # (inf times a zero weight is NaN, otherwise the one infinite term decides the sign), the same
+    # pattern as the float64 oracle whatever the order of the additions; the other tokens are finite
+    rng = np.random.default_rng(n_tokens + d_out)
+    x, codes, sb, zp = _exact_case(rng, n_tokens, d_in, d_out)
+    bad = {0: np.nan, n_tokens // 2: np.inf, n_tokens - 1: -np.inf}
+    for t, v in bad.items():
+        x[t, 7 + 3 * t % (d_in - 8)] = v
+    xt = _x_torch(x, "bf16")
+    print(f"[gpu w4a16] non-finite activations, tokens={n_tokens} d_in={d_in} d_out={d_out}", flush=True)
+    y = B.awq_w4a16_gemm(xt, *_dev(codes, sb, zp), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    got = y.cpu().numpy().astype(np.float64)
+    with np.errstate(invalid="ignore"):
+        want = Q.w4a16_matmul(x, codes, sb, zp, "bf16")
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    assert np.array_equal(np.isinf(got) & (got > 0), np.isinf(want) & (want > 0))
+    assert np.array_equal(np.isinf(got) & (got < 0), np.isinf(want) & (want < 0))
+    fin = np.isfinite(want)
+    assert np.array_equal(got[fin], want[fin])  # exact-arithmetic inputs elsewhere
