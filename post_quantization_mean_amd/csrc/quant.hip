@@ -43,7 +43,7 @@ constexpr int kThreads = 256;
 constexpr int kRows = 4;               // rows per wave (per lane)
 constexpr int kRowsPerBlock = 4 * kRows;
 #ifndef AWQ_PACK_ROWS
-#define AWQ_PACK_ROWS 2
+#define AWQ_PACK_ROWS 1
 #endif
 #ifndef AWQ_PACK_NT
 #define AWQ_PACK_NT 1  // the pack reads W once: non-temporal loads (measured 6-9 % faster on large layers)
@@ -54,13 +54,15 @@ constexpr int kRowsPerBlock = 4 * kRows;
 #ifndef AWQ_PACK_DEPTH
 #define AWQ_PACK_DEPTH 1
 #endif
-constexpr int kPackRows = AWQ_PACK_ROWS;    // pack: rows per wave per row block
-constexpr int kPackRowsPerBlock = 4 * kPackRows;
+constexpr int kPackRows = AWQ_PACK_ROWS;    // pack: rows per row block (the same rows for every wave)
 constexpr int kPackDepth = AWQ_PACK_DEPTH;  // pack: row blocks in flight ahead of the current one
 
-// Layout of both kernels: 16 channels per lane, 8 lanes per group, 1024 channels per block
+// Layout of both kernels: 16 channels per lane, 8 lanes per group, 1024 channels per wave; a
+// quant_delta block's four waves take different rows of one 1024-channel slice, a pack block's
+// four waves adjacent slices of the same rows
 constexpr int kChans = 16;
 constexpr int kChansPerBlock = 64 * kChans;
+constexpr int kPackChansPerBlock = 4 * kChansPerBlock;
 
 // The float32 fast path. With y32 = fl(w * fl(s)) (relative error 2^-23), the group's
 // min/max taken on y32, step32 = fl(fl(max - min) * fl(1/15)) (relative error 2^-22 A/R +
@@ -472,10 +474,13 @@ __device__ __forceinline__ void exact_pack_group(float wa, float wb, const doubl
   }
 }
 
-// a6: codes of W * s packed two per byte, with each group's step and zero point. Same layout and
-// float32 fast path as quant_delta (one scale vector, so no candidate loop): q = round(y / step)
+// a6: codes of W * s packed two per byte, with each group's step and zero point. The lane layout
+// and float32 fast path of quant_delta (one scale vector, so no candidate loop): q = round(y / step)
 // + zero, proved equal to the float64 definition by the residual and zero-point checks; flagged
-// groups are redone by the whole wave in float64.
+// groups are redone by the whole wave in float64. A block's four waves take four adjacent
+// 1024-channel slices of the same row, so each row block reads 8 KiB of one row and writes 2 KiB of
+// its codes and 128 bytes each of its steps and zero points (for bf16 weights: 12 % faster on the
+// 70B layers than four waves on four rows of one slice, with the codes' non-temporal stores).
 template <typename T>
 __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(WParts w, int64_t d_in, int64_t d_out,
                                                                  const double* __restrict__ s_in,
@@ -487,18 +492,21 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(WParts w, int64
   __shared__ uint4 slot[4][RawRow<T, E>::NV * 64];                 // per wave: one row slice
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: row math stays scalar
-  const int64_t cb = (int64_t)blockIdx.x * kChansPerBlock;
+  // this wave's 1024-channel slice (past d_in in the last column block when d_in is not a multiple
+  // of 4096: such a wave loads nothing and stores nothing)
+  const int64_t cb = (int64_t)blockIdx.x * kPackChansPerBlock + (int64_t)wave * kChansPerBlock;
   const int64_t c0 = cb + lane * E;
   const bool col_ok = c0 < d_in;
   const int64_t n_groups = d_in / kGroup;
-  const int64_t n_rb = (d_out + kPackRowsPerBlock - 1) / kPackRowsPerBlock;
+  const int64_t n_rb = (d_out + kPackRows - 1) / kPackRows;
   // Row blocks blockIdx.y, blockIdx.y + gridDim.y, ...; the weights of the next kPackDepth row
   // blocks are in flight while the current one is quantized.
-  const int valid16 = (int)((std::min<int64_t>(d_in - cb, kChansPerBlock) * (int64_t)sizeof(T)) / 16);
+  const int valid16 =
+      (int)((std::max<int64_t>(0, std::min<int64_t>(d_in - cb, kChansPerBlock)) * (int64_t)sizeof(T)) / 16);
   auto load_rows = [&](RawRow<T, E>(&dst)[kPackRows], int64_t rb) {
 #pragma unroll
     for (int i = 0; i < kPackRows; ++i) {
-      const int64_t o = rb * kPackRowsPerBlock + wave * kPackRows + i;
+      const int64_t o = rb * kPackRows + i;
       if (o < d_out)
         dst[i].load(row_ptr<T>(w, o, d_in) + cb, valid16, lane);
       else
@@ -521,7 +529,7 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(WParts w, int64
   }
 
   for (int64_t rb = blockIdx.y; rb < n_rb; rb += gridDim.y) {
-    const int64_t row0 = rb * kPackRowsPerBlock + wave * kPackRows;
+    const int64_t row0 = rb * kPackRows;
     RowE<T, E> wv[kPackRows];
 #pragma unroll
     for (int i = 0; i < kPackRows; ++i) raw[0][i].regroup(slot[wave], lane, wv[i]);
@@ -553,11 +561,11 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(WParts w, int64
       const bool ok = fg.ok && em <= kHalfGuard32;
       bad[i] = group_mask(__ballot(live && !ok));
       if (live && !((bad[i] >> lane) & 1)) {
-        uint2 v;
-        v.x = ev[0] | (od[0] << 4);  // q in [0, 15] when the checks pass
-        v.y = ev[1] | (od[1] << 4);
-        // row bases are wave-uniform (scalar registers), the lane offsets 32-bit
-        *reinterpret_cast<uint2*>(codes + (o * (d_in / 2) + cb / 2) + (uint32_t)(lane * (E / 2))) = v;
+        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 v = {ev[0] | (od[0] << 4), ev[1] | (od[1] << 4)};  // q in [0, 15] when the checks pass
+        // row bases are wave-uniform (scalar registers), the lane offsets 32-bit; the block's four
+        // waves write 2 KiB of one row's codes, non-temporal (written once, not read again here)
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(codes + (o * (d_in / 2) + cb / 2) + (uint32_t)(lane * (E / 2))));
         if ((lane & 7) == 0) {
           const int64_t gb = o * n_groups + cb / kGroup;
           qscales[gb + (uint32_t)(lane >> 3)] = fg.step;
@@ -624,8 +632,8 @@ hipError_t launch_quantize_pack(const WParts& w, int dtype, int64_t d_in, const 
   const int64_t d_out = w.row_begin[w.n];
   // four resident blocks per compute unit (4 waves per SIMD at the kernel's register use), each
   // looping over row blocks
-  const int64_t col_blocks = (d_in + kChansPerBlock - 1) / kChansPerBlock;
-  const int64_t row_blocks = (d_out + kPackRowsPerBlock - 1) / kPackRowsPerBlock;
+  const int64_t col_blocks = (d_in + kPackChansPerBlock - 1) / kPackChansPerBlock;
+  const int64_t row_blocks = (d_out + kPackRows - 1) / kPackRows;
   const int64_t ry = std::max<int64_t>(1, std::min<int64_t>(row_blocks, AWQ_PACK_GRID / col_blocks));
   dim3 grid((unsigned)col_blocks, (unsigned)ry);
   if (dtype == 1)
