@@ -54,15 +54,14 @@ constexpr int kRowsPerBlock = 4 * kRows;
 #ifndef AWQ_PACK_DEPTH
 #define AWQ_PACK_DEPTH 1
 #endif
-constexpr int kPackRows = AWQ_PACK_ROWS;    // pack: rows per row block (the same rows for every wave)
+constexpr int kPackRows = AWQ_PACK_ROWS;    // pack: rows per wave per row block
 constexpr int kPackDepth = AWQ_PACK_DEPTH;  // pack: row blocks in flight ahead of the current one
 
 // Layout of both kernels: 16 channels per lane, 8 lanes per group, 1024 channels per wave; a
 // quant_delta block's four waves take different rows of one 1024-channel slice, a pack block's
-// four waves adjacent slices of the same rows
+// four waves up to four adjacent slices of the same rows
 constexpr int kChans = 16;
 constexpr int kChansPerBlock = 64 * kChans;
-constexpr int kPackChansPerBlock = 4 * kChansPerBlock;
 
 // The float32 fast path. With y32 = fl(w * fl(s)) (relative error 2^-23), the group's
 // min/max taken on y32, step32 = fl(fl(max - min) * fl(1/15)) (relative error 2^-22 A/R +
@@ -478,10 +477,12 @@ __device__ __forceinline__ void exact_pack_group(float wa, float wb, const doubl
 // and float32 fast path of quant_delta (one scale vector, so no candidate loop): q = round(y / step)
 // + zero, proved equal to the float64 definition by the residual and zero-point checks; flagged
 // groups are redone by the whole wave in float64. A block's four waves take four adjacent
-// 1024-channel slices of the same row, so each row block reads 8 KiB of one row and writes 2 KiB of
-// its codes and 128 bytes each of its steps and zero points (for bf16 weights: 12 % faster on the
-// 70B layers than four waves on four rows of one slice, with the codes' non-temporal stores).
-template <typename T>
+// 1024-channel slices of the same row (spb = 4), so each row block reads 8 KiB of one row and
+// writes 2 KiB of its codes and 128 bytes each of its steps and zero points (for bf16 weights: 12 %
+// faster on the 70B layers than four waves on four rows of one slice, with the codes' non-temporal
+// stores). When the row's slice count is not a multiple of 4, spb = 2 or 1 slices per block with
+// 2 or 4 rows per row block, so that no wave is idle.
+template <typename T, int SPB>
 __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(WParts w, int64_t d_in, int64_t d_out,
                                                                  const double* __restrict__ s_in,
                                                                  uint8_t* __restrict__ codes,
@@ -492,13 +493,17 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(WParts w, int64
   __shared__ uint4 slot[4][RawRow<T, E>::NV * 64];                 // per wave: one row slice
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: row math stays scalar
-  // this wave's 1024-channel slice (past d_in in the last column block when d_in is not a multiple
-  // of 4096: such a wave loads nothing and stores nothing)
-  const int64_t cb = (int64_t)blockIdx.x * kPackChansPerBlock + (int64_t)wave * kChansPerBlock;
+  // this wave's 1024-channel slice (wave % SPB of the block's SPB slices; SPB divides the row's
+  // slice count, so a slice past d_in occurs only in a single-slice row narrower than 1024) and its
+  // rows (wave / SPB of the row block's 4 / SPB row sets); compile-time SPB keeps this arithmetic
+  // scalar
+  const int sw = SPB == 4 ? wave : wave % SPB, rw = SPB == 4 ? 0 : wave / SPB;  // wave < 4
+  constexpr int rows_rb = (4 / SPB) * kPackRows;
+  const int64_t cb = ((int64_t)blockIdx.x * SPB + sw) * kChansPerBlock;
   const int64_t c0 = cb + lane * E;
   const bool col_ok = c0 < d_in;
   const int64_t n_groups = d_in / kGroup;
-  const int64_t n_rb = (d_out + kPackRows - 1) / kPackRows;
+  const int64_t n_rb = (d_out + rows_rb - 1) / rows_rb;
   // Row blocks blockIdx.y, blockIdx.y + gridDim.y, ...; the weights of the next kPackDepth row
   // blocks are in flight while the current one is quantized.
   const int valid16 =
@@ -506,7 +511,7 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(WParts w, int64
   auto load_rows = [&](RawRow<T, E>(&dst)[kPackRows], int64_t rb) {
 #pragma unroll
     for (int i = 0; i < kPackRows; ++i) {
-      const int64_t o = rb * kPackRows + i;
+      const int64_t o = rb * rows_rb + rw * kPackRows + i;
       if (o < d_out)
         dst[i].load(row_ptr<T>(w, o, d_in) + cb, valid16, lane);
       else
@@ -529,7 +534,7 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(WParts w, int64
   }
 
   for (int64_t rb = blockIdx.y; rb < n_rb; rb += gridDim.y) {
-    const int64_t row0 = rb * kPackRows;
+    const int64_t row0 = rb * rows_rb + rw * kPackRows;
     RowE<T, E> wv[kPackRows];
 #pragma unroll
     for (int i = 0; i < kPackRows; ++i) raw[0][i].regroup(slot[wave], lane, wv[i]);
@@ -632,16 +637,21 @@ hipError_t launch_quantize_pack(const WParts& w, int dtype, int64_t d_in, const 
   const int64_t d_out = w.row_begin[w.n];
   // four resident blocks per compute unit (4 waves per SIMD at the kernel's register use), each
   // looping over row blocks
-  const int64_t col_blocks = (d_in + kPackChansPerBlock - 1) / kPackChansPerBlock;
-  const int64_t row_blocks = (d_out + kPackRows - 1) / kPackRows;
+  const int64_t slices = (d_in + kChansPerBlock - 1) / kChansPerBlock;
+  const int spb = slices % 4 == 0 ? 4 : (slices % 2 == 0 ? 2 : 1);  // slices per block
+  const int64_t col_blocks = slices / spb;
+  const int64_t row_blocks = (d_out + (4 / spb) * kPackRows - 1) / ((4 / spb) * kPackRows);
   const int64_t ry = std::max<int64_t>(1, std::min<int64_t>(row_blocks, AWQ_PACK_GRID / col_blocks));
   dim3 grid((unsigned)col_blocks, (unsigned)ry);
+  auto launch = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, st, w, d_in, d_out, s, codes, qscales, zeros);
+  };
   if (dtype == 1)
-    hipLaunchKernelGGL(quantize_pack_kernel<uint16_t>, grid, dim3(kThreads), 0, st, w, d_in, d_out, s,
-                       codes, qscales, zeros);
+    launch(spb == 4 ? quantize_pack_kernel<uint16_t, 4>
+                    : (spb == 2 ? quantize_pack_kernel<uint16_t, 2> : quantize_pack_kernel<uint16_t, 1>));
   else
-    hipLaunchKernelGGL(quantize_pack_kernel<float>, grid, dim3(kThreads), 0, st, w, d_in, d_out, s,
-                       codes, qscales, zeros);
+    launch(spb == 4 ? quantize_pack_kernel<float, 4>
+                    : (spb == 2 ? quantize_pack_kernel<float, 2> : quantize_pack_kernel<float, 1>));
   return hipGetLastError();
 }
 
