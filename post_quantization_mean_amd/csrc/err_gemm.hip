@@ -35,7 +35,8 @@
 // delta_I G_IJ delta_J^T, and G_JI = G_IJ^T makes the (J, I) term equal to the (I, J) one, so the
 // form is sum_I (delta_I G_II delta_I^T + 2 sum_{J>I} delta_I G_IJ delta_J^T): row tile I runs K over
 // the blocks J >= I, about half the matrix work of the full K range, with G's fragments halved
-// while K is in block I and the tile's sum doubled. The tiles' lengths fall with I, so a compute
+// while K is in block I (or G stored with its diagonal blocks halved, PREHALVED) and the tile's sum
+// doubled. The tiles' lengths fall with I, so a compute
 // unit takes row tile I and then row tile R - 1 - I of the same column (R = ceil(d_in / 256) row
 // tiles): every pair has the same length, the 256 units stay in step, and their 16 x 16
 // super-blocks keep sharing operands in L2.
@@ -232,7 +233,7 @@ struct Epi {
 // Persistent: one workgroup per compute unit walks tiles G = blockIdx.x, + gridDim.x, ... The
 // next tile's first K stage is loaded into the free LDS buffer during the current tile's last K
 // step, so its load latency hides behind that step and the epilogue.
-template <typename T, int MODE = kSse>
+template <typename T, int MODE = kSse, bool PREHALVED = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void error_sse_kernel(const T* __restrict__ x, int64_t ld_x, const T* __restrict__ delta,
                       int64_t n_tokens, int64_t d_in, int64_t d_out, int tiles_m, int tiles_n,
@@ -293,7 +294,7 @@ void error_sse_kernel(const T* __restrict__ x, int64_t ld_x, const T* __restrict
   auto substep = [&](auto zc, uint32_t hf, uint4 (&use)[NR], uint4 (&nxt)[NR], const char* src, int sl, bool reads,
                      const TileOps& lt, uint32_t fstage, int kbyte, int l0, int l1) {
     constexpr bool ZC = decltype(zc)::value;
-    if constexpr (MODE == kQuad) {
+    if constexpr (MODE == kQuad && !PREHALVED) {
       if (hf != kF16One) {  // wave-uniform: only the diagonal block's K steps pay for the products
 #pragma unroll
         for (int f = 0; f < FM; ++f) use[f] = scale_f16x8(use[f], hf);
@@ -523,7 +524,7 @@ hipError_t launch_gram_store(const uint16_t* xt, int64_t n_pad, int64_t d_in, fl
 
 hipError_t launch_quad_sse(const uint16_t* g16, const int32_t* gexp, const uint16_t* delta16, const int32_t* dexp,
                            int n_cand, int64_t d_in, int64_t d_out, int64_t cand_stride, double* tile_sse,
-                           hipStream_t st) {
+                           hipStream_t st, bool prehalved) {
   const int tiles_m = (int)((d_in + BM - 1) / BM);
   const int tiles_n = (int)((d_out + BN - 1) / BN);
   const int n_cols = tiles_n * n_cand;
@@ -533,8 +534,12 @@ hipError_t launch_quad_sse(const uint16_t* g16, const int32_t* gexp, const uint1
   epi.gexp = gexp;
   epi.cand_stride = cand_stride;
   // A = G ([d_in, d_in], symmetric: its rows are its columns), B = the candidates' delta
-  hipLaunchKernelGGL((error_sse_kernel<uint16_t, kQuad>), dim3(grid), dim3(kThreads), 0, st, g16, d_in, delta16,
-                     d_in, d_in, d_out, tiles_m, tiles_n, n_cols, tile_sse, epi);
+  if (prehalved)
+    hipLaunchKernelGGL((error_sse_kernel<uint16_t, kQuad, true>), dim3(grid), dim3(kThreads), 0, st, g16, d_in,
+                       delta16, d_in, d_in, d_out, tiles_m, tiles_n, n_cols, tile_sse, epi);
+  else
+    hipLaunchKernelGGL((error_sse_kernel<uint16_t, kQuad>), dim3(grid), dim3(kThreads), 0, st, g16, d_in, delta16,
+                       d_in, d_in, d_out, tiles_m, tiles_n, n_cols, tile_sse, epi);
   return hipGetLastError();
 }
 
