@@ -202,7 +202,10 @@ AWQ_API int awq_search_loss_form(int dtype, int64_t n_tokens, int64_t d_in, int6
 AWQ_API size_t awq_gram_workspace_bytes(int64_t n_tokens, int64_t d_in);
 
 /* G = X^T X for bfloat16 activations, written as float16(G * 2^gram_exp[0]); gram_exp[0] is chosen
- * so that G's largest entry (on its diagonal) scales to at most 2^14.
+ * so that G's largest entry (on its diagonal) scales to at most 2^14. The 256 x 256 blocks on the
+ * diagonal (rows and columns 256 I .. 256 I + 255) hold those float16 values times 1/2 (a float16
+ * product: exact but for values below float16's normal range, under 2^-26 of G's largest entry), the
+ * form awq_gram_error_sse takes.
  *   x          device, bfloat16 [n_tokens, ld_x] (the rules of awq_act_stats).
  *   gram       device, float16 bits [d_in, d_in], 16-byte aligned, written.
  *   gram_exp   device, int32 [1], written.
@@ -227,8 +230,7 @@ AWQ_API int awq_quant_delta_f16(const void* const* w_parts, const int64_t* part_
  * then zeros, awq_error_tiles(n_tokens, d_out) entries per candidate (n_tokens >= d_in, else
  * AWQ_ERR_SHAPE). Tile (I, t) holds, over output rows t, delta_I G_II delta_I^T + 2 sum_{J>I}
  * delta_I G_IJ delta_J^T for the 256-blocks I, J of d_in: only G's blocks on and above the diagonal
- * are read. G's diagonal block enters halved and the tile's sum doubled; the halving is exact but for
- * float16 values that fall below float16's normal range, under 2^-26 of G's largest entry.
+ * are read. G's diagonal blocks enter halved, as awq_gram stores them, and the tile's sum doubled.
  *   gram, gram_exp    as written by awq_gram.
  *   delta, delta_exp  as written by awq_quant_delta_f16.
  *   tile_sse          device, float64 [n_cand, awq_error_tiles(n_tokens, d_out)], written. */

@@ -222,8 +222,7 @@ int run_search(const void* x, int64_t ld_x, const void* const* w_parts, const in
     p += round_up((size_t)d_in * (size_t)awq::gram_n_pad(n_tokens) * 2, 256);
     float* g32 = reinterpret_cast<float*>(p);
     uint16_t* d16 = static_cast<uint16_t*>(delta);
-    // G's diagonal blocks stored halved: the quadratic form's K loop then scales nothing
-    e = awq::launch_gram(x, ld_x, n_tokens, d_in, xt, g32, g16, gexp, st, /*halve_diag=*/true);
+    e = awq::launch_gram(x, ld_x, n_tokens, d_in, xt, g32, g16, gexp, st);
     if (e != hipSuccess) return hip_fail(e, "gram launch");
     for (int k0 = 0; k0 < n_grid; k0 += cand_per_pass) {
       const int nk = n_grid - k0 < cand_per_pass ? n_grid - k0 : cand_per_pass;
@@ -235,7 +234,7 @@ int run_search(const void* x, int64_t ld_x, const void* const* w_parts, const in
                                             : awq::launch_quant_delta_row_f16(w, d_in, quantizer, cs, nk, d16, dexp, st);
       if (e != hipSuccess) return hip_fail(e, "quant_delta_f16 launch");
       if ((e = awq::launch_fill_f64(ts, (int64_t)nk * tiles, 0.0, st)) != hipSuccess) return hip_fail(e, "fill launch");
-      if ((e = awq::launch_quad_sse(g16, gexp, d16, dexp, nk, d_in, d_out, tiles, ts, st, /*prehalved=*/true)) != hipSuccess)
+      if ((e = awq::launch_quad_sse(g16, gexp, d16, dexp, nk, d_in, d_out, tiles, ts, st)) != hipSuccess)
         return hip_fail(e, "gram_error_sse launch");
     }
     e = awq::launch_loss_argmin(tile_sse, tiles, n_grid, n_tokens, d_out, cand_scales, d_in, losses,

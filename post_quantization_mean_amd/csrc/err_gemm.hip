@@ -34,9 +34,8 @@
 // delta G delta^T. With d_in cut into 256-blocks, the form is the sum over block pairs (I, J) of
 // delta_I G_IJ delta_J^T, and G_JI = G_IJ^T makes the (J, I) term equal to the (I, J) one, so the
 // form is sum_I (delta_I G_II delta_I^T + 2 sum_{J>I} delta_I G_IJ delta_J^T): row tile I runs K over
-// the blocks J >= I, about half the matrix work of the full K range, with G's fragments halved
-// while K is in block I (or G stored with its diagonal blocks halved, PREHALVED) and the tile's sum
-// doubled. The tiles' lengths fall with I, so a compute
+// the blocks J >= I, about half the matrix work of the full K range: G is stored with its diagonal
+// blocks halved (gram.hip), and the tile's sum is doubled. The tiles' lengths fall with I, so a compute
 // unit takes row tile I and then row tile R - 1 - I of the same column (R = ceil(d_in / 256) row
 // tiles): every pair has the same length, the 256 units stay in step, and their 16 x 16
 // super-blocks keep sharing operands in L2.
@@ -85,19 +84,6 @@ __device__ __forceinline__ void mma_pair(const uint4& a, const uint4& b, f32x16&
   }
 }
 
-// A fragment of eight float16 values times f, a pair of equal float16 values (exact for a power
-// of two down to float16's normal range).
-__device__ __forceinline__ uint4 scale_f16x8(uint4 a, uint32_t f) {
-  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-  const h2 m = __builtin_bit_cast(h2, f);
-  a.x = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, a.x) * m);
-  a.y = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, a.y) * m);
-  a.z = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, a.z) * m);
-  a.w = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, a.w) * m);
-  return a;
-}
-constexpr uint32_t kF16One = 0x3C003C00u, kF16Half = 0x38003800u;
-
 constexpr int KB = 128;
 constexpr int kStageBytes = (BM + BN) * KB;  // 64 KiB
 constexpr int kThreads = 256;
@@ -115,7 +101,6 @@ struct TileOps {
   int m0, n0, cand;
   int k_steps;  // K steps of this tile (>= 2)
   int k_last;   // kQuad: byte offset of the last K step if K is walked downwards, else 0
-  int d0, d1;   // kQuad: the K steps [d0, d1) (in walk order) lie in the diagonal block
 };
 // Tile G of the upper triangle tm <= tn of a tiles x tiles grid, row by row.
 __device__ __forceinline__ void tri_of(int G, int tiles, int& tm, int& tn) {
@@ -215,9 +200,6 @@ __device__ __forceinline__ TileOps tile_ops(int G, const T* x, int64_t ld_x, con
   t.cand = cand;
   t.k_steps = (int)((d_in - k0) * (int64_t)sizeof(T) / KB);
   t.k_last = down ? (t.k_steps - 1) * KB : 0;
-  const int nd = (int)(min((int64_t)BM, d_in - k0) * (int64_t)sizeof(T) / KB);  // the diagonal block's steps
-  t.d0 = MODE != kQuad ? 0 : down ? t.k_steps - nd : 0;
-  t.d1 = MODE != kQuad ? 0 : down ? t.k_steps : nd;
   return t;
 }
 
@@ -233,7 +215,7 @@ struct Epi {
 // Persistent: one workgroup per compute unit walks tiles G = blockIdx.x, + gridDim.x, ... The
 // next tile's first K stage is loaded into the free LDS buffer during the current tile's last K
 // step, so its load latency hides behind that step and the epilogue.
-template <typename T, int MODE = kSse, bool PREHALVED = false>
+template <typename T, int MODE = kSse>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void error_sse_kernel(const T* __restrict__ x, int64_t ld_x, const T* __restrict__ delta,
                       int64_t n_tokens, int64_t d_in, int64_t d_out, int tiles_m, int tiles_n,
@@ -289,17 +271,10 @@ void error_sse_kernel(const T* __restrict__ x, int64_t ld_x, const T* __restrict
   // next sub-step's fragment reads (if `reads`). A load holds up the wave's issue for about as
   // long as the texture unit takes to accept its 64 addresses, so one per MFMA keeps the matrix
   // core fed (two back to back left it idle for ~10 % of the cycles).
-  // (zc: the tile's first sub-step, which writes every accumulator once from zero; kQuad: hf is the
-  // float16 pair that scales the A fragments of `use`'s K step, one half in the diagonal block)
-  auto substep = [&](auto zc, uint32_t hf, uint4 (&use)[NR], uint4 (&nxt)[NR], const char* src, int sl, bool reads,
+  // (zc: the tile's first sub-step, which writes every accumulator once from zero)
+  auto substep = [&](auto zc, uint4 (&use)[NR], uint4 (&nxt)[NR], const char* src, int sl, bool reads,
                      const TileOps& lt, uint32_t fstage, int kbyte, int l0, int l1) {
     constexpr bool ZC = decltype(zc)::value;
-    if constexpr (MODE == kQuad && !PREHALVED) {
-      if (hf != kF16One) {  // wave-uniform: only the diagonal block's K steps pay for the products
-#pragma unroll
-        for (int f = 0; f < FM; ++f) use[f] = scale_f16x8(use[f], hf);
-      }
-    }
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
       const int fm = g >> 1, fn = (g & 1) * 2;
@@ -314,10 +289,6 @@ void error_sse_kernel(const T* __restrict__ x, int64_t ld_x, const T* __restrict
   };
   const std::false_type acc_in{};
   const std::true_type acc_zero{};
-  // kQuad: the factor of K step kt's A fragments in tile t
-  auto hf_of = [&](const TileOps& t, int kt) -> uint32_t {
-    return (unsigned)(kt - t.d0) < (unsigned)(t.d1 - t.d0) ? kF16Half : kF16One;
-  };
   // kQuad: the epilogue's delta[o, j] (four consecutive j per 8 bytes), loaded while the tile's last
   // K steps run; element e of accumulator (i, j) in lane l is row 32 i + 8 (e / 4) + 4 (l / 32) +
   // e % 4 of the wave's 128 A rows and column 32 j + l % 32 of its 128 B rows. Here n_tokens = d_in
@@ -370,7 +341,7 @@ void error_sse_kernel(const T* __restrict__ x, int64_t ld_x, const T* __restrict
     // one's fragments); the loop runs B C | barrier | D A', so that K step 0's A, which starts
     // the accumulators, stays outside it. Loads: the rest of stage kt+1 in A(kt), the first
     // kSplit of stage kt+2 in D(kt) into the buffer the barrier of step kt freed.
-    substep(acc_zero, hf_of(cur_t, 0), f0, f1, lds + par * kStageBytes, slot[1], true, cur_t,
+    substep(acc_zero, f0, f1, lds + par * kStageBytes, slot[1], true, cur_t,
             lds_base + (par ^ 1) * kStageBytes, KB,
             kSplit, 16);
     int kt = 0;
@@ -379,13 +350,12 @@ void error_sse_kernel(const T* __restrict__ x, int64_t ld_x, const T* __restrict
       char* cur = lds + b * kStageBytes;
       char* nxt = lds + (b ^ 1) * kStageBytes;
       const uint32_t fre = lds_base + b * kStageBytes;  // stage kt's buffer, refilled with stage kt+2
-      const uint32_t hf = hf_of(cur_t, kt);
-      substep(acc_in, hf, f1, f0, cur, slot[2], true, cur_t, 0, 0, 0, 0);
-      substep(acc_in, hf, f0, f1, cur, slot[3], true, cur_t, 0, 0, 0, 0);
+      substep(acc_in, f1, f0, cur, slot[2], true, cur_t, 0, 0, 0, 0);
+      substep(acc_in, f0, f1, cur, slot[3], true, cur_t, 0, 0, 0, 0);
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // stage kt+1 has landed
       __syncthreads();                           // and every wave has read all of stage kt
-      substep(acc_in, hf, f1, f0, nxt, slot[0], true, cur_t, fre, (kt + 2) * KB, 0, kSplit);
-      substep(acc_in, hf_of(cur_t, kt + 1), f0, f1, nxt, slot[1], true, cur_t, fre, (kt + 2) * KB, kSplit, 16);
+      substep(acc_in, f1, f0, nxt, slot[0], true, cur_t, fre, (kt + 2) * KB, 0, kSplit);
+      substep(acc_in, f0, f1, nxt, slot[1], true, cur_t, fre, (kt + 2) * KB, kSplit, 16);
     }
     {  // K step k_steps-2 (B C D), then A of the last step, which starts the next tile's stage 0
       // in the buffer this step's barrier freed
@@ -394,14 +364,13 @@ void error_sse_kernel(const T* __restrict__ x, int64_t ld_x, const T* __restrict
       char* nxt = lds + (b ^ 1) * kStageBytes;
       const uint32_t fre = lds_base + b * kStageBytes;
       const int nl = has_next ? 16 : 0;
-      const uint32_t hf = hf_of(cur_t, kt);
-      substep(acc_in, hf, f1, f0, cur, slot[2], true, cur_t, 0, 0, 0, 0);
-      substep(acc_in, hf, f0, f1, cur, slot[3], true, cur_t, 0, 0, 0, 0);
+      substep(acc_in, f1, f0, cur, slot[2], true, cur_t, 0, 0, 0, 0);
+      substep(acc_in, f0, f1, cur, slot[3], true, cur_t, 0, 0, 0, 0);
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       __syncthreads();  // every wave has read all of stage k_steps-2: its buffer is free
       load_dq(cur_t);
-      substep(acc_in, hf, f1, f0, nxt, slot[0], true, cur_t, 0, 0, 0, 0);
-      substep(acc_in, hf_of(cur_t, kt + 1), f0, f1, nxt, slot[1], true, nxt_t, fre, 0, 0, min(nl, 8));
+      substep(acc_in, f1, f0, nxt, slot[0], true, cur_t, 0, 0, 0, 0);
+      substep(acc_in, f0, f1, nxt, slot[1], true, nxt_t, fre, 0, 0, min(nl, 8));
       ++kt;
     }
     {  // K step k_steps-1: B C D
@@ -409,10 +378,9 @@ void error_sse_kernel(const T* __restrict__ x, int64_t ld_x, const T* __restrict
       char* cur = lds + b * kStageBytes;
       const uint32_t fre = lds_base + (b ^ 1) * kStageBytes;
       const int nl = has_next ? 16 : 0;
-      const uint32_t hf = hf_of(cur_t, kt);
-      substep(acc_in, hf, f1, f0, cur, slot[2], true, nxt_t, fre, 0, 8, nl);
-      substep(acc_in, hf, f0, f1, cur, slot[3], true, nxt_t, 0, 0, 0, 0);
-      substep(acc_in, hf, f1, f0, cur, slot[0], false, nxt_t, 0, 0, 0, 0);
+      substep(acc_in, f1, f0, cur, slot[2], true, nxt_t, fre, 0, 8, nl);
+      substep(acc_in, f0, f1, cur, slot[3], true, nxt_t, 0, 0, 0, 0);
+      substep(acc_in, f1, f0, cur, slot[0], false, nxt_t, 0, 0, 0, 0);
       par = b ^ 1;
     }
 
@@ -524,7 +492,7 @@ hipError_t launch_gram_store(const uint16_t* xt, int64_t n_pad, int64_t d_in, fl
 
 hipError_t launch_quad_sse(const uint16_t* g16, const int32_t* gexp, const uint16_t* delta16, const int32_t* dexp,
                            int n_cand, int64_t d_in, int64_t d_out, int64_t cand_stride, double* tile_sse,
-                           hipStream_t st, bool prehalved) {
+                           hipStream_t st) {
   const int tiles_m = (int)((d_in + BM - 1) / BM);
   const int tiles_n = (int)((d_out + BN - 1) / BN);
   const int n_cols = tiles_n * n_cand;
@@ -534,12 +502,8 @@ hipError_t launch_quad_sse(const uint16_t* g16, const int32_t* gexp, const uint1
   epi.gexp = gexp;
   epi.cand_stride = cand_stride;
   // A = G ([d_in, d_in], symmetric: its rows are its columns), B = the candidates' delta
-  if (prehalved)
-    hipLaunchKernelGGL((error_sse_kernel<uint16_t, kQuad, true>), dim3(grid), dim3(kThreads), 0, st, g16, d_in,
-                       delta16, d_in, d_in, d_out, tiles_m, tiles_n, n_cols, tile_sse, epi);
-  else
-    hipLaunchKernelGGL((error_sse_kernel<uint16_t, kQuad>), dim3(grid), dim3(kThreads), 0, st, g16, d_in, delta16,
-                       d_in, d_in, d_out, tiles_m, tiles_n, n_cols, tile_sse, epi);
+  hipLaunchKernelGGL((error_sse_kernel<uint16_t, kQuad>), dim3(grid), dim3(kThreads), 0, st, g16, d_in, delta16,
+                     d_in, d_in, d_out, tiles_m, tiles_n, n_cols, tile_sse, epi);
   return hipGetLastError();
 }
 

@@ -18,10 +18,10 @@ hipError_t launch_error_sse(const void* x, int64_t ld_x, const void* delta, int 
 hipError_t launch_gram_store(const uint16_t* xt, int64_t n_pad, int64_t d_in, float* g, hipStream_t stream);
 // ... and per tile a share of sum_o delta_k[o] G delta_k[o]^T from float16 G (scaled by 2^gexp[0])
 // and float16 delta_k (scaled by 2^dexp[k]), unscaled exactly, in tile_sse[k * cand_stride + tile].
-// Reads only G's 256-blocks on and above the diagonal; the diagonal blocks are halved while they
-// are read, or, with prehalved, were stored halved (launch_gram with halve_diag).
+// Reads only G's 256-blocks on and above the diagonal; the diagonal blocks are stored halved
+// (launch_gram) and each tile's sum is doubled.
 hipError_t launch_quad_sse(const uint16_t* g16, const int32_t* gexp, const uint16_t* delta16, const int32_t* dexp,
                            int n_cand, int64_t d_in, int64_t d_out, int64_t cand_stride, double* tile_sse,
-                           hipStream_t stream, bool prehalved = false);
+                           hipStream_t stream);
 
 }  // namespace awq

@@ -98,7 +98,7 @@ __global__ __launch_bounds__(1024) void gram_exp_kernel(const float* __restrict_
 // so reads and writes are rows of 64 contiguous values either way.
 __global__ __launch_bounds__(kThreads) void gram_f16_kernel(const float* __restrict__ g, int64_t d_in,
                                                             const int32_t* __restrict__ gexp,
-                                                            uint16_t* __restrict__ g16, int halve_diag) {
+                                                            uint16_t* __restrict__ g16) {
   __shared__ float t[kTT][kTT + 1];
   const float sc = ldexpf(1.f, gexp[0]);
   const int64_t i0 = (int64_t)blockIdx.y * kTT, j0 = (int64_t)blockIdx.x * kTT;
@@ -117,9 +117,10 @@ __global__ __launch_bounds__(kThreads) void gram_f16_kernel(const float* __restr
     }
   }
   __syncthreads();
-  // 64 rows x 8 chunks of 8 halves; in a diagonal 256-block with halve_diag, each float16 value is
-  // then multiplied by 1/2 in float16 (exact in float16's normal range)
-  const _Float16 hm = (halve_diag && i0 / 256 == j0 / 256) ? (_Float16)0.5f : (_Float16)1.0f;
+  // 64 rows x 8 chunks of 8 halves; in a diagonal 256-block each float16 value is then multiplied
+  // by 1/2 in float16 (exact in float16's normal range): the quadratic form's K loop takes G's
+  // diagonal blocks halved and doubles each tile's sum, with no per-step scaling
+  const _Float16 hm = i0 / 256 == j0 / 256 ? (_Float16)0.5f : (_Float16)1.0f;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int r = (tid >> 3) + 32 * h, ch = tid & 7;
@@ -220,7 +221,7 @@ __global__ void fill_f64_kernel(double* __restrict__ p, int64_t n, double v) {
 int64_t gram_n_pad(int64_t n_tokens) { return (n_tokens + kTT - 1) / kTT * kTT; }
 
 hipError_t launch_gram(const void* x, int64_t ld_x, int64_t n_tokens, int64_t d_in, uint16_t* xt, float* g32,
-                       uint16_t* g16, int32_t* gexp, hipStream_t st, bool halve_diag) {
+                       uint16_t* g16, int32_t* gexp, hipStream_t st) {
   const int64_t n_pad = gram_n_pad(n_tokens);
   hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)((d_in + kTT - 1) / kTT), (unsigned)(n_pad / kTT)),
                      dim3(kThreads), 0, st, static_cast<const uint16_t*>(x), ld_x, n_tokens, d_in, xt, n_pad);
@@ -231,7 +232,7 @@ hipError_t launch_gram(const void* x, int64_t ld_x, int64_t n_tokens, int64_t d_
   hipLaunchKernelGGL(gram_exp_kernel, dim3(1), dim3(1024), 0, st, g32, d_in, gexp);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const unsigned nb = (unsigned)(d_in / kTT);  // d_in is a multiple of 128
-  hipLaunchKernelGGL(gram_f16_kernel, dim3(nb, nb), dim3(kThreads), 0, st, g32, d_in, gexp, g16, (int)halve_diag);
+  hipLaunchKernelGGL(gram_f16_kernel, dim3(nb, nb), dim3(kThreads), 0, st, g32, d_in, gexp, g16);
   return hipGetLastError();
 }
 

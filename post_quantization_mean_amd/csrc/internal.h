@@ -57,11 +57,10 @@ hipError_t launch_quant_delta_f16(const WParts& w, int64_t d_in, const double* c
 // ---- the Gram form of the loss (gram.hip)
 int64_t gram_n_pad(int64_t n_tokens);  // tokens of X^T's rows: a multiple of 64
 // X^T into xt ([d_in, gram_n_pad]), G = X^T X into g32 ([d_in, d_in] float32), its scale exponent
-// into gexp[0] and float16(G * 2^gexp) into g16; with halve_diag, the 256 x 256 blocks on the
-// diagonal are stored times 1/2 (a float16 product, as the quadratic form would form it) for
-// launch_quad_sse(..., prehalved = true)
+// into gexp[0] and float16(G * 2^gexp) into g16, the 256 x 256 blocks on the diagonal times 1/2 (a
+// float16 product), the operand launch_quad_sse takes
 hipError_t launch_gram(const void* x, int64_t ld_x, int64_t n_tokens, int64_t d_in, uint16_t* xt, float* g32,
-                       uint16_t* g16, int32_t* gexp, hipStream_t stream, bool halve_diag = false);
+                       uint16_t* g16, int32_t* gexp, hipStream_t stream);
 // dexp[k] for k < n_cand: the scale exponent of ratio k's delta, from the bound
 // (1.5 max|W| max(s_k) + b) / min(s_k) + max|W| (b: 1e-8 for the INT4 quantizers, 1.27e-6 for the
 // symmetric INT8 one); dexp[n_cand]: max |W| (scratch)
